@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of single-token GQA decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one call of the library (split-KV kernel + merge kernel) over one
+batch of seeded synthetic inputs already resident in HBM. The timed region
+replays a HIP graph that holds exactly K calls, cycling over R distinct copies
+of the inputs (R * KV bytes >= 1 GiB, so the 256 MB last-level cache and the
+L2s cannot serve the KV cache from one call to the next). Prints ONE JSON line.
+
+Metric: effective KV GB/s = K and V bytes the call attends (each read once)
+divided by the time per call, and its fraction of the 8 TB/s HBM peak.
+`roofline.achieved` uses the split kernel's own duration, measured with HIP
+events recorded on its stream right before and after it.
+`cpu_baseline` times the fp64 oracle on one host thread in a subprocess.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import statistics
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E datasheet peak
+DEFAULT_WORKLOAD = "llama70b_gqa_b1_s8192"
+ROTATE_BYTES = 1 << 30
+KERNEL_SOURCES = ["gqa_common.h", "split_kv_mfma.h", "split_kv_valu.h", "merge.h", "gqa_decode.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "decode_attention_gqa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Hip:
+    """The few HIP runtime calls bench.py needs for events, via ctypes."""
+
+    def __init__(self):
+        path = None
+        for cand in ("libamdhip64.so", "/opt/rocm/lib/libamdhip64.so"):
+            try:
+                self.lib = ctypes.CDLL(cand)
+                path = cand
+                break
+            except OSError:
+                continue
+        if path is None:
+            raise RuntimeError("libamdhip64.so not found")
+        L = self.lib
+        L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def elapsed_ms(self, a, b) -> float:
+        assert self.lib.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+
+def cpu_baseline(name: str, budget_s: float) -> dict:
+    """Time oracle.attend on the host, one thread, in a child process."""
+    code = f"""
+import json, os, sys, time
+sys.path.insert(0, {ROOT!r})
+import numpy as np
+import oracle, workloads
+w = workloads.WORKLOADS[{name!r}]
+inp = workloads.make_inputs(w)
+heads = None
+groups = w.h_kv
+if inp.kv_bytes() > (1 << 30):          # very long context: time one kv group of sequence 0
+    heads = [(0, h) for h in range(w.n_rep)]
+    groups = 1
+t0 = time.perf_counter(); n = 0
+while True:
+    oracle.attend(inp.q, inp.k, inp.v, inp.seq_lens, inp.scale, w.h_kv, dtype=w.dtype, heads=heads)
+    n += 1
+    if time.perf_counter() - t0 >= {budget_s}:
+        break
+dt = (time.perf_counter() - t0) / n
+if heads is None:
+    sample_bytes = inp.kv_bytes()
+    sample = f"whole workload per call, {{n}} call(s)"
+else:
+    sample_bytes = 2 * int(inp.seq_lens[0]) * w.d * 2
+    sample = f"kv group 0 of sequence 0 ({{w.n_rep}} query heads, {{int(inp.seq_lens[0])}} tokens) per call, {{n}} call(s)"
+print(json.dumps(dict(seconds_per_call=dt, sample_bytes=sample_bytes, calls=n, sample=sample)))
+"""
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
+               HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       timeout=600)
+    if r.returncode != 0:
+        raise RuntimeError("cpu baseline failed: " + r.stderr[-2000:])
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    gbs = d["sample_bytes"] / d["seconds_per_call"] / 1e9
+    return {"value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 numpy oracle on {name}: {d['sample']}; "
+                      f"{d['seconds_per_call'] * 1e3:.1f} ms per sample (BLAS and OpenMP threads = 1)"}
+
+
+def traffic_from_profile(name: str, src_hash: str):
+    """HBM bytes per split-kernel launch from committed rocprofv3 counters,
+    or None when absent or taken on different kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"counters_split_kv_{name}.json")
+    if not os.path.exists(p):
+        return None, None
+    d = json.load(open(p))
+    if d.get("kernel_source_hash") != src_hash:
+        return None, d
+    return d.get("hbm_bytes_per_launch"), d
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--n-splits", type=int, default=0)
+    ap.add_argument("--valu", action="store_true", help="vector-ALU split kernel (comparison)")
+    ap.add_argument("--eager", action="store_true", help="time eager calls instead of a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device copy of this many MiB first (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    import workloads
+
+    src_hash = kernel_source_hash()
+    w = workloads.WORKLOADS[args.workload]
+    log(f"[bench] workload {w.name}: generating inputs")
+    inp = workloads.make_inputs(w)
+    kv_bytes = inp.kv_bytes()
+    s_max = int(inp.seq_lens.max())
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    q0, k0, v0 = up(inp.q), up(inp.k), up(inp.v)
+    lens = torch.from_numpy(inp.seq_lens).to(dev)
+    free, _ = torch.cuda.mem_get_info()
+    R = max(1, min(math.ceil(ROTATE_BYTES / kv_bytes), int(0.5 * free // max(1, kv_bytes))))
+    sets = [(q0, k0, v0)] + [(q0.clone(), k0.clone(), v0.clone()) for _ in range(R - 1)]
+    log(f"[bench] {R} rotating input set(s) of {kv_bytes / 2**20:.1f} MiB KV")
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {n} bytes copied")
+
+    ns = args.n_splits if args.n_splits > 0 else gqa.gqa_decode_pick_splits(w.B, w.h_kv, s_max)
+    ws = torch.empty(gqa.gqa_decode_workspace_bytes(w.B, w.h_q, w.d, ns), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.B, w.h_q, w.d), dtype=torch.float32, device=dev)
+    scale = float(inp.scale)
+
+    def call(i):
+        q, k, v = sets[i % R]
+        gqa.gqa_decode_attn_ex(q, k, v, lens, out, scale=scale, n_splits=args.n_splits,
+                               s_kv_hint=s_max, workspace=ws, valu=args.valu)
+
+    stream = torch.cuda.Stream()
+    hip = Hip()
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            call(i)
+        torch.cuda.synchronize()
+        log(f"[bench] {args.warmup} warmup calls done")
+
+        # ---- the timed region: exactly K calls
+        if args.eager:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                call(i)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+        else:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(args.steps):
+                    call(i)
+            g.replay()                       # first replay uploads the graph (untimed)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            g.replay()
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+        log(f"[bench] timed {args.steps} calls")
+        sec_per_call = (t1 - t0) / args.steps
+
+        # ---- split kernel alone, HIP events on its stream (eager calls)
+        n_ev = min(args.steps, 100)
+        evs = [(hip.event(), hip.event()) for _ in range(n_ev)]
+        for i in range(n_ev):
+            assert gqa.lib.gqa_decode_set_split_events(evs[i][0], evs[i][1]) == 0
+            call(i)
+        assert gqa.lib.gqa_decode_set_split_events(None, None) == 0
+        torch.cuda.synchronize()
+        split_ms = [hip.elapsed_ms(a, b) for a, b in evs]
+        for a, b in evs:
+            hip.lib.hipEventDestroy(a)
+            hip.lib.hipEventDestroy(b)
+    split_us = statistics.mean(split_ms) * 1e3
+    log(f"[bench] split kernel: mean {split_us:.2f} us, median {statistics.median(split_ms) * 1e3:.2f} us")
+
+    # sanity: finite output
+    if not torch.isfinite(out).all():
+        raise RuntimeError("non-finite output")
+
+    gbs = kv_bytes / sec_per_call / 1e9
+    achieved = kv_bytes / (split_us * 1e-6) / 1e9
+    traffic, tinfo = traffic_from_profile(w.name, src_hash)
+    res = {
+        "metric": "decode attention effective KV GB/s (and % of HBM peak, us/call) at Llama-70B GQA shapes",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec_per_call * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normals; shapes of the Llama-2-70B decode workload)",
+        "config": {
+            "workload": w.name, "B": w.B, "h_q": w.h_q, "h_kv": w.h_kv, "d_head": w.d,
+            "seq_lens": inp.seq_lens.tolist() if w.B <= 16 else f"{w.B} sequences",
+            "kv_bytes_per_call": kv_bytes, "n_splits": ns,
+            "split_kernel": "valu" if args.valu else ("mfma" if w.dtype == "bf16" else "valu"),
+            "timing": "eager calls" if args.eager else "one HIP graph holding the K calls",
+            "rotating_input_sets": R,
+        },
+        "us_per_call": sec_per_call * 1e6,
+        "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "split_kv_mfma" if (w.dtype == "bf16" and not args.valu) else "split_kv_valu",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": kv_bytes,
+            "kernel_us": split_us,
+        },
+        "kernel_source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host")
+        res["cpu_baseline"] = cpu_baseline(w.name, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,170 @@
+"""Single-token grouped-query decode attention for MI355X (gfx950).
+
+Thin Python binding of the C library `libgqa_decode.so` (C ABI declared in
+include/gqa_decode.h). This module only marshals arguments: it checks torch
+tensors, takes their device pointers and the current HIP stream, allocates
+the output and the split workspace with torch, and calls the library. Every
+step of the attention runs in the library's HIP kernels.
+
+If the library is not built, importing this module raises: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_pick_splits",
+    "gqa_decode_workspace_bytes", "gqa_status_string", "GQAError", "lib", "LIB_PATH",
+    "GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_WORKSPACE", "GQA_ERR_HIP",
+    "GQA_DTYPE_F32", "GQA_DTYPE_BF16", "GQA_FLAG_VALU", "GQA_MAX_SPLITS",
+]
+
+GQA_OK = 0
+GQA_ERR_INVALID_ARG = -1
+GQA_ERR_UNSUPPORTED = -2
+GQA_ERR_WORKSPACE = -3
+GQA_ERR_HIP = -4
+GQA_DTYPE_F32 = 0
+GQA_DTYPE_BF16 = 1
+GQA_FLAG_VALU = 1
+GQA_MAX_SPLITS = 4096
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_decode.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python decode_attention_gqa_amd/build.py` "
+        "(or __graft_entry__.build()). There is no non-HIP fallback.")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+lib.gqa_decode_attn.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32]
+lib.gqa_decode_attn.restype = _i32
+lib.gqa_decode_attn_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32,
+                                   _i32, _i32, _i64, _vp, _sz, _vp, _i32]
+lib.gqa_decode_attn_ex.restype = _i32
+lib.gqa_decode_pick_splits.argtypes = [_i32, _i32, _i64, _i32]
+lib.gqa_decode_pick_splits.restype = _i32
+lib.gqa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
+lib.gqa_decode_workspace_bytes.restype = _sz
+lib.gqa_status_string.argtypes = [_i32]
+lib.gqa_status_string.restype = ctypes.c_char_p
+lib.gqa_decode_set_split_events.argtypes = [_vp, _vp]
+lib.gqa_decode_set_split_events.restype = _i32
+lib.gqa_last_error.argtypes = []
+lib.gqa_last_error.restype = ctypes.c_char_p
+
+
+class GQAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.gqa_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {gqa_status_string(status)} ({status}): {msg}")
+
+
+def gqa_status_string(status: int) -> str:
+    return lib.gqa_status_string(status).decode()
+
+
+def gqa_decode_pick_splits(B: int, h_kv: int, s_kv_max: int = 0, num_cus: int = 0) -> int:
+    """Split count the library picks (num_cus <= 0: the current device's)."""
+    r = lib.gqa_decode_pick_splits(B, h_kv, s_kv_max, num_cus)
+    if r < 0:
+        raise GQAError(r, "gqa_decode_pick_splits")
+    return r
+
+
+def gqa_decode_workspace_bytes(B: int, h_q: int, d_head: int, n_splits: int) -> int:
+    return int(lib.gqa_decode_workspace_bytes(B, h_q, d_head, n_splits))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.bfloat16:
+        return GQA_DTYPE_BF16
+    if dt == torch.float32:
+        return GQA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def gqa_decode_attn_ex(q, k_cache, v_cache, seq_lens, out=None, *, scale=None, n_splits=0,
+                       out_dtype=None, s_kv_hint=0, kv_token_offsets=None, workspace=None,
+                       stream=None, valu=False):
+    """Decode attention for one query token per sequence.
+
+    q [B, h_q, d], k_cache / v_cache [T, h_kv, d] (packed by default), seq_lens [B]
+    int32; all on the same GPU, contiguous, q/k/v of one dtype (bf16 or fp32).
+    Returns out [B, h_q, d] (fp32 unless out_dtype=torch.bfloat16).
+    The work is enqueued on `stream` (default: torch's current stream).
+    """
+    torch = _torch()
+    B, h_q, d = q.shape
+    h_kv = k_cache.shape[1]
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share one dtype")
+    if k_cache.dim() != 3 or k_cache.shape != v_cache.shape or k_cache.shape[2] != d:
+        raise ValueError("k_cache and v_cache must be [T, h_kv, d_head]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    if kv_token_offsets is not None and (kv_token_offsets.dtype != torch.int64
+                                         or kv_token_offsets.shape != (B,) or not kv_token_offsets.is_cuda):
+        raise ValueError("kv_token_offsets must be an int64 [B] GPU tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((B, h_q, d), dtype=out_dtype, device=q.device)
+    elif out.shape != (B, h_q, d) or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, h_q, d_head] tensor of out_dtype")
+    with torch.cuda.device(q.device):
+        ns = n_splits if n_splits > 0 else gqa_decode_pick_splits(B, h_kv, int(s_kv_hint), 0)
+        need = gqa_decode_workspace_bytes(B, h_q, d, ns) if ns <= GQA_MAX_SPLITS else 0
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        st = stream if stream is not None else torch.cuda.current_stream(q.device)
+        r = lib.gqa_decode_attn_ex(
+            q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+            kv_token_offsets.data_ptr() if kv_token_offsets is not None else None,
+            out.data_ptr(), B, h_q, h_kv, d, float(scale), int(n_splits),
+            _dtype_code(q.dtype), _dtype_code(out_dtype), int(s_kv_hint),
+            workspace.data_ptr() if workspace is not None else None,
+            workspace.numel() * workspace.element_size() if workspace is not None else 0,
+            ctypes.c_void_p(st.cuda_stream), GQA_FLAG_VALU if valu else 0)
+    if r != GQA_OK:
+        raise GQAError(r, "gqa_decode_attn_ex")
+    return out
+
+
+def gqa_decode_attn(q, k_cache, v_cache, seq_lens, out=None, *, scale=None, n_splits=0):
+    """The base entry point: bf16 inputs, packed cache, fp32 out, null stream,
+    library-owned workspace (same names and arguments as the C function)."""
+    torch = _torch()
+    B, h_q, d = q.shape
+    h_kv = k_cache.shape[1]
+    if q.dtype != torch.bfloat16:
+        raise TypeError("gqa_decode_attn takes bf16 q/k/v; use gqa_decode_attn_ex for fp32")
+    if out is None:
+        out = torch.empty((B, h_q, d), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    with torch.cuda.device(q.device):
+        r = lib.gqa_decode_attn(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                seq_lens.data_ptr(), out.data_ptr(), B, h_q, h_kv, d,
+                                float(scale), int(n_splits))
+    if r != GQA_OK:
+        raise GQAError(r, "gqa_decode_attn")
+    return out

@@ -1,0 +1,73 @@
+// Shared device-side definitions of the split-KV decode attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+constexpr int kWaves = 4;            // waves per workgroup of the split kernels
+constexpr int kThreads = 64 * kWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Arguments of the split kernels (one struct so launches stay readable).
+struct SplitArgs {
+  const void* q;              // [B, h_q, D]
+  const void* k;              // [T, h_kv, D]
+  const void* v;              // [T, h_kv, D]
+  const int32_t* seq_lens;    // [B]
+  const int64_t* kv_off;      // [B] or nullptr (packed)
+  float* ws_o;                // [B, h_q, n_splits, D] unnormalised partial outputs
+  float2* ws_ml;              // [B, h_q, n_splits] (m, l), m in log2 units
+  int h_q;
+  int h_kv;
+  int n_splits;
+  int min_chunk;              // lower bound of the chunk length (tokens)
+  float scale_log2;           // scale * log2(e): scores are kept in log2 units
+};
+
+struct MergeArgs {
+  const int32_t* seq_lens;
+  const float* ws_o;
+  const float2* ws_ml;
+  void* out;                  // [B, h_q, D] fp32 or bf16
+  int h_q;
+  int n_splits;
+  int min_chunk;
+};
+
+__device__ __forceinline__ int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Chunk length and number of non-empty chunks of a sequence of S tokens.
+// The split kernels and the merge kernel both use this, so they agree on
+// which chunks exist: chunk s covers tokens [s*c, min(S, (s+1)*c)).
+__device__ __forceinline__ void chunking(int64_t S, int n_splits, int min_chunk,
+                                         int64_t& c, int& n_active) {
+  if (S <= 0) {
+    c = 0;
+    n_active = 0;
+    return;
+  }
+  c = ceil_div64(S, n_splits);
+  if (c < min_chunk) c = min_chunk;
+  n_active = (int)ceil_div64(S, c);
+}
+
+// First token row of sequence b: explicit offsets, or the packed prefix sum
+// sum_{j<b} S_j computed by the calling wave (every lane gets the result).
+__device__ __forceinline__ int64_t seq_offset(const int32_t* seq_lens, const int64_t* kv_off,
+                                              int b, int lane) {
+  if (kv_off) return kv_off[b];
+  int64_t acc = 0;
+  for (int j = lane; j < b; j += 64) acc += seq_lens[j];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  return acc;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace gqa

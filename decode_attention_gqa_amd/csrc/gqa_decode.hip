@@ -1,0 +1,274 @@
+// Host side of the decode attention library: argument checks, split
+// heuristic, workspace, kernel selection and launches. C ABI in gqa_decode.h.
+#include "gqa_decode.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "gqa_common.h"
+#include "merge.h"
+#include "split_kv_mfma.h"
+#include "split_kv_valu.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+// Heuristic constants (see gqa_decode_pick_splits).
+constexpr int kTargetWgPerCu = 2;    // resident split workgroups per CU the grid aims for
+constexpr int kMinChunk = 128;       // tokens: one 32-token block per wave of a workgroup
+constexpr int kBalance = 4;          // workgroups per resident slot for the longest sequence
+
+// Library-owned fallback workspace, one grow-only buffer per device.
+std::mutex g_ws_mu;
+std::vector<std::pair<void*, size_t>> g_ws;  // index = device ordinal
+
+int device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+  *cus = n;
+  return GQA_OK;
+}
+
+int library_workspace(size_t bytes, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1, {nullptr, 0});
+  auto& slot = g_ws[dev];
+  if (slot.second < bytes) {
+    // Older work on any stream may still read the old buffer: wait for it.
+    if (slot.first) {
+      e = hipDeviceSynchronize();
+      if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
+      (void)hipFree(slot.first);
+      slot = {nullptr, 0};
+    }
+    void* p = nullptr;
+    e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+    slot = {p, bytes};
+  }
+  *ptr = slot.first;
+  return GQA_OK;
+}
+
+bool valid_nrep(int r) { return r == 1 || r == 2 || r == 4 || r == 8 || r == 16; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+size_t ws_bytes(int B, int h_q, int d, int n) {
+  const size_t rows = (size_t)B * h_q * n;
+  size_t o = rows * d * sizeof(float);
+  o = (o + 255) & ~(size_t)255;
+  size_t ml = rows * sizeof(float2);
+  return (o + ml + 255) & ~(size_t)255;
+}
+
+// ---------------------------------------------------------------- launches
+template <int D, int NREP>
+hipError_t launch_split(bool bf16, bool valu, dim3 grid, hipStream_t st, const gqa::SplitArgs& a) {
+  if (!bf16) {
+    hipLaunchKernelGGL((gqa::split_kv_valu<float, D, NREP>), grid, dim3(gqa::kThreads), 0, st, a);
+  } else if (valu) {
+    hipLaunchKernelGGL((gqa::split_kv_valu<__bf16, D, NREP>), grid, dim3(gqa::kThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP>), grid, dim3(gqa::kThreads), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_split_nrep(int nrep, bool bf16, bool valu, dim3 grid, hipStream_t st,
+                             const gqa::SplitArgs& a) {
+  switch (nrep) {
+    case 1: return launch_split<D, 1>(bf16, valu, grid, st, a);
+    case 2: return launch_split<D, 2>(bf16, valu, grid, st, a);
+    case 4: return launch_split<D, 4>(bf16, valu, grid, st, a);
+    case 8: return launch_split<D, 8>(bf16, valu, grid, st, a);
+    default: return launch_split<D, 16>(bf16, valu, grid, st, a);
+  }
+}
+
+template <int D>
+hipError_t launch_merge(bool out_bf16, int B, int h_q, hipStream_t st, const gqa::MergeArgs& a) {
+  dim3 grid((unsigned)((int64_t)B * h_q));
+  if (out_bf16)
+    hipLaunchKernelGGL((gqa::merge_splits<D, __bf16>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((gqa::merge_splits<D, float>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+int pick_splits_host(int B, int h_kv, int64_t s_kv_max, int num_cus) {
+  // Enough workgroups to fill every CU at B = 1 ...
+  const int64_t units = (int64_t)B * h_kv;
+  const int64_t slots = (int64_t)kTargetWgPerCu * num_cus;
+  int64_t n = (slots + units - 1) / units;
+  if (s_kv_max > 0) {
+    // ... and, when the longest sequence is known, chunks short enough that
+    // its workgroups are spread over about kBalance rounds of the resident
+    // slots (ragged batches stay balanced), never shorter than kMinChunk.
+    int64_t chunk = (s_kv_max * units + kBalance * slots - 1) / (kBalance * slots);
+    if (chunk < kMinChunk) chunk = kMinChunk;
+    const int64_t by_len = (s_kv_max + chunk - 1) / chunk;
+    if (by_len > n) n = by_len;
+    const int64_t cap = (s_kv_max + kMinChunk - 1) / kMinChunk;
+    if (n > cap) n = cap;
+  }
+  if (n < 1) n = 1;
+  if (n > GQA_MAX_SPLITS) n = GQA_MAX_SPLITS;
+  return (int)n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_status_string(int status) {
+  switch (status) {
+    case GQA_OK: return "ok";
+    case GQA_ERR_INVALID_ARG: return "invalid argument";
+    case GQA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case GQA_ERR_WORKSPACE: return "workspace too small";
+    case GQA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* gqa_last_error(void) { return g_last_error.c_str(); }
+
+int gqa_decode_set_split_events(hipEvent_t before, hipEvent_t after) {
+  if ((before == nullptr) != (after == nullptr))
+    return fail(GQA_ERR_INVALID_ARG, "give both events or neither");
+  g_ev_before = before;
+  g_ev_after = after;
+  return GQA_OK;
+}
+
+size_t gqa_decode_workspace_bytes(int B, int h_q, int d_head, int n_splits) {
+  if (B < 1 || h_q < 1 || d_head < 1 || n_splits < 1) return 0;
+  return ws_bytes(B, h_q, d_head, n_splits);
+}
+
+int gqa_decode_pick_splits(int B, int h_kv, int64_t s_kv_max, int num_cus) {
+  if (B < 1 || h_kv < 1) return fail(GQA_ERR_INVALID_ARG, "B and h_kv must be >= 1");
+  if (num_cus <= 0) {
+    int st = device_cus(&num_cus);
+    if (st != GQA_OK) return st;
+  }
+  return pick_splits_host(B, h_kv, s_kv_max, num_cus);
+}
+
+int gqa_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* seq_lens, const int64_t* kv_token_offsets,
+                       void* out, int B, int h_q, int h_kv, int d_head,
+                       float scale, int n_splits, int in_dtype, int out_dtype,
+                       int64_t s_kv_hint, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream, int flags) {
+  // ---- host-side checks, before any HIP call
+  if (!q || !k_cache || !v_cache || !seq_lens || !out)
+    return fail(GQA_ERR_INVALID_ARG, "null tensor pointer");
+  if (B < 1 || h_q < 1 || h_kv < 1) return fail(GQA_ERR_INVALID_ARG, "B, h_q, h_kv must be >= 1");
+  if (B > 65535 || h_kv > 65535) return fail(GQA_ERR_INVALID_ARG, "B and h_kv must be <= 65535");
+  if (h_q % h_kv) return fail(GQA_ERR_INVALID_ARG, "h_q (%d) is not a multiple of h_kv (%d)", h_q, h_kv);
+  const int nrep = h_q / h_kv;
+  if (!valid_nrep(nrep)) return fail(GQA_ERR_UNSUPPORTED, "h_q / h_kv = %d not in {1, 2, 4, 8, 16}", nrep);
+  if (d_head != 64 && d_head != 128) return fail(GQA_ERR_UNSUPPORTED, "d_head %d not in {64, 128}", d_head);
+  if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale is not finite");
+  if (in_dtype != GQA_DTYPE_F32 && in_dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "in_dtype %d", in_dtype);
+  if (out_dtype != GQA_DTYPE_F32 && out_dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "out_dtype %d", out_dtype);
+  if (flags & ~GQA_FLAG_VALU) return fail(GQA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (n_splits > GQA_MAX_SPLITS) return fail(GQA_ERR_INVALID_ARG, "n_splits %d > %d", n_splits, GQA_MAX_SPLITS);
+  if (s_kv_hint < 0) return fail(GQA_ERR_INVALID_ARG, "s_kv_hint < 0");
+  const size_t in_el = in_dtype == GQA_DTYPE_BF16 ? 2 : 4;
+  const size_t out_el = out_dtype == GQA_DTYPE_BF16 ? 2 : 4;
+  for (const void* p : {q, k_cache, v_cache, (const void*)out})
+    if (reinterpret_cast<uintptr_t>(p) % 16) return fail(GQA_ERR_INVALID_ARG, "tensor pointer not 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(seq_lens) % 4 || reinterpret_cast<uintptr_t>(kv_token_offsets) % 8)
+    return fail(GQA_ERR_INVALID_ARG, "seq_lens / kv_token_offsets misaligned");
+  const size_t qo_elems = (size_t)B * h_q * d_head;
+  if (overlap(out, qo_elems * out_el, q, qo_elems * in_el) ||
+      overlap(out, qo_elems * out_el, seq_lens, (size_t)B * 4) ||
+      out == k_cache || out == v_cache)
+    return fail(GQA_ERR_INVALID_ARG, "out overlaps an input");
+  if (workspace && reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(GQA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+
+  // ---- split plan
+  int num_cus = 0;
+  int st = device_cus(&num_cus);
+  if (st != GQA_OK) return st;
+  const int ns = n_splits > 0 ? n_splits : pick_splits_host(B, h_kv, s_kv_hint, num_cus);
+  const int min_chunk = n_splits > 0 ? 1 : kMinChunk;
+  const size_t need = ws_bytes(B, h_q, d_head, ns);
+  if (workspace) {
+    if (workspace_bytes < need)
+      return fail(GQA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    if (overlap(out, qo_elems * out_el, workspace, need)) return fail(GQA_ERR_INVALID_ARG, "out overlaps workspace");
+  } else {
+    st = library_workspace(need, &workspace);
+    if (st != GQA_OK) return st;
+  }
+  float* ws_o = static_cast<float*>(workspace);
+  size_t o_bytes = ((size_t)B * h_q * ns * d_head * sizeof(float) + 255) & ~(size_t)255;
+  float2* ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + o_bytes);
+
+  gqa::SplitArgs sa{q, k_cache, v_cache, seq_lens, kv_token_offsets, ws_o, ws_ml,
+                    h_q, h_kv, ns, min_chunk, scale * gqa::kLog2e};
+  const dim3 grid((unsigned)ns, (unsigned)h_kv, (unsigned)B);
+  const bool bf16 = in_dtype == GQA_DTYPE_BF16;
+  const bool valu = (flags & GQA_FLAG_VALU) != 0;
+  hipError_t e;
+  if (g_ev_before && (e = hipEventRecord(g_ev_before, stream)) != hipSuccess)
+    return fail(GQA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  e = d_head == 128 ? launch_split_nrep<128>(nrep, bf16, valu, grid, stream, sa)
+                    : launch_split_nrep<64>(nrep, bf16, valu, grid, stream, sa);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
+  if (g_ev_after && (e = hipEventRecord(g_ev_after, stream)) != hipSuccess)
+    return fail(GQA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+
+  gqa::MergeArgs ma{seq_lens, ws_o, ws_ml, out, h_q, ns, min_chunk};
+  const bool obf16 = out_dtype == GQA_DTYPE_BF16;
+  e = d_head == 128 ? launch_merge<128>(obf16, B, h_q, stream, ma) : launch_merge<64>(obf16, B, h_q, stream, ma);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
+  return GQA_OK;
+}
+
+int gqa_decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* seq_lens, void* out,
+                    int B, int h_q, int h_kv, int d_head,
+                    float scale, int n_splits) {
+  return gqa_decode_attn_ex(q, k_cache, v_cache, seq_lens, nullptr, out, B, h_q, h_kv, d_head,
+                            scale, n_splits, GQA_DTYPE_BF16, GQA_DTYPE_F32, 0, nullptr, 0,
+                            nullptr, 0);
+}
+
+}  // extern "C"

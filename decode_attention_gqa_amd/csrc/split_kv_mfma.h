@@ -1,0 +1,261 @@
+// Split-KV partial attention on the gfx950 matrix cores (bf16 q, K, V).
+//
+// One workgroup owns one chunk of one (sequence b, kv head g) pair and the
+// n_rep query heads of that group. Each of its 4 waves walks 32-token blocks
+// of the chunk (wave w takes blocks w, w+4, ...) and keeps an online-softmax
+// state (m, l, o) for the group's heads; at the end the 4 states are merged
+// in LDS and the workgroup writes one (m, l, o) triplet per head.
+//
+// Per 32-token block, with 16x16x32 bf16 MFMAs:
+//   scores  S^T[t, h] = K[t, :] . Q[h, :]      A = K rows, B = Q^T (2 tiles x D/32 steps)
+//   output  O^T[i, h] += V[t, i] * P[h, t]     A = V^T,    B = P^T (D/16 tiles)
+// Computing the transposed products makes the MFMA output layout of the
+// scores (lane = head, registers = 4 tokens) exactly the B-operand layout the
+// P.V product needs, and puts the per-head softmax statistics in the same
+// lanes as the output rows they rescale - no cross-lane shuffles besides the
+// max reduction. Query heads n_rep..15 of the 16-wide tile are zero padding.
+//
+// Data movement: K and V go straight from HBM to registers with 16-byte
+// loads (nothing is staged in LDS; the group's heads share each K/V register
+// inside the MFMA). A lane's 8 V loads are 8 tokens x 8 consecutive
+// dimensions; an in-register 8x8 transpose of 16-bit values turns them into
+// the MFMA A operand (8 tokens of one dimension). K is used in its natural
+// row layout. Every K and V byte of the chunk is read exactly once.
+//
+// The softmax probabilities are split into bf16 hi + lo parts and both are
+// multiplied with V, so P.V keeps about 16 significant bits of P (bf16 alone
+// would keep 8); l is accumulated from the fp32 values.
+#pragma once
+
+#include "gqa_common.h"
+
+namespace gqa {
+
+template <int D>
+struct MfmaTile {
+  static constexpr int KS = D / 32;   // k-steps of the score product
+  static constexpr int NT = D / 16;   // output tiles (16 dims each) of P.V
+  static constexpr int VW = NT / 2;   // dwords per lane per V token load (8 or 4 bf16)
+};
+
+// Per-lane registers of one 32-token block.
+template <int D>
+struct KVRegs {
+  uint4 k[2][MfmaTile<D>::KS];        // K rows: tile x (tokens 16x + lane%16), step kk
+  uint32_t v[8][MfmaTile<D>::VW];     // V: token slot j, VW dwords of consecutive dims
+};
+
+// Token (within the 32-token block) that lane group `grp` holds in slot j of
+// the P operand. It follows from the score output layout: tile 0 gives
+// tokens 4*grp + r, tile 1 gives 16 + 4*grp + r (r = 0..3).
+__device__ __forceinline__ int slot_token(int grp, int j) {
+  return (j < 4) ? (4 * grp + j) : (16 + 4 * grp + (j - 4));
+}
+
+template <int D>
+__device__ __forceinline__ void load_block(KVRegs<D>& r, const __bf16* kblk, const __bf16* vblk,
+                                           int64_t rs, int grp, int n, int nv) {
+  constexpr int KS = MfmaTile<D>::KS, NT = MfmaTile<D>::NT, VW = MfmaTile<D>::VW;
+  const bool tail = nv < 32;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    int t = 16 * x + n;
+    if (tail) t = min(t, nv - 1);     // clamped rows are read but masked out of the softmax
+    const __bf16* row = kblk + (int64_t)t * rs + 8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) r.k[x][kk] = *reinterpret_cast<const uint4*>(row + 32 * kk);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int t = slot_token(grp, j);
+    if (tail) t = min(t, nv - 1);
+    const __bf16* row = vblk + (int64_t)t * rs + NT * n;
+    if constexpr (VW == 4) {
+      uint4 u = *reinterpret_cast<const uint4*>(row);
+      r.v[j][0] = u.x; r.v[j][1] = u.y; r.v[j][2] = u.z; r.v[j][3] = u.w;
+    } else {
+      uint2 u = *reinterpret_cast<const uint2*>(row);
+      r.v[j][0] = u.x; r.v[j][1] = u.y;
+    }
+  }
+}
+
+// A operand of output tile nt: dimension NT*(lane%16) + nt of the 8 slot tokens.
+template <int D>
+__device__ __forceinline__ bf16x8 v_tile(const KVRegs<D>& r, int nt) {
+  const int w = nt >> 1;
+  uint4 a;
+  uint32_t* pa = reinterpret_cast<uint32_t*>(&a);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = r.v[2 * i][w], y = r.v[2 * i + 1][w];
+    pa[i] = (nt & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+  }
+  return __builtin_bit_cast(bf16x8, a);
+}
+
+struct SoftmaxState {
+  float m;   // running max of this lane's head (log2 units), shared by the 4 lane groups
+  float l;   // partial sum of exponentials over this lane's tokens
+};
+
+template <int D>
+__device__ __forceinline__ void compute_block(const KVRegs<D>& r, const bf16x8 (&qop)[MfmaTile<D>::KS],
+                                              f32x4 (&acc)[MfmaTile<D>::NT], SoftmaxState& st,
+                                              float scale_log2, int grp, int nv) {
+  constexpr int KS = MfmaTile<D>::KS, NT = MfmaTile<D>::NT;
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k[0][kk]), qop[kk], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k[1][kk]), qop[kk], s1, 0, 0, 0);
+  }
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = s0[i] * scale_log2;
+    x[4 + i] = s1[i] * scale_log2;
+  }
+  if (nv < 32) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (slot_token(grp, j) >= nv) x[j] = -INFINITY;
+  }
+  float mb = x[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) mb = fmaxf(mb, x[j]);
+  mb = fmaxf(mb, __shfl_xor(mb, 16));
+  mb = fmaxf(mb, __shfl_xor(mb, 32));
+  const float mn = fmaxf(st.m, mb);          // finite: token 0 of a block is always valid
+  const float alpha = fast_exp2(st.m - mn);  // 0 on the first block (m = -inf)
+  st.m = mn;
+  float p[8], ls = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p[j] = fast_exp2(x[j] - mn);
+    ls += p[j];
+  }
+  st.l = st.l * alpha + ls;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
+  bf16x8 ph, pl;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 h = (__bf16)p[j];
+    ph[j] = h;
+    pl[j] = (__bf16)(p[j] - (float)h);
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const bf16x8 a = v_tile<D>(r, nt);
+    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph, acc[nt], 0, 0, 0);
+    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl, acc[nt], 0, 0, 0);
+  }
+}
+
+template <int D, int NREP>
+__global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
+  constexpr int KS = MfmaTile<D>::KS, NT = MfmaTile<D>::NT;
+  static_assert(NREP >= 1 && NREP <= 16, "one 16-wide MFMA tile holds the query heads of a group");
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int grp = lane >> 4, n = lane & 15;
+
+  const int64_t S = a.seq_lens[b];
+  int64_t c;
+  int n_active;
+  chunking(S, a.n_splits, a.min_chunk, c, n_active);
+  if (s >= n_active) return;                       // the merge reads chunks < n_active only
+  const int64_t t0 = (int64_t)s * c;
+  const int64_t ntok = (S - t0 < c) ? (S - t0) : c;
+  const int64_t off = seq_offset(a.seq_lens, a.kv_off, b, lane);
+
+  const int64_t rs = (int64_t)a.h_kv * D;          // elements between consecutive tokens
+  const __bf16* kbase = static_cast<const __bf16*>(a.k) + ((off + t0) * a.h_kv + g) * D;
+  const __bf16* vbase = static_cast<const __bf16*>(a.v) + ((off + t0) * a.h_kv + g) * D;
+
+  // Q^T as the B operand: lane (grp, n) holds q[head n][32*kk + 8*grp .. +8].
+  bf16x8 qop[KS];
+  {
+    const int h = g * NREP + n;
+    const __bf16* qrow = static_cast<const __bf16*>(a.q) + ((int64_t)b * a.h_q + h) * D + 8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      uint4 u = make_uint4(0u, 0u, 0u, 0u);
+      if (n < NREP) u = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
+      qop[kk] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  SoftmaxState st{-INFINITY, 0.f};
+
+  const int nblk = (int)((ntok + 31) / 32);
+  int blk = w;
+  if (blk < nblk) {
+    KVRegs<D> cur, nxt;
+    int nv = (int)min<int64_t>(32, ntok - (int64_t)blk * 32);
+    load_block<D>(cur, kbase + (int64_t)blk * 32 * rs, vbase + (int64_t)blk * 32 * rs, rs, grp, n, nv);
+    while (true) {
+      const int nb = blk + kWaves;
+      const bool more = nb < nblk;
+      int nvn = 0;
+      if (more) {                                  // prefetch the next block before computing
+        nvn = (int)min<int64_t>(32, ntok - (int64_t)nb * 32);
+        load_block<D>(nxt, kbase + (int64_t)nb * 32 * rs, vbase + (int64_t)nb * 32 * rs, rs, grp, n, nvn);
+      }
+      compute_block<D>(cur, qop, acc, st, a.scale_log2, grp, nv);
+      if (!more) break;
+      cur = nxt;
+      nv = nvn;
+      blk = nb;
+    }
+  }
+
+  // l: sum the 4 lane groups' partial sums (m is already shared by them).
+  st.l += __shfl_xor(st.l, 16);
+  st.l += __shfl_xor(st.l, 32);
+
+  // Merge the 4 waves' states in LDS and write the workgroup's triplets.
+  constexpr int OP = D + 4;                        // padded row (fewer bank conflicts)
+  __shared__ float sm_m[kWaves][16], sm_l[kWaves][16];
+  __shared__ float sm_o[kWaves][NREP][OP];
+  if (grp == 0) {
+    sm_m[w][n] = st.m;
+    sm_l[w][n] = st.l;
+  }
+  if (n < NREP) {
+    // lane (grp, n) holds o[head n][NT*(4*grp + r) + nt]
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sm_o[w][n][NT * (4 * grp + r) + nt] = acc[nt][r];
+  }
+  __syncthreads();
+  constexpr int Q4 = D / 4;
+  for (int idx = tid; idx < NREP * Q4; idx += kThreads) {
+    const int h = idx / Q4, d4 = (idx % Q4) * 4;
+    float M = sm_m[0][h];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][h]);
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float mw = sm_m[ww][h];
+      const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);   // a wave with no block
+      L += f * sm_l[ww][h];
+      o.x += f * sm_o[ww][h][d4 + 0];
+      o.y += f * sm_o[ww][h][d4 + 1];
+      o.z += f * sm_o[ww][h][d4 + 2];
+      o.w += f * sm_o[ww][h][d4 + 3];
+    }
+    const int64_t row = ((int64_t)b * a.h_q + g * NREP + h) * a.n_splits + s;
+    *reinterpret_cast<float4*>(a.ws_o + row * D + d4) = o;
+    if (d4 == 0) a.ws_ml[row] = make_float2(M, L);
+  }
+}
+
+}  // namespace gqa

@@ -1,0 +1,151 @@
+/*
+ * gqa_decode.h - single-token grouped-query decode attention on gfx950 (MI355X).
+ *
+ * What the library computes. For every sequence b, query head h and the
+ * S_b cached positions of sequence b:
+ *
+ *     s_t      = scale * <q[b, h, :], K[off_b + t, g, :]>,   g = h / (h_q / h_kv)
+ *     out[b,h] = sum_t softmax(s)_t * V[off_b + t, g, :]
+ *
+ * Query heads form contiguous groups of n_rep = h_q / h_kv that share one
+ * key/value head (tinygrad issue #5244 "llama speed tracking issue",
+ * `Attention.__call__`: q is split by n_rep * head_dim, k and v by head_dim;
+ * the exllama discussion "Llama 2 is out": 70B has 64 heads in 8 groups).
+ *
+ * How. The KV range of each (sequence, kv head) is cut into n_splits chunks,
+ * one per workgroup. Each chunk yields a partial (m, l, o) triplet - running
+ * max, sum of exponentials, unnormalised output - and a second kernel merges
+ * the triplets exactly and divides o by l (kernbench2 page
+ * `_attention_mesh_mlo.py`: module docstring, the local partial-attention
+ * block, the receive-and-merge blocks and the final normalisation). Here the
+ * split runs across the workgroups of one GPU instead of across ranks.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller. The library
+ *    never frees or keeps them beyond the call.
+ *  - All argument checks run on the host before any HIP call; on error
+ *    nothing is launched and nothing is written.
+ *  - Work is enqueued on the stream and the call returns without waiting for
+ *    it (no host synchronisation). Results are valid once the stream has
+ *    executed past the call.
+ *  - Return value: GQA_OK (0) or a negative gqa status. gqa_last_error()
+ *    gives a message for the calling thread's last failure.
+ *  - No C++ exception crosses this interface.
+ *  - `out` must not overlap q, k_cache, v_cache, seq_lens or the workspace.
+ *
+ * Layouts (row-major, element strides implied by the shapes):
+ *  q        [B, h_q, d_head]
+ *  k_cache  [T, h_kv, d_head]  T >= sum_b S_b. Packed: sequence b occupies
+ *  v_cache  [T, h_kv, d_head]  token rows [off_b, off_b + S_b) with
+ *                              off_b = sum_{j<b} S_j, unless per-sequence
+ *                              offsets are given (`_ex`).
+ *  seq_lens [B] int32, S_b >= 0 (device memory). S_b = 0 gives out = 0.
+ *  out      [B, h_q, d_head]
+ */
+#ifndef GQA_DECODE_H
+#define GQA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    GQA_OK = 0,
+    GQA_ERR_INVALID_ARG = -1, /* null pointer, bad count, h_q % h_kv != 0, non-finite scale,
+                                 overlapping out, n_splits above GQA_MAX_SPLITS, unknown flag */
+    GQA_ERR_UNSUPPORTED = -2, /* d_head not in {64, 128}, n_rep not in {1, 2, 4, 8, 16},
+                                 unknown dtype or dtype combination */
+    GQA_ERR_WORKSPACE = -3,   /* caller workspace smaller than gqa_decode_workspace_bytes() */
+    GQA_ERR_HIP = -4          /* no device, allocation or launch failure (message kept) */
+};
+
+/* Element types of q/k_cache/v_cache (one type for all three) and of out. */
+enum { GQA_DTYPE_F32 = 0, GQA_DTYPE_BF16 = 1 };
+
+/* Flags of gqa_decode_attn_ex. */
+enum {
+    GQA_FLAG_VALU = 1 /* use the vector-ALU split kernel instead of the matrix-core one
+                         (bf16 inputs; fp32 inputs always use it). For comparison. */
+};
+
+/* Largest split count. */
+#define GQA_MAX_SPLITS 4096
+
+/*
+ * Attention for bf16 q/k_cache/v_cache in the packed layout, fp32 `out`, on
+ * the null stream, with a library-owned workspace (allocated on first use on
+ * each device and grown when needed; it is shared, so calls that may run
+ * concurrently on different streams must use gqa_decode_attn_ex with their
+ * own workspace).
+ *  scale     multiplies q.k before the softmax (1/sqrt(d_head) for Llama).
+ *  n_splits  > 0 forces the number of KV chunks per (sequence, kv head);
+ *            <= 0 lets gqa_decode_pick_splits choose.
+ */
+int gqa_decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* seq_lens, void* out,
+                    int B, int h_q, int h_kv, int d_head,
+                    float scale, int n_splits);
+
+/*
+ * Full form.
+ *  kv_token_offsets  [B] int64 device array of the first token row of each
+ *                    sequence (e.g. b * S_max for a padded [B, S_max, h_kv, d]
+ *                    cache); NULL means the packed layout.
+ *  in_dtype          GQA_DTYPE_BF16 or GQA_DTYPE_F32 (q, k_cache, v_cache).
+ *  out_dtype         GQA_DTYPE_F32, or GQA_DTYPE_BF16 (rounded to nearest even).
+ *  s_kv_hint         host-side upper bound of max_b S_b, or 0 if unknown. Only
+ *                    the split heuristic uses it; the kernels read seq_lens.
+ *  workspace         device buffer of at least gqa_decode_workspace_bytes(B, h_q,
+ *                    d_head, n) bytes, n being the split count that will be used
+ *                    (n_splits if > 0, else gqa_decode_pick_splits(B, h_kv,
+ *                    s_kv_hint, 0)); 256-byte aligned. NULL: library-owned.
+ *  stream            HIP stream (NULL: null stream).
+ *  flags             0 or GQA_FLAG_VALU.
+ */
+int gqa_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* seq_lens, const int64_t* kv_token_offsets,
+                       void* out, int B, int h_q, int h_kv, int d_head,
+                       float scale, int n_splits, int in_dtype, int out_dtype,
+                       int64_t s_kv_hint, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream, int flags);
+
+/*
+ * Split count the library uses when n_splits <= 0: enough workgroups that
+ * every compute unit has work at B = 1, no more chunks than the longest
+ * sequence can fill (when s_kv_max > 0 is known), at most GQA_MAX_SPLITS.
+ * num_cus <= 0 queries the current device (returns a negative status if that
+ * fails). Pure host arithmetic otherwise.
+ */
+int gqa_decode_pick_splits(int B, int h_kv, int64_t s_kv_max, int num_cus);
+
+/* Workspace bytes for n_splits chunks: B*h_q*n_splits*(d_head + 2) floats,
+ * rounded up to 256 bytes. 0 for invalid arguments. */
+size_t gqa_decode_workspace_bytes(int B, int h_q, int d_head, int n_splits);
+
+/*
+ * Profiling: make the calling thread's following gqa_decode_attn* calls
+ * record `before` on their stream right before the split kernel and `after`
+ * right after it (events created by the caller with hipEventCreate), so
+ * hipEventElapsedTime(before, after) is that kernel's duration. NULL, NULL
+ * turns it off. Host-only; returns GQA_OK or GQA_ERR_INVALID_ARG if only one
+ * event is given.
+ */
+int gqa_decode_set_split_events(hipEvent_t before, hipEvent_t after);
+
+/* Static description of a status code. */
+const char* gqa_status_string(int status);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* gqa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_DECODE_H */

@@ -1,0 +1,53 @@
+"""Helpers shared by the GPU tests: upload seeded inputs and run the library."""
+from __future__ import annotations
+
+import numpy as np
+
+import workloads
+
+TOL_F32 = 5e-3      # max abs error vs the fp64 oracle, fp32 output
+TOL_BF16 = 1.6e-2   # max abs error vs the fp64 oracle, bf16-rounded output
+
+
+def to_device(inp: workloads.Inputs, device="cuda"):
+    import torch
+
+    def conv(a):
+        if inp.w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    return conv(inp.q), conv(inp.k), conv(inp.v), torch.from_numpy(inp.seq_lens).to(device)
+
+
+def run_gpu(inp: workloads.Inputs, n_splits=0, out_dtype="f32", valu=False, poison=True,
+            hint=True, dev=None, stream=None):
+    """Run the library on `inp`; returns (out as float64 numpy, split count used).
+
+    The workspace is filled with NaN first, so a chunk the merge reads but no
+    split workgroup wrote shows up as NaN in the output.
+    """
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    q, k, v, lens = dev if dev is not None else to_device(inp)
+    w = inp.w
+    s_max = int(inp.seq_lens.max()) if len(inp.seq_lens) else 0
+    hint_v = s_max if hint else 0
+    ns = n_splits if n_splits > 0 else gqa.gqa_decode_pick_splits(w.B, w.h_kv, hint_v)
+    ws = torch.empty(gqa.gqa_decode_workspace_bytes(w.B, w.h_q, w.d, ns), dtype=torch.uint8, device=q.device)
+    if poison:
+        ws.view(torch.float32).fill_(float("nan"))
+    odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    out = gqa.gqa_decode_attn_ex(q, k, v, lens, scale=float(inp.scale), n_splits=n_splits,
+                                 out_dtype=odt, s_kv_hint=hint_v, workspace=ws, valu=valu,
+                                 stream=stream)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), ns
+
+
+def max_err(got, ref) -> float:
+    ok = ~np.isnan(ref)
+    if not np.all(np.isfinite(got[ok])):
+        return float("inf")
+    return float(np.max(np.abs(got[ok] - ref[ok]))) if ok.any() else 0.0

@@ -1,0 +1,154 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/gqa_decode.h declares, rejects bad arguments on the host before any
+HIP call, and its split heuristic and workspace size follow their contract.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_decode.h")
+
+
+@pytest.fixture(scope="module")
+def gqa():
+    import decode_attention_gqa_amd as m
+    return m
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(gqa_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_pick_splits",
+                            "gqa_decode_workspace_bytes", "gqa_status_string", "gqa_last_error",
+                            "gqa_decode_set_split_events"])
+
+
+def test_library_exports_every_declared_symbol(gqa):
+    lib = ctypes.CDLL(gqa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_constants_match_header(gqa):
+    src = open(HEADER).read()
+    for name in ["GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_WORKSPACE",
+                 "GQA_ERR_HIP", "GQA_DTYPE_F32", "GQA_DTYPE_BF16", "GQA_FLAG_VALU"]:
+        m = re.search(rf"\b{name}\s*=\s*(-?\d+)", src)
+        assert m and int(m.group(1)) == getattr(gqa, name), name
+    assert int(re.search(r"#define GQA_MAX_SPLITS (\d+)", src).group(1)) == gqa.GQA_MAX_SPLITS
+
+
+def test_status_strings(gqa):
+    assert gqa.gqa_status_string(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert gqa.gqa_status_string(s) not in ("ok", "unknown status")
+    assert gqa.gqa_status_string(-99) == "unknown status"
+
+
+# Fake, 256-byte aligned addresses: every call below must fail in the host
+# checks, before any HIP call, so nothing ever dereferences them.
+P = 0x10000
+Q, K, V, L, O, W = (P * i for i in range(1, 7))
+
+
+def call(gqa, **kw):
+    a = dict(q=Q, k=K, v=V, lens=L, offs=None, out=O, B=1, h_q=64, h_kv=8, d=128, scale=0.088,
+             n_splits=0, in_dt=1, out_dt=0, hint=0, ws=None, ws_bytes=0, stream=None, flags=0)
+    a.update(kw)
+    return gqa.lib.gqa_decode_attn_ex(a["q"], a["k"], a["v"], a["lens"], a["offs"], a["out"], a["B"],
+                                      a["h_q"], a["h_kv"], a["d"], a["scale"], a["n_splits"], a["in_dt"],
+                                      a["out_dt"], a["hint"], a["ws"], a["ws_bytes"], a["stream"], a["flags"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(lens=None), -1), (dict(out=None), -1),
+    (dict(B=0), -1), (dict(B=-3), -1), (dict(h_q=0), -1), (dict(h_kv=0), -1), (dict(B=70000), -1),
+    (dict(h_q=60, h_kv=8), -1),                       # not a multiple
+    (dict(h_q=24, h_kv=8), -2),                       # n_rep = 3
+    (dict(h_q=256, h_kv=8), -2),                      # n_rep = 32
+    (dict(d=96), -2), (dict(d=256), -2),
+    (dict(scale=math.inf), -1), (dict(scale=math.nan), -1),
+    (dict(in_dt=2), -2), (dict(out_dt=7), -2),
+    (dict(flags=2), -1),
+    (dict(n_splits=4097), -1),
+    (dict(hint=-1), -1),
+    (dict(q=Q + 8), -1),                              # misaligned
+    (dict(out=Q), -1),                                # out aliases q
+    (dict(out=K), -1),                                # out aliases k
+    (dict(ws=W + 64, ws_bytes=1 << 20), -1),          # workspace not 256-byte aligned
+])
+def test_host_checks_reject_bad_arguments(gqa, kw, status):
+    assert call(gqa, **kw) == status
+    assert gqa.lib.gqa_last_error().decode() != ""
+
+
+def test_base_entry_point_checks_too(gqa):
+    r = gqa.lib.gqa_decode_attn(None, K, V, L, O, 1, 64, 8, 128, 0.088, 0)
+    assert r == gqa.GQA_ERR_INVALID_ARG
+    r = gqa.lib.gqa_decode_attn(Q, K, V, L, O, 1, 64, 8, 80, 0.088, 0)
+    assert r == gqa.GQA_ERR_UNSUPPORTED
+
+
+def test_no_device_is_reported_not_crashed(gqa):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call(gqa) == gqa.GQA_ERR_HIP
+    assert gqa.lib.gqa_decode_pick_splits(1, 8, 8192, 0) == gqa.GQA_ERR_HIP
+
+
+def test_workspace_bytes(gqa):
+    for B, h_q, d, n in [(1, 64, 128, 64), (8, 64, 128, 37), (1, 8, 64, 4), (3, 5, 64, 1)]:
+        o = B * h_q * n * d * 4
+        o = (o + 255) // 256 * 256
+        want = (o + B * h_q * n * 8 + 255) // 256 * 256
+        assert gqa.gqa_decode_workspace_bytes(B, h_q, d, n) == want
+    assert gqa.gqa_decode_workspace_bytes(0, 64, 128, 4) == 0
+    assert gqa.gqa_decode_workspace_bytes(1, 64, 128, 0) == 0
+
+
+@pytest.mark.parametrize("B,h_kv,S", [(1, 8, 8192), (1, 32, 4096), (8, 8, 32768), (1, 8, 1 << 20),
+                                      (1, 2, 256), (1, 8, 0), (64, 8, 100), (1, 1, 1 << 31)])
+def test_split_heuristic_contract(gqa, B, h_kv, S):
+    cus = 256
+    n = gqa.gqa_decode_pick_splits(B, h_kv, S, cus)
+    assert 1 <= n <= gqa.GQA_MAX_SPLITS
+    fill = math.ceil(2 * cus / (B * h_kv))
+    if S == 0:
+        assert n == min(fill, gqa.GQA_MAX_SPLITS)
+    else:
+        # never more chunks than the longest sequence fills with 128 tokens each
+        assert n <= max(1, math.ceil(S / 128))
+        # every CU gets work whenever the sequence is long enough
+        if S >= 128 * fill:
+            assert n * B * h_kv >= 2 * cus
+
+
+def test_split_heuristic_values(gqa):
+    # 70B GQA at B = 1: 8 kv heads x 64 chunks = 512 workgroups of 128 tokens at 8k
+    assert gqa.gqa_decode_pick_splits(1, 8, 8192, 256) == 64
+    assert gqa.gqa_decode_pick_splits(1, 8, 1 << 20, 256) == 256
+    assert gqa.gqa_decode_pick_splits(8, 8, 32768, 256) == 32
+
+
+def test_binding_rejects_cpu_tensors(gqa):
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 8, 64, dtype=torch.bfloat16)
+    kv = torch.zeros(16, 2, 64, dtype=torch.bfloat16)
+    lens = torch.tensor([16], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        gqa.gqa_decode_attn_ex(q, kv, kv, lens)
+
+
+def test_split_events_need_both_or_neither(gqa):
+    assert gqa.lib.gqa_decode_set_split_events(0x1000, None) == gqa.GQA_ERR_INVALID_ARG
+    assert gqa.lib.gqa_decode_set_split_events(None, None) == gqa.GQA_OK

@@ -1,0 +1,185 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle.
+
+Bar: max abs error <= 5e-3 with fp32 output, <= 1.6e-2 with bf16 output, on
+the same seeded inputs. Each case prints its name, shape and error first, so
+a failing run names its case.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import TOL_BF16, TOL_F32, max_err, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def ref_of(inp, heads=None):
+    return oracle.attend(inp.q, inp.k, inp.v, inp.seq_lens, inp.scale, inp.w.h_kv,
+                         dtype=inp.w.dtype, heads=heads)
+
+
+def report(name, err, ns, tol):
+    print(f"[parity] {name}: n_splits={ns} max_abs_err={err:.3e} tol={tol:.1e}", flush=True)
+    assert err <= tol, f"{name}: max abs error {err} > {tol}"
+
+
+@pytest.mark.parametrize("name", ["tiny_gqa_f32", "llama2_7b_mha_s4096", "llama70b_gqa_b1_s8192",
+                                  "llama70b_gqa_b8_ragged"])
+def test_workload_parity(name):
+    inp = workloads.make_inputs(name)
+    print(f"[case] {name} B={inp.w.B} lens={inp.seq_lens.tolist()}", flush=True)
+    got, ns = run_gpu(inp, n_splits=inp.w.n_splits)
+    report(name, max_err(got, ref_of(inp)), ns, TOL_F32)
+
+
+@pytest.mark.parametrize("name", ["llama2_7b_mha_s4096", "llama70b_gqa_b1_s8192"])
+def test_workload_parity_bf16_out(name):
+    inp = workloads.make_inputs(name)
+    got, ns = run_gpu(inp, out_dtype="bf16")
+    report(name + "/bf16-out", max_err(got, ref_of(inp)), ns, TOL_BF16)
+
+
+def test_bf16_output_is_rounded_fp32_output():
+    inp = workloads.make_inputs("llama70b_gqa_b1_s8192")
+    dev = to_device(inp)
+    f32, _ = run_gpu(inp, dev=dev)
+    b16, _ = run_gpu(inp, out_dtype="bf16", dev=dev)
+    rounded = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(f32.astype(np.float32)))
+    np.testing.assert_array_equal(b16, rounded.astype(np.float64))
+
+
+def test_long_context_1m_sampled_heads():
+    """Full-size 1M-token case (4 GiB KV, K ~ N(0, 4)); the oracle computes a
+    sample of heads from 3 of the 8 kv groups, plus the value-hull property on
+    all heads."""
+    inp = workloads.make_inputs("llama70b_gqa_b1_s1m")
+    print(f"[case] 1M B=1 S={int(inp.seq_lens[0])}", flush=True)
+    got, ns = run_gpu(inp)
+    heads = [(0, 0), (0, 5), (0, 13), (0, 63)]
+    report("llama70b_gqa_b1_s1m/sampled", max_err(got, ref_of(inp, heads=heads)), ns, TOL_F32)
+    vmin = workloads.bf16_bits_to_f32(inp.v).min(axis=0)  # [h_kv, d]
+    vmax = workloads.bf16_bits_to_f32(inp.v).max(axis=0)
+    g = np.arange(64) // 8
+    assert np.all(got[0] <= vmax[g] + 1e-6) and np.all(got[0] >= vmin[g] - 1e-6)
+
+
+@pytest.mark.parametrize("valu", [False, True], ids=["mfma", "valu"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n_rep", [1, 2, 4, 8, 16])
+def test_shapes_ragged_tail(n_rep, d, valu):
+    """Several 32/64-token blocks per chunk plus ragged tails, 3 sequences."""
+    inp = workloads.custom(f"grid_r{n_rep}_d{d}", B=3, h_q=2 * n_rep, h_kv=2, d=d,
+                           seq_lens=[1000, 37, 2049], seed=20 + n_rep + d)
+    ref = ref_of(inp)
+    for ns in (0, 7):
+        got, used = run_gpu(inp, n_splits=ns, valu=valu)
+        report(f"grid n_rep={n_rep} d={d} {'valu' if valu else 'mfma'} ns={ns}", max_err(got, ref), used, TOL_F32)
+
+
+@pytest.mark.parametrize("n_rep,d", [(4, 64), (8, 128), (1, 128)])
+def test_fp32_inputs(n_rep, d):
+    inp = workloads.custom("f32", B=2, h_q=2 * n_rep, h_kv=2, d=d, seq_lens=[333, 1200],
+                           dtype="f32", seed=40 + d)
+    got, ns = run_gpu(inp, n_splits=5)
+    report(f"fp32 n_rep={n_rep} d={d}", max_err(got, ref_of(inp)), ns, TOL_F32)
+
+
+@pytest.mark.parametrize("ns", [1, 2, 7, 64, 300, 0])
+def test_split_counts_agree(ns):
+    inp = workloads.make_inputs("llama70b_gqa_b1_s8192")
+    got, used = run_gpu(inp, n_splits=ns)
+    report(f"70B S=8192 ns={ns}", max_err(got, ref_of(inp)), used, TOL_F32)
+
+
+def test_empty_short_and_block_edge_sequences():
+    """S_b = 0, 1 and values around the 32-token block; more chunks than
+    tokens, so some chunks are empty."""
+    lens = [0, 1, 3, 31, 32, 33, 0, 64, 65]
+    inp = workloads.custom("edges", B=len(lens), h_q=16, h_kv=2, d=128, seq_lens=lens, seed=50)
+    ref = ref_of(inp)
+    for ns in (8, 40, 1, 0):
+        for valu in (False, True):
+            got, used = run_gpu(inp, n_splits=ns, valu=valu)
+            report(f"edges ns={ns} valu={valu}", max_err(got, ref), used, TOL_F32)
+            assert np.all(got[0] == 0) and np.all(got[6] == 0)
+
+
+def test_identical_value_rows():
+    inp = workloads.custom("idv", B=2, h_q=64, h_kv=8, d=128, seq_lens=[3000, 517], seed=51)
+    inp.v[:] = inp.v[:1]                               # every row equal to row 0
+    got, ns = run_gpu(inp)
+    want = workloads.bf16_bits_to_f32(inp.v[0]).astype(np.float64)   # [h_kv, d]
+    for h in range(64):
+        np.testing.assert_allclose(got[:, h, :], np.broadcast_to(want[h // 8], (2, 128)), rtol=0, atol=1e-5)
+    report("identical V rows", max_err(got, ref_of(inp)), ns, TOL_F32)
+
+
+def test_one_hot_dominant_score():
+    S, t_star = 5000, 4321
+    inp = workloads.custom("onehot", B=1, h_q=64, h_kv=8, d=128, seq_lens=[S], seed=52)
+    one = workloads.f32_to_bf16_bits(np.float32([1.0]))[0]
+    big = workloads.f32_to_bf16_bits(np.float32([60.0]))[0]
+    inp.q[0, :, :] = 0
+    inp.q[0, :, 0] = one                              # q = e_0 for every head
+    inp.k[:, :, 0] = 0
+    inp.k[t_star, :, 0] = big                         # score gap 60/sqrt(128) ~ 5.3 -> weight ~0.96 ...
+    inp.k[t_star, :, 1:] = 0
+    inp.q[0, :, 1] = one
+    inp.k[t_star, :, 1] = workloads.f32_to_bf16_bits(np.float32([600.0]))[0]   # ... plus 53: one-hot
+    got, ns = run_gpu(inp)
+    want = workloads.bf16_bits_to_f32(inp.v[t_star]).astype(np.float64)
+    for h in range(64):
+        np.testing.assert_allclose(got[0, h], want[h // 8], rtol=0, atol=1e-6)
+
+
+def test_bitwise_deterministic():
+    inp = workloads.make_inputs("llama70b_gqa_b8_ragged")
+    dev = to_device(inp)
+    a, _ = run_gpu(inp, dev=dev)
+    b, _ = run_gpu(inp, dev=dev, poison=False)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_padded_layout_with_token_offsets():
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    lens = np.array([700, 64, 1500], dtype=np.int32)
+    S_max = 1536
+    inp = workloads.custom("padded", B=3, h_q=32, h_kv=4, d=128, seq_lens=lens, seed=53)
+    ref = ref_of(inp)
+    q, k, v, dl = to_device(inp)
+    kp = torch.full((3 * S_max, 4, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vp = torch.full_like(kp, float("nan"))
+    off = np.concatenate([[0], np.cumsum(lens[:-1])])
+    for b in range(3):
+        kp[b * S_max:b * S_max + lens[b]] = k[off[b]:off[b] + lens[b]]
+        vp[b * S_max:b * S_max + lens[b]] = v[off[b]:off[b] + lens[b]]
+    offs = torch.arange(3, dtype=torch.int64, device="cuda") * S_max
+    out = gqa.gqa_decode_attn_ex(q, kp, vp, dl, scale=float(inp.scale), kv_token_offsets=offs,
+                                 s_kv_hint=S_max)
+    torch.cuda.synchronize()
+    report("padded layout", max_err(out.cpu().numpy().astype(np.float64), ref), 0, TOL_F32)
+
+
+def test_base_entry_point_and_library_workspace():
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    inp = workloads.make_inputs("llama70b_gqa_b1_s8192")
+    q, k, v, dl = to_device(inp)
+    ref = ref_of(inp)
+    for ns in (0, 16, 128):                            # the library workspace grows
+        out = gqa.gqa_decode_attn(q, k, v, dl, scale=float(inp.scale), n_splits=ns)
+        torch.cuda.synchronize()
+        report(f"base entry ns={ns}", max_err(out.cpu().numpy().astype(np.float64), ref), ns, TOL_F32)
+
+
+def test_runs_on_a_side_stream():
+    import torch
+    inp = workloads.make_inputs("llama2_7b_mha_s4096")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got, ns = run_gpu(inp, stream=s)
+    report("side stream", max_err(got, ref_of(inp)), ns, TOL_F32)
