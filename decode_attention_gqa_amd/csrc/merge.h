@@ -2,10 +2,16 @@
 // (sequence, query head) and the final division o / l.
 //
 // The combination follows the kernbench2 page `_attention_mesh_mlo.py`
-// (receive-and-merge blocks, then o / l), applied to all chunks at once:
+// (receive-and-merge blocks, then o / l), applied to many chunks at once:
 // with M = max_s m_s and w_s = exp(m_s - M) (exp2 here: m is in log2 units),
 //   out = (sum_s w_s o_s) / (sum_s w_s l_s).
 // Every chunk below n_active is non-empty, so M is finite and l > 0.
+//
+// One workgroup per (sequence, head). Its threads form SLOTS row slots of
+// D/4 lanes (a float4 of the row each); a slot takes every SLOTS-th chunk,
+// U chunks per round with all their loads issued before any is used, and
+// keeps its own running (m, l, o) - the same merge rule applied
+// incrementally. The slots' states are merged once more through LDS.
 #pragma once
 
 #include "gqa_common.h"
@@ -25,10 +31,16 @@ __device__ __forceinline__ void store4<__bf16>(__bf16* p, float4 v) {
   *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, h);
 }
 
+// exp2(m - M) for a state that may be empty (m = -inf); M is finite or -inf.
+__device__ __forceinline__ float rescale(float m, float M) {
+  return (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+}
+
 template <int D, typename TO>
 __global__ __launch_bounds__(256) void merge_splits(MergeArgs a) {
   constexpr int LPS = D / 4;                 // lanes per chunk row (float4 each)
   constexpr int SLOTS = 256 / LPS;           // chunks processed side by side
+  constexpr int U = 8;                       // chunks per slot per round
   const int bh = blockIdx.x;
   const int b = bh / a.h_q;
   const int tid = threadIdx.x;
@@ -43,46 +55,65 @@ __global__ __launch_bounds__(256) void merge_splits(MergeArgs a) {
   }
   const float2* ml = a.ws_ml + (int64_t)bh * a.n_splits;
   const float* o = a.ws_o + (int64_t)bh * a.n_splits * D;
-
-  __shared__ float red[4];
-  __shared__ float4 sacc[SLOTS][LPS];
-  __shared__ float sl[SLOTS];
-
-  float mx = -INFINITY;
-  for (int i = tid; i < n_active; i += 256) mx = fmaxf(mx, ml[i].x);
-#pragma unroll
-  for (int k = 32; k > 0; k >>= 1) mx = fmaxf(mx, __shfl_xor(mx, k));
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-
   const int slot = tid / LPS, q = tid % LPS;
+
+  float m = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float L = 0.f;
-  for (int i = slot; i < n_active; i += SLOTS) {
-    const float2 v = ml[i];
-    const float f = fast_exp2(v.x - M);
-    const float4 x = *reinterpret_cast<const float4*>(o + (int64_t)i * D + 4 * q);
-    acc.x += f * x.x;
-    acc.y += f * x.y;
-    acc.z += f * x.z;
-    acc.w += f * x.w;
-    L += f * v.y;
+  for (int base = 0; base < n_active; base += SLOTS * U) {
+    float2 mv[U];
+    float4 ov[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * SLOTS + slot;
+      if (i < n_active) {
+        mv[u] = ml[i];
+        ov[u] = *reinterpret_cast<const float4*>(o + (int64_t)i * D + 4 * q);
+      } else {
+        mv[u] = make_float2(-INFINITY, 0.f);
+        ov[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    float mn = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mn = fmaxf(mn, mv[u].x);
+    const float f0 = rescale(m, mn);
+    acc.x *= f0; acc.y *= f0; acc.z *= f0; acc.w *= f0;
+    L *= f0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float f = rescale(mv[u].x, mn);
+      acc.x += f * ov[u].x;
+      acc.y += f * ov[u].y;
+      acc.z += f * ov[u].z;
+      acc.w += f * ov[u].w;
+      L += f * mv[u].y;
+    }
+    m = mn;
   }
+
+  __shared__ float sm[SLOTS], sl[SLOTS];
+  __shared__ float4 sacc[SLOTS][LPS];
   sacc[slot][q] = acc;
-  if (q == 0) sl[slot] = L;
+  if (q == 0) {
+    sm[slot] = m;
+    sl[slot] = L;
+  }
   __syncthreads();
   if (tid < LPS) {
-    float4 r = sacc[0][tid];
-    float Lt = sl[0];
+    float M = sm[0];
 #pragma unroll
-    for (int k = 1; k < SLOTS; ++k) {
+    for (int k = 1; k < SLOTS; ++k) M = fmaxf(M, sm[k]);
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+    float Lt = 0.f;
+#pragma unroll
+    for (int k = 0; k < SLOTS; ++k) {
+      const float f = rescale(sm[k], M);
       const float4 y = sacc[k][tid];
-      r.x += y.x;
-      r.y += y.y;
-      r.z += y.z;
-      r.w += y.w;
-      Lt += sl[k];
+      r.x += f * y.x;
+      r.y += f * y.y;
+      r.z += f * y.z;
+      r.w += f * y.w;
+      Lt += f * sl[k];
     }
     const float inv = 1.f / Lt;
     store4<TO>(out + 4 * tid, make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv));
