@@ -39,6 +39,13 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is not built; run `python decode_attention_gqa_amd/build.py` "
         "(or __graft_entry__.build()). There is no non-HIP fallback.")
 
+# torch ships its own HIP runtime (torch/lib/libamdhip64.so, soname
+# libamdhip64.so.7). Import it first so the library's libamdhip64.so.7
+# dependency resolves to that already-loaded copy: loading the library first
+# would bring in the system runtime, torch would then load its copy too, and
+# two HIP runtimes in one process do not share devices or streams.
+import torch  # noqa: E402,F401
+
 lib = ctypes.CDLL(LIB_PATH)
 
 _vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float

@@ -70,4 +70,17 @@ __device__ __forceinline__ int64_t seq_offset(const int32_t* seq_lens, const int
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// (split s, kv head g, sequence b) of a split workgroup. Splits vary fastest
+// in the grid: measured against kv-head-fastest and an XCD-grouped order, this
+// order streams long sequences fastest (1M tokens: 722 us vs 769 and 747 us).
+struct WgCoord {
+  int s, g, b;
+};
+__device__ __forceinline__ WgCoord wg_coord() {
+  return {(int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z};
+}
+inline dim3 split_grid(int n_splits, int h_kv, int B) {
+  return dim3((unsigned)n_splits, (unsigned)h_kv, (unsigned)B);
+}
+
 }  // namespace gqa

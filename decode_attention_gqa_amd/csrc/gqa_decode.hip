@@ -243,7 +243,7 @@ int gqa_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
 
   gqa::SplitArgs sa{q, k_cache, v_cache, seq_lens, kv_token_offsets, ws_o, ws_ml,
                     h_q, h_kv, ns, min_chunk, scale * gqa::kLog2e};
-  const dim3 grid((unsigned)ns, (unsigned)h_kv, (unsigned)B);
+  const dim3 grid = gqa::split_grid(ns, h_kv, B);
   const bool bf16 = in_dtype == GQA_DTYPE_BF16;
   const bool valu = (flags & GQA_FLAG_VALU) != 0;
   hipError_t e;

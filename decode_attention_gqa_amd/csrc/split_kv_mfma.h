@@ -157,7 +157,8 @@ template <int D, int NREP>
 __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
   constexpr int KS = MfmaTile<D>::KS, NT = MfmaTile<D>::NT;
   static_assert(NREP >= 1 && NREP <= 16, "one 16-wide MFMA tile holds the query heads of a group");
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const WgCoord wc = wg_coord();
+  const int s = wc.s, g = wc.g, b = wc.b;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = lane >> 4, n = lane & 15;
 

@@ -57,7 +57,8 @@ template <typename T, int D, int NREP>
 __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
   constexpr int DPL = D / 64;                      // output dimensions per lane
   constexpr int TB = 64;                           // tokens per block (one per lane)
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const WgCoord wc = wg_coord();
+  const int s = wc.s, g = wc.g, b = wc.b;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
   const int64_t S = a.seq_lens[b];
