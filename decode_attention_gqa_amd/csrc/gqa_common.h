@@ -39,21 +39,21 @@ struct MergeArgs {
   int min_chunk;
 };
 
-__device__ __forceinline__ int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
 // Chunk length and number of non-empty chunks of a sequence of S tokens.
 // The split kernels and the merge kernel both use this, so they agree on
 // which chunks exist: chunk s covers tokens [s*c, min(S, (s+1)*c)).
-__device__ __forceinline__ void chunking(int64_t S, int n_splits, int min_chunk,
-                                         int64_t& c, int& n_active) {
+// 32-bit unsigned arithmetic suffices: S < 2^31 and n_splits <= 4096, so
+// S + c - 1 < 2^32.
+__device__ __forceinline__ void chunking(int S, int n_splits, int min_chunk, int& c, int& n_active) {
   if (S <= 0) {
     c = 0;
     n_active = 0;
     return;
   }
-  c = ceil_div64(S, n_splits);
-  if (c < min_chunk) c = min_chunk;
-  n_active = (int)ceil_div64(S, c);
+  unsigned uc = ((unsigned)S + (unsigned)n_splits - 1u) / (unsigned)n_splits;
+  if (uc < (unsigned)min_chunk) uc = (unsigned)min_chunk;
+  c = (int)uc;
+  n_active = (int)(((unsigned)S + uc - 1u) / uc);
 }
 
 // First token row of sequence b: explicit offsets, or the packed prefix sum
@@ -61,6 +61,7 @@ __device__ __forceinline__ void chunking(int64_t S, int n_splits, int min_chunk,
 __device__ __forceinline__ int64_t seq_offset(const int32_t* seq_lens, const int64_t* kv_off,
                                               int b, int lane) {
   if (kv_off) return kv_off[b];
+  if (b == 0) return 0;
   int64_t acc = 0;
   for (int j = lane; j < b; j += 64) acc += seq_lens[j];
 #pragma unroll

@@ -5,7 +5,8 @@
 // (receive-and-merge blocks, then o / l), applied to many chunks at once:
 // with M = max_s m_s and w_s = exp(m_s - M) (exp2 here: m is in log2 units),
 //   out = (sum_s w_s o_s) / (sum_s w_s l_s).
-// Every chunk below n_active is non-empty, so M is finite and l > 0.
+// Every chunk below n_active is non-empty, so M is finite and l > 0 unless
+// the sequence is empty.
 //
 // One workgroup per (sequence, head). Its threads form SLOTS row slots of
 // D/4 lanes (a float4 of the row each); a slot takes every SLOTS-th chunk,
@@ -45,50 +46,58 @@ __global__ __launch_bounds__(256) void merge_splits(MergeArgs a) {
   const int b = bh / a.h_q;
   const int tid = threadIdx.x;
   TO* out = static_cast<TO*>(a.out) + (int64_t)bh * D;
-
-  int64_t c;
-  int n_active;
-  chunking(a.seq_lens[b], a.n_splits, a.min_chunk, c, n_active);
-  if (n_active == 0) {                       // empty sequence: nothing attended
-    if (tid < LPS) store4<TO>(out + 4 * tid, make_float4(0.f, 0.f, 0.f, 0.f));
-    return;
-  }
   const float2* ml = a.ws_ml + (int64_t)bh * a.n_splits;
   const float* o = a.ws_o + (int64_t)bh * a.n_splits * D;
   const int slot = tid / LPS, q = tid % LPS;
 
+  // The loads of a round do not wait for seq_lens: indices are clamped into
+  // [0, n_splits), so every load is in bounds and none sits in a branch, and
+  // rows of chunks that turn out to be empty (never written by the split
+  // kernel) are discarded, before any use, once seq_lens has arrived.
   float m = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int base = 0; base < n_active; base += SLOTS * U) {
-    float2 mv[U];
-    float4 ov[U];
+  float2 mv[U];
+  float4 ov[U];
+  auto load_round = [&](int base) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = base + u * SLOTS + slot;
-      if (i < n_active) {
-        mv[u] = ml[i];
-        ov[u] = *reinterpret_cast<const float4*>(o + (int64_t)i * D + 4 * q);
-      } else {
-        mv[u] = make_float2(-INFINITY, 0.f);
-        ov[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      const int i = min(base + u * SLOTS + slot, a.n_splits - 1);
+      mv[u] = ml[i];
+      ov[u] = *reinterpret_cast<const float4*>(o + (int64_t)i * D + 4 * q);
     }
+  };
+  auto merge_round = [&](int base, int n_active) {
+    bool act[U];
     float mn = m;
 #pragma unroll
-    for (int u = 0; u < U; ++u) mn = fmaxf(mn, mv[u].x);
+    for (int u = 0; u < U; ++u) {
+      act[u] = base + u * SLOTS + slot < n_active;
+      if (act[u]) mn = fmaxf(mn, mv[u].x);
+    }
     const float f0 = rescale(m, mn);
     acc.x *= f0; acc.y *= f0; acc.z *= f0; acc.w *= f0;
     L *= f0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float f = rescale(mv[u].x, mn);
-      acc.x += f * ov[u].x;
-      acc.y += f * ov[u].y;
-      acc.z += f * ov[u].z;
-      acc.w += f * ov[u].w;
-      L += f * mv[u].y;
+      if (act[u]) {
+        const float f = fast_exp2(mv[u].x - mn);
+        acc.x += f * ov[u].x;
+        acc.y += f * ov[u].y;
+        acc.z += f * ov[u].z;
+        acc.w += f * ov[u].w;
+        L += f * mv[u].y;
+      }
     }
     m = mn;
+  };
+  load_round(0);
+  __builtin_amdgcn_sched_barrier(0);           // keep the first loads ahead of the seq_lens wait
+  int c, n_active;
+  chunking(a.seq_lens[b], a.n_splits, a.min_chunk, c, n_active);
+  merge_round(0, n_active);
+  for (int base = SLOTS * U; base < n_active; base += SLOTS * U) {
+    load_round(base);
+    merge_round(base, n_active);
   }
 
   __shared__ float sm[SLOTS], sl[SLOTS];
@@ -115,7 +124,8 @@ __global__ __launch_bounds__(256) void merge_splits(MergeArgs a) {
       r.w += f * y.w;
       Lt += f * sl[k];
     }
-    const float inv = 1.f / Lt;
+    // Lt = 0 only for an empty sequence (S = 0): nothing attended, out = 0.
+    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
     store4<TO>(out + 4 * tid, make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv));
   }
 }

@@ -162,13 +162,12 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = lane >> 4, n = lane & 15;
 
-  const int64_t S = a.seq_lens[b];
-  int64_t c;
-  int n_active;
+  const int S = a.seq_lens[b];
+  int c, n_active;
   chunking(S, a.n_splits, a.min_chunk, c, n_active);
   if (s >= n_active) return;                       // the merge reads chunks < n_active only
   const int64_t t0 = (int64_t)s * c;
-  const int64_t ntok = (S - t0 < c) ? (S - t0) : c;
+  const int ntok = (int)min<int64_t>((int64_t)S - t0, c);
   const int64_t off = seq_offset(a.seq_lens, a.kv_off, b, lane);
 
   const int64_t rs = (int64_t)a.h_kv * D;          // elements between consecutive tokens
@@ -193,18 +192,18 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   SoftmaxState st{-INFINITY, 0.f};
 
-  const int nblk = (int)((ntok + 31) / 32);
+  const int nblk = (ntok >> 5) + ((ntok & 31) != 0);
   int blk = w;
   if (blk < nblk) {
     KVRegs<D> cur, nxt;
-    int nv = (int)min<int64_t>(32, ntok - (int64_t)blk * 32);
+    int nv = min(32, ntok - blk * 32);
     load_block<D>(cur, kbase + (int64_t)blk * 32 * rs, vbase + (int64_t)blk * 32 * rs, rs, grp, n, nv);
     while (true) {
       const int nb = blk + kWaves;
       const bool more = nb < nblk;
       int nvn = 0;
       if (more) {                                  // prefetch the next block before computing
-        nvn = (int)min<int64_t>(32, ntok - (int64_t)nb * 32);
+        nvn = min(32, ntok - nb * 32);
         load_block<D>(nxt, kbase + (int64_t)nb * 32 * rs, vbase + (int64_t)nb * 32 * rs, rs, grp, n, nvn);
       }
       compute_block<D>(cur, qop, acc, st, a.scale_log2, grp, nv);

@@ -61,13 +61,12 @@ __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
   const int s = wc.s, g = wc.g, b = wc.b;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
-  const int64_t S = a.seq_lens[b];
-  int64_t c;
-  int n_active;
+  const int S = a.seq_lens[b];
+  int c, n_active;
   chunking(S, a.n_splits, a.min_chunk, c, n_active);
   if (s >= n_active) return;
   const int64_t t0 = (int64_t)s * c;
-  const int64_t ntok = (S - t0 < c) ? (S - t0) : c;
+  const int ntok = (int)min<int64_t>((int64_t)S - t0, c);
   const int64_t off = seq_offset(a.seq_lens, a.kv_off, b, lane);
   const int64_t rs = (int64_t)a.h_kv * D;
   const T* kbase = static_cast<const T*>(a.k) + ((off + t0) * a.h_kv + g) * D;
@@ -90,9 +89,9 @@ __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
     for (int e = 0; e < DPL; ++e) o[h][e] = 0.f;
   }
 
-  const int nblk = (int)((ntok + TB - 1) / TB);
+  const int nblk = ntok / TB + (ntok % TB != 0);
   for (int blk = w; blk < nblk; blk += kWaves) {
-    const int nv = (int)min<int64_t>(TB, ntok - (int64_t)blk * TB);
+    const int nv = min(TB, ntok - blk * TB);
     const bool valid = lane < nv;
     const T* krow = kbase + ((int64_t)blk * TB + (valid ? lane : nv - 1)) * rs;
     float x[NREP];
