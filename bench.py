@@ -11,8 +11,9 @@ L2s cannot serve the KV cache from one call to the next). Prints ONE JSON line.
 
 Metric: effective KV GB/s = K and V bytes the call attends (each read once)
 divided by the time per call, and its fraction of the 8 TB/s HBM peak.
-`roofline.achieved` uses the split kernel's own duration, measured with HIP
-events recorded on its stream right before and after it.
+`roofline.achieved` uses the split kernel's own duration: HIP events recorded
+on the launch stream around a replay of a graph of K split-only launches
+(gqa_decode_partial), divided by K.
 `cpu_baseline` times the fp64 oracle on one host thread in a subprocess.
 """
 from __future__ import annotations
@@ -23,7 +24,6 @@ import hashlib
 import json
 import math
 import os
-import statistics
 import subprocess
 import sys
 import time
@@ -145,6 +145,8 @@ def main() -> int:
     ap.add_argument("--n-splits", type=int, default=0)
     ap.add_argument("--valu", action="store_true", help="vector-ALU split kernel (comparison)")
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of a HIP graph")
+    ap.add_argument("--fused", action="store_true",
+                    help="single-launch form (GQA_FLAG_FUSED) instead of split + merge kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -204,7 +206,7 @@ def main() -> int:
     def call(i):
         q, k, v = sets[i % R]
         gqa.gqa_decode_attn_ex(q, k, v, lens, out, scale=scale, n_splits=args.n_splits,
-                               s_kv_hint=s_max, workspace=ws, valu=args.valu)
+                               s_kv_hint=s_max, workspace=ws, valu=args.valu, fused=args.fused)
 
     stream = torch.cuda.Stream()
     hip = Hip()
@@ -236,20 +238,37 @@ def main() -> int:
         log(f"[bench] timed {args.steps} calls")
         sec_per_call = (t1 - t0) / args.steps
 
-        # ---- split kernel alone, HIP events on its stream (eager calls)
-        n_ev = min(args.steps, 100)
-        evs = [(hip.event(), hip.event()) for _ in range(n_ev)]
-        for i in range(n_ev):
-            assert gqa.lib.gqa_decode_set_split_events(evs[i][0], evs[i][1]) == 0
-            call(i)
-        assert gqa.lib.gqa_decode_set_split_events(None, None) == 0
+        # ---- the split kernel alone: a HIP graph of K split-only launches
+        # (gqa_decode_partial) over the same rotating inputs, with HIP events
+        # recorded on the launch stream around one replay.
+        def partial(i):
+            q, k, v = sets[i % R]
+            gqa.gqa_decode_partial(q, k, v, lens, ws, scale=scale, n_splits=args.n_splits,
+                                   s_kv_hint=s_max, valu=args.valu)
+
+        if args.eager:
+            graph_p = None
+        else:
+            graph_p = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph_p, stream=stream):
+                for i in range(args.steps):
+                    partial(i)
+            graph_p.replay()
         torch.cuda.synchronize()
-        split_ms = [hip.elapsed_ms(a, b) for a, b in evs]
-        for a, b in evs:
-            hip.lib.hipEventDestroy(a)
-            hip.lib.hipEventDestroy(b)
-    split_us = statistics.mean(split_ms) * 1e3
-    log(f"[bench] split kernel: mean {split_us:.2f} us, median {statistics.median(split_ms) * 1e3:.2f} us")
+        e0, e1 = hip.event(), hip.event()
+        hip.lib.hipEventRecord(e0, ctypes.c_void_p(stream.cuda_stream))
+        if graph_p is not None:
+            graph_p.replay()
+        else:
+            for i in range(args.steps):
+                partial(i)
+        hip.lib.hipEventRecord(e1, ctypes.c_void_p(stream.cuda_stream))
+        split_us = hip.elapsed_ms(e0, e1) * 1e3 / args.steps
+        hip.lib.hipEventDestroy(e0)
+        hip.lib.hipEventDestroy(e1)
+        call(0)
+        torch.cuda.synchronize()
+    log(f"[bench] split kernel alone: {split_us:.2f} us per launch")
 
     # sanity: finite output
     if not torch.isfinite(out).all():
@@ -277,6 +296,7 @@ def main() -> int:
             "kv_bytes_per_call": kv_bytes, "n_splits": ns,
             "split_kernel": "valu" if args.valu else ("mfma" if w.dtype == "bf16" else "valu"),
             "timing": "eager calls" if args.eager else "one HIP graph holding the K calls",
+            "launches_per_call": 1 if args.fused else 2,
             "rotating_input_sets": R,
         },
         "us_per_call": sec_per_call * 1e6,

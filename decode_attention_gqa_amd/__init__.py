@@ -16,10 +16,12 @@ import math
 import os
 
 __all__ = [
-    "gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_pick_splits",
+    "gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_partial", "gqa_decode_merge",
+    "gqa_decode_pick_splits",
     "gqa_decode_workspace_bytes", "gqa_status_string", "GQAError", "lib", "LIB_PATH",
     "GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_WORKSPACE", "GQA_ERR_HIP",
-    "GQA_DTYPE_F32", "GQA_DTYPE_BF16", "GQA_FLAG_VALU", "GQA_MAX_SPLITS",
+    "GQA_DTYPE_F32", "GQA_DTYPE_BF16", "GQA_FLAG_VALU", "GQA_FLAG_FUSED", "GQA_MAX_SPLITS",
+    "workspace_layout",
 ]
 
 GQA_OK = 0
@@ -30,6 +32,7 @@ GQA_ERR_HIP = -4
 GQA_DTYPE_F32 = 0
 GQA_DTYPE_BF16 = 1
 GQA_FLAG_VALU = 1
+GQA_FLAG_FUSED = 2
 GQA_MAX_SPLITS = 4096
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_decode.so")
@@ -54,6 +57,11 @@ lib.gqa_decode_attn.restype = _i32
 lib.gqa_decode_attn_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32,
                                    _i32, _i32, _i64, _vp, _sz, _vp, _i32]
 lib.gqa_decode_attn_ex.restype = _i32
+lib.gqa_decode_partial.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i64,
+                                   _vp, _sz, _vp, _i32]
+lib.gqa_decode_partial.restype = _i32
+lib.gqa_decode_merge.argtypes = [_vp, _vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _vp]
+lib.gqa_decode_merge.restype = _i32
 lib.gqa_decode_pick_splits.argtypes = [_i32, _i32, _i64, _i32]
 lib.gqa_decode_pick_splits.restype = _i32
 lib.gqa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
@@ -89,6 +97,17 @@ def gqa_decode_workspace_bytes(B: int, h_q: int, d_head: int, n_splits: int) -> 
     return int(lib.gqa_decode_workspace_bytes(B, h_q, d_head, n_splits))
 
 
+def workspace_layout(B: int, h_q: int, d_head: int, n_splits: int) -> dict:
+    """Byte offsets of the workspace parts, as include/gqa_decode.h documents
+    them: arrival counters at 0, partial outputs at `o`, (m, l) pairs at `ml`;
+    `total` equals gqa_decode_workspace_bytes."""
+    r = lambda x: (x + 255) // 256 * 256
+    rows = B * h_q * n_splits
+    o = r(B * h_q * 8)
+    ml = o + r(rows * d_head * 4)
+    return {"counters": 0, "o": o, "ml": ml, "total": ml + r(rows * 8)}
+
+
 def _torch():
     import torch
     return torch
@@ -105,7 +124,7 @@ def _dtype_code(dt) -> int:
 
 def gqa_decode_attn_ex(q, k_cache, v_cache, seq_lens, out=None, *, scale=None, n_splits=0,
                        out_dtype=None, s_kv_hint=0, kv_token_offsets=None, workspace=None,
-                       stream=None, valu=False):
+                       stream=None, valu=False, fused=False):
     """Decode attention for one query token per sequence.
 
     q [B, h_q, d], k_cache / v_cache [T, h_kv, d] (packed by default), seq_lens [B]
@@ -116,20 +135,7 @@ def gqa_decode_attn_ex(q, k_cache, v_cache, seq_lens, out=None, *, scale=None, n
     torch = _torch()
     B, h_q, d = q.shape
     h_kv = k_cache.shape[1]
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
-        raise TypeError("q, k_cache and v_cache must share one dtype")
-    if k_cache.dim() != 3 or k_cache.shape != v_cache.shape or k_cache.shape[2] != d:
-        raise ValueError("k_cache and v_cache must be [T, h_kv, d_head]")
-    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
-        raise ValueError("seq_lens must be int32 [B]")
-    if kv_token_offsets is not None and (kv_token_offsets.dtype != torch.int64
-                                         or kv_token_offsets.shape != (B,) or not kv_token_offsets.is_cuda):
-        raise ValueError("kv_token_offsets must be an int64 [B] GPU tensor")
+    _check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out_dtype = out_dtype or torch.float32
@@ -150,9 +156,71 @@ def gqa_decode_attn_ex(q, k_cache, v_cache, seq_lens, out=None, *, scale=None, n
             _dtype_code(q.dtype), _dtype_code(out_dtype), int(s_kv_hint),
             workspace.data_ptr() if workspace is not None else None,
             workspace.numel() * workspace.element_size() if workspace is not None else 0,
-            ctypes.c_void_p(st.cuda_stream), GQA_FLAG_VALU if valu else 0)
+            ctypes.c_void_p(st.cuda_stream),
+            (GQA_FLAG_VALU if valu else 0) | (GQA_FLAG_FUSED if fused else 0))
     if r != GQA_OK:
         raise GQAError(r, "gqa_decode_attn_ex")
+    return out
+
+
+def _check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets):
+    torch = _torch()
+    B, h_q, d = q.shape
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share one dtype")
+    if k_cache.dim() != 3 or k_cache.shape != v_cache.shape or k_cache.shape[2] != d:
+        raise ValueError("k_cache and v_cache must be [T, h_kv, d_head]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    if kv_token_offsets is not None and (kv_token_offsets.dtype != torch.int64
+                                         or kv_token_offsets.shape != (B,) or not kv_token_offsets.is_cuda):
+        raise ValueError("kv_token_offsets must be an int64 [B] GPU tensor")
+
+
+def gqa_decode_partial(q, k_cache, v_cache, seq_lens, workspace, *, scale=None, n_splits=0,
+                       s_kv_hint=0, kv_token_offsets=None, stream=None, valu=False):
+    """Split kernel only: writes the per-chunk (m, l, o) triplets into
+    `workspace` (a uint8 GPU tensor, see gqa_decode_workspace_bytes)."""
+    torch = _torch()
+    _check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets)
+    B, h_q, d = q.shape
+    h_kv = k_cache.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    with torch.cuda.device(q.device):
+        st = stream if stream is not None else torch.cuda.current_stream(q.device)
+        r = lib.gqa_decode_partial(
+            q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+            kv_token_offsets.data_ptr() if kv_token_offsets is not None else None,
+            B, h_q, h_kv, d, float(scale), int(n_splits), _dtype_code(q.dtype), int(s_kv_hint),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            ctypes.c_void_p(st.cuda_stream), GQA_FLAG_VALU if valu else 0)
+    if r != GQA_OK:
+        raise GQAError(r, "gqa_decode_partial")
+
+
+def gqa_decode_merge(seq_lens, workspace, out, *, h_kv, n_splits=0, s_kv_hint=0, stream=None):
+    """Merge the triplets a gqa_decode_partial call (same seq_lens, shapes,
+    n_splits and s_kv_hint) wrote, into out [B, h_q, d] (fp32 or bf16)."""
+    torch = _torch()
+    B, h_q, d = out.shape
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,) or not seq_lens.is_cuda:
+        raise ValueError("seq_lens must be an int32 [B] GPU tensor")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    with torch.cuda.device(out.device):
+        st = stream if stream is not None else torch.cuda.current_stream(out.device)
+        r = lib.gqa_decode_merge(seq_lens.data_ptr(), workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), out.data_ptr(),
+                                 B, h_q, h_kv, d, int(n_splits), int(s_kv_hint),
+                                 _dtype_code(out.dtype), ctypes.c_void_p(st.cuda_stream))
+    if r != GQA_OK:
+        raise GQAError(r, "gqa_decode_merge")
     return out
 
 

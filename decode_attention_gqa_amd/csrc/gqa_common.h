@@ -27,6 +27,12 @@ struct SplitArgs {
   int n_splits;
   int min_chunk;              // lower bound of the chunk length (tokens)
   float scale_log2;           // scale * log2(e): scores are kept in log2 units
+  // single-launch form only (see fused_tail.h)
+  int fused;                  // 1: the last workgroup of each group merges and writes out
+  int out_bf16;               // out is bf16 (else fp32)
+  void* out;                  // [B, h_q, D]
+  unsigned long long* counters;   // [B * h_kv] arrival counters: (call tag << 16) | arrivals
+  unsigned long long tag;     // this call's tag (48 bits), see fused_tail.h
 };
 
 struct MergeArgs {

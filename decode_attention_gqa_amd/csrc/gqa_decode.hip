@@ -7,11 +7,13 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
 
 #include "gqa_common.h"
+#include "fused_tail.h"
 #include "merge.h"
 #include "split_kv_mfma.h"
 #include "split_kv_valu.h"
@@ -20,6 +22,7 @@ namespace {
 
 thread_local std::string g_last_error;
 thread_local hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
+std::atomic<unsigned long long> g_call_tag{1};   // tags of single-launch calls (48 bits used)
 
 int fail(int status, const char* fmt, ...) {
   char buf[512];
@@ -82,13 +85,22 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-size_t ws_bytes(int B, int h_q, int d, int n) {
+// Workspace layout, 256-byte aligned parts: arrival counters [B * h_kv] (room
+// for B * h_q) uint64 at 0, so their place does not depend on the split
+// count; o [B, h_q, n, d] fp32 at o_off; (m, l) [B, h_q, n] fp32 at ml_off.
+struct WsLayout {
+  size_t o_off, ml_off, total;
+};
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+WsLayout ws_layout(int B, int h_q, int d, int n) {
   const size_t rows = (size_t)B * h_q * n;
-  size_t o = rows * d * sizeof(float);
-  o = (o + 255) & ~(size_t)255;
-  size_t ml = rows * sizeof(float2);
-  return (o + ml + 255) & ~(size_t)255;
+  WsLayout l;
+  l.o_off = round256((size_t)B * h_q * sizeof(unsigned long long));
+  l.ml_off = l.o_off + round256(rows * d * sizeof(float));
+  l.total = l.ml_off + round256(rows * sizeof(float2));
+  return l;
 }
+size_t ws_bytes(int B, int h_q, int d, int n) { return ws_layout(B, h_q, d, n).total; }
 
 // ---------------------------------------------------------------- launches
 template <int D, int NREP>
@@ -185,67 +197,97 @@ int gqa_decode_pick_splits(int B, int h_kv, int64_t s_kv_max, int num_cus) {
   return pick_splits_host(B, h_kv, s_kv_max, num_cus);
 }
 
-int gqa_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
-                       const int32_t* seq_lens, const int64_t* kv_token_offsets,
-                       void* out, int B, int h_q, int h_kv, int d_head,
-                       float scale, int n_splits, int in_dtype, int out_dtype,
-                       int64_t s_kv_hint, void* workspace, size_t workspace_bytes,
-                       hipStream_t stream, int flags) {
-  // ---- host-side checks, before any HIP call
-  if (!q || !k_cache || !v_cache || !seq_lens || !out)
-    return fail(GQA_ERR_INVALID_ARG, "null tensor pointer");
+}  // extern "C"
+
+namespace {
+
+// Checks shared by every compute entry point (host only, no HIP call).
+int check_shape(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_hint) {
   if (B < 1 || h_q < 1 || h_kv < 1) return fail(GQA_ERR_INVALID_ARG, "B, h_q, h_kv must be >= 1");
   if (B > 65535 || h_kv > 65535) return fail(GQA_ERR_INVALID_ARG, "B and h_kv must be <= 65535");
   if (h_q % h_kv) return fail(GQA_ERR_INVALID_ARG, "h_q (%d) is not a multiple of h_kv (%d)", h_q, h_kv);
-  const int nrep = h_q / h_kv;
-  if (!valid_nrep(nrep)) return fail(GQA_ERR_UNSUPPORTED, "h_q / h_kv = %d not in {1, 2, 4, 8, 16}", nrep);
+  if (!valid_nrep(h_q / h_kv))
+    return fail(GQA_ERR_UNSUPPORTED, "h_q / h_kv = %d not in {1, 2, 4, 8, 16}", h_q / h_kv);
   if (d_head != 64 && d_head != 128) return fail(GQA_ERR_UNSUPPORTED, "d_head %d not in {64, 128}", d_head);
+  if (n_splits > GQA_MAX_SPLITS) return fail(GQA_ERR_INVALID_ARG, "n_splits %d > %d", n_splits, GQA_MAX_SPLITS);
+  if (s_kv_hint < 0) return fail(GQA_ERR_INVALID_ARG, "s_kv_hint < 0");
+  return GQA_OK;
+}
+
+int check_inputs(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                 const int64_t* kv_token_offsets, float scale, int in_dtype, int flags) {
+  if (!q || !k_cache || !v_cache || !seq_lens) return fail(GQA_ERR_INVALID_ARG, "null tensor pointer");
   if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale is not finite");
   if (in_dtype != GQA_DTYPE_F32 && in_dtype != GQA_DTYPE_BF16)
     return fail(GQA_ERR_UNSUPPORTED, "in_dtype %d", in_dtype);
-  if (out_dtype != GQA_DTYPE_F32 && out_dtype != GQA_DTYPE_BF16)
-    return fail(GQA_ERR_UNSUPPORTED, "out_dtype %d", out_dtype);
-  if (flags & ~GQA_FLAG_VALU) return fail(GQA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
-  if (n_splits > GQA_MAX_SPLITS) return fail(GQA_ERR_INVALID_ARG, "n_splits %d > %d", n_splits, GQA_MAX_SPLITS);
-  if (s_kv_hint < 0) return fail(GQA_ERR_INVALID_ARG, "s_kv_hint < 0");
-  const size_t in_el = in_dtype == GQA_DTYPE_BF16 ? 2 : 4;
-  const size_t out_el = out_dtype == GQA_DTYPE_BF16 ? 2 : 4;
-  for (const void* p : {q, k_cache, v_cache, (const void*)out})
+  if (flags & ~(GQA_FLAG_VALU | GQA_FLAG_FUSED)) return fail(GQA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  for (const void* p : {q, k_cache, v_cache})
     if (reinterpret_cast<uintptr_t>(p) % 16) return fail(GQA_ERR_INVALID_ARG, "tensor pointer not 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(seq_lens) % 4 || reinterpret_cast<uintptr_t>(kv_token_offsets) % 8)
     return fail(GQA_ERR_INVALID_ARG, "seq_lens / kv_token_offsets misaligned");
-  const size_t qo_elems = (size_t)B * h_q * d_head;
-  if (overlap(out, qo_elems * out_el, q, qo_elems * in_el) ||
-      overlap(out, qo_elems * out_el, seq_lens, (size_t)B * 4) ||
-      out == k_cache || out == v_cache)
-    return fail(GQA_ERR_INVALID_ARG, "out overlaps an input");
+  return GQA_OK;
+}
+
+int check_out(const void* out, int out_dtype, size_t qo_elems) {
+  if (!out) return fail(GQA_ERR_INVALID_ARG, "null tensor pointer");
+  if (out_dtype != GQA_DTYPE_F32 && out_dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "out_dtype %d", out_dtype);
+  if (reinterpret_cast<uintptr_t>(out) % 16) return fail(GQA_ERR_INVALID_ARG, "tensor pointer not 16-byte aligned");
+  (void)qo_elems;
+  return GQA_OK;
+}
+
+// Split count, chunk floor and workspace partition of one call.
+struct Plan {
+  int ns, min_chunk;
+  size_t need;
+  float* ws_o;
+  float2* ws_ml;
+  unsigned long long* counters;
+};
+
+int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_hint,
+              void* workspace, size_t workspace_bytes, bool allow_library_ws, Plan* pl) {
   if (workspace && reinterpret_cast<uintptr_t>(workspace) % 256)
     return fail(GQA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
-
-  // ---- split plan
-  int num_cus = 0;
-  int st = device_cus(&num_cus);
-  if (st != GQA_OK) return st;
-  const int ns = n_splits > 0 ? n_splits : pick_splits_host(B, h_kv, s_kv_hint, num_cus);
-  const int min_chunk = n_splits > 0 ? 1 : kMinChunk;
-  const size_t need = ws_bytes(B, h_q, d_head, ns);
+  if (!workspace && !allow_library_ws) return fail(GQA_ERR_INVALID_ARG, "this entry point needs a workspace");
+  int ns = n_splits;
+  if (ns <= 0) {
+    int num_cus = 0;
+    int st = device_cus(&num_cus);
+    if (st != GQA_OK) return st;
+    ns = pick_splits_host(B, h_kv, s_kv_hint, num_cus);
+  }
+  pl->ns = ns;
+  pl->min_chunk = n_splits > 0 ? 1 : kMinChunk;
+  pl->need = ws_bytes(B, h_q, d_head, ns);
   if (workspace) {
-    if (workspace_bytes < need)
-      return fail(GQA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
-    if (overlap(out, qo_elems * out_el, workspace, need)) return fail(GQA_ERR_INVALID_ARG, "out overlaps workspace");
+    if (workspace_bytes < pl->need)
+      return fail(GQA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, pl->need);
   } else {
-    st = library_workspace(need, &workspace);
+    int st = library_workspace(pl->need, &workspace);
     if (st != GQA_OK) return st;
   }
-  float* ws_o = static_cast<float*>(workspace);
-  size_t o_bytes = ((size_t)B * h_q * ns * d_head * sizeof(float) + 255) & ~(size_t)255;
-  float2* ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + o_bytes);
+  const WsLayout lay = ws_layout(B, h_q, d_head, ns);
+  pl->counters = static_cast<unsigned long long*>(workspace);
+  pl->ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.o_off);
+  pl->ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + lay.ml_off);
+  return GQA_OK;
+}
 
-  gqa::SplitArgs sa{q, k_cache, v_cache, seq_lens, kv_token_offsets, ws_o, ws_ml,
-                    h_q, h_kv, ns, min_chunk, scale * gqa::kLog2e};
-  const dim3 grid = gqa::split_grid(ns, h_kv, B);
+int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* seq_lens, const int64_t* kv_token_offsets, int B, int h_q, int h_kv,
+              int d_head, float scale, int in_dtype, hipStream_t stream, int flags,
+              void* out = nullptr, int out_dtype = GQA_DTYPE_F32) {
+  const int fused = (flags & GQA_FLAG_FUSED) ? 1 : 0;
+  gqa::SplitArgs sa{q, k_cache, v_cache, seq_lens, kv_token_offsets, pl.ws_o, pl.ws_ml,
+                    h_q, h_kv, pl.ns, pl.min_chunk, scale * gqa::kLog2e,
+                    fused, out_dtype == GQA_DTYPE_BF16 ? 1 : 0, out, pl.counters,
+                    fused ? (g_call_tag.fetch_add(1) & 0xFFFFFFFFFFFFull) : 0ull};
+  const dim3 grid = gqa::split_grid(pl.ns, h_kv, B);
   const bool bf16 = in_dtype == GQA_DTYPE_BF16;
   const bool valu = (flags & GQA_FLAG_VALU) != 0;
+  const int nrep = h_q / h_kv;
   hipError_t e;
   if (g_ev_before && (e = hipEventRecord(g_ev_before, stream)) != hipSuccess)
     return fail(GQA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
@@ -254,12 +296,82 @@ int gqa_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
   if (g_ev_after && (e = hipEventRecord(g_ev_after, stream)) != hipSuccess)
     return fail(GQA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  return GQA_OK;
+}
 
-  gqa::MergeArgs ma{seq_lens, ws_o, ws_ml, out, h_q, ns, min_chunk};
+int run_merge(const Plan& pl, const int32_t* seq_lens, void* out, int B, int h_q, int d_head,
+              int out_dtype, hipStream_t stream) {
+  gqa::MergeArgs ma{seq_lens, pl.ws_o, pl.ws_ml, out, h_q, pl.ns, pl.min_chunk};
   const bool obf16 = out_dtype == GQA_DTYPE_BF16;
-  e = d_head == 128 ? launch_merge<128>(obf16, B, h_q, stream, ma) : launch_merge<64>(obf16, B, h_q, stream, ma);
+  hipError_t e = d_head == 128 ? launch_merge<128>(obf16, B, h_q, stream, ma)
+                               : launch_merge<64>(obf16, B, h_q, stream, ma);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
   return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* seq_lens, const int64_t* kv_token_offsets,
+                       void* out, int B, int h_q, int h_kv, int d_head,
+                       float scale, int n_splits, int in_dtype, int out_dtype,
+                       int64_t s_kv_hint, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream, int flags) {
+  int st;
+  if (!out) return fail(GQA_ERR_INVALID_ARG, "null tensor pointer");
+  if ((st = check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets, scale, in_dtype, flags))) return st;
+  if ((st = check_shape(B, h_q, h_kv, d_head, n_splits, s_kv_hint))) return st;
+  const size_t qo = (size_t)B * h_q * d_head;
+  if ((st = check_out(out, out_dtype, qo))) return st;
+  const size_t in_el = in_dtype == GQA_DTYPE_BF16 ? 2 : 4, out_el = out_dtype == GQA_DTYPE_BF16 ? 2 : 4;
+  if (overlap(out, qo * out_el, q, qo * in_el) || overlap(out, qo * out_el, seq_lens, (size_t)B * 4) ||
+      out == k_cache || out == v_cache)
+    return fail(GQA_ERR_INVALID_ARG, "out overlaps an input");
+  if (workspace && overlap(out, qo * out_el, workspace, workspace_bytes))
+    return fail(GQA_ERR_INVALID_ARG, "out overlaps workspace");
+  Plan pl;
+  if ((st = make_plan(B, h_q, h_kv, d_head, n_splits, s_kv_hint, workspace, workspace_bytes, true, &pl))) return st;
+  if ((st = run_split(pl, q, k_cache, v_cache, seq_lens, kv_token_offsets, B, h_q, h_kv, d_head, scale,
+                      in_dtype, stream, flags, out, out_dtype)))
+    return st;
+  if (flags & GQA_FLAG_FUSED) return GQA_OK;
+  return run_merge(pl, seq_lens, out, B, h_q, d_head, out_dtype, stream);
+}
+
+int gqa_decode_partial(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* seq_lens, const int64_t* kv_token_offsets,
+                       int B, int h_q, int h_kv, int d_head, float scale, int n_splits,
+                       int in_dtype, int64_t s_kv_hint, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream, int flags) {
+  int st;
+  if ((st = check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets, scale, in_dtype, flags))) return st;
+  if (flags & GQA_FLAG_FUSED) return fail(GQA_ERR_INVALID_ARG, "gqa_decode_partial does not merge");
+  if ((st = check_shape(B, h_q, h_kv, d_head, n_splits, s_kv_hint))) return st;
+  Plan pl;
+  if ((st = make_plan(B, h_q, h_kv, d_head, n_splits, s_kv_hint, workspace, workspace_bytes, false, &pl))) return st;
+  return run_split(pl, q, k_cache, v_cache, seq_lens, kv_token_offsets, B, h_q, h_kv, d_head, scale,
+                   in_dtype, stream, flags);
+}
+
+int gqa_decode_merge(const int32_t* seq_lens, const void* workspace, size_t workspace_bytes, void* out,
+                     int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_hint,
+                     int out_dtype, hipStream_t stream) {
+  int st;
+  if (!seq_lens || !workspace) return fail(GQA_ERR_INVALID_ARG, "null pointer");
+  if (reinterpret_cast<uintptr_t>(seq_lens) % 4) return fail(GQA_ERR_INVALID_ARG, "seq_lens misaligned");
+  if ((st = check_shape(B, h_q, h_kv, d_head, n_splits, s_kv_hint))) return st;
+  const size_t qo = (size_t)B * h_q * d_head;
+  if ((st = check_out(out, out_dtype, qo))) return st;
+  const size_t out_el = out_dtype == GQA_DTYPE_BF16 ? 2 : 4;
+  if (overlap(out, qo * out_el, workspace, workspace_bytes) || overlap(out, qo * out_el, seq_lens, (size_t)B * 4))
+    return fail(GQA_ERR_INVALID_ARG, "out overlaps an input");
+  Plan pl;
+  if ((st = make_plan(B, h_q, h_kv, d_head, n_splits, s_kv_hint, const_cast<void*>(workspace), workspace_bytes,
+                      false, &pl)))
+    return st;
+  return run_merge(pl, seq_lens, out, B, h_q, d_head, out_dtype, stream);
 }
 
 int gqa_decode_attn(const void* q, const void* k_cache, const void* v_cache,

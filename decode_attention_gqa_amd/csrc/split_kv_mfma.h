@@ -27,6 +27,7 @@
 // would keep 8); l is accumulated from the fp32 values.
 #pragma once
 
+#include "fused_tail.h"
 #include "gqa_common.h"
 
 namespace gqa {
@@ -165,7 +166,10 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
   const int S = a.seq_lens[b];
   int c, n_active;
   chunking(S, a.n_splits, a.min_chunk, c, n_active);
-  if (s >= n_active) return;                       // the merge reads chunks < n_active only
+  if (s >= n_active) {                             // the merge reads chunks < n_active only
+    if (a.fused && n_active == 0 && s == 0) fused_empty<D, NREP>(a, g, b);
+    return;
+  }
   const int64_t t0 = (int64_t)s * c;
   const int ntok = (int)min<int64_t>((int64_t)S - t0, c);
   const int64_t off = seq_offset(a.seq_lens, a.kv_off, b, lane);
@@ -256,6 +260,7 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
     *reinterpret_cast<float4*>(a.ws_o + row * D + d4) = o;
     if (d4 == 0) a.ws_ml[row] = make_float2(M, L);
   }
+  if (a.fused) fused_epilogue<D, NREP>(a, g, b, n_active);
 }
 
 }  // namespace gqa

@@ -11,6 +11,7 @@
 // It serves the fp32 inputs and measures what the matrix cores buy for bf16.
 #pragma once
 
+#include "fused_tail.h"
 #include "gqa_common.h"
 
 namespace gqa {
@@ -64,7 +65,10 @@ __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
   const int S = a.seq_lens[b];
   int c, n_active;
   chunking(S, a.n_splits, a.min_chunk, c, n_active);
-  if (s >= n_active) return;
+  if (s >= n_active) {
+    if (a.fused && n_active == 0 && s == 0) fused_empty<D, NREP>(a, g, b);
+    return;
+  }
   const int64_t t0 = (int64_t)s * c;
   const int ntok = (int)min<int64_t>((int64_t)S - t0, c);
   const int64_t off = seq_offset(a.seq_lens, a.kv_off, b, lane);
@@ -170,6 +174,7 @@ __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
     a.ws_o[row * D + d] = ov;
     if (d == 0) a.ws_ml[row] = make_float2(M, L);
   }
+  if (a.fused) fused_epilogue<D, NREP>(a, g, b, n_active);
 }
 
 }  // namespace gqa

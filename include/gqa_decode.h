@@ -70,8 +70,16 @@ enum { GQA_DTYPE_F32 = 0, GQA_DTYPE_BF16 = 1 };
 
 /* Flags of gqa_decode_attn_ex. */
 enum {
-    GQA_FLAG_VALU = 1 /* use the vector-ALU split kernel instead of the matrix-core one
-                         (bf16 inputs; fp32 inputs always use it). For comparison. */
+    GQA_FLAG_VALU = 1,  /* use the vector-ALU split kernel instead of the matrix-core one
+                           (bf16 inputs; fp32 inputs always use it). For comparison. */
+    GQA_FLAG_FUSED = 2  /* one kernel launch: the last split workgroup of each (sequence,
+                           kv head) merges that group's triplets and writes out (uses the
+                           workspace's arrival counters, see gqa_decode_workspace_bytes).
+                           Correct, but slower on MI355X than the default two launches:
+                           making a workgroup's triplets visible to a workgroup on another
+                           XCD takes device-scope fences that write back and invalidate
+                           the XCD's L2 (measured 206 us vs 12.6 us per call for 64 query /
+                           8 kv heads, 8k tokens). */
 };
 
 /* Largest split count. */
@@ -106,7 +114,7 @@ int gqa_decode_attn(const void* q, const void* k_cache, const void* v_cache,
  *                    (n_splits if > 0, else gqa_decode_pick_splits(B, h_kv,
  *                    s_kv_hint, 0)); 256-byte aligned. NULL: library-owned.
  *  stream            HIP stream (NULL: null stream).
- *  flags             0 or GQA_FLAG_VALU.
+ *  flags             0 or an OR of GQA_FLAG_VALU and GQA_FLAG_FUSED.
  */
 int gqa_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* seq_lens, const int64_t* kv_token_offsets,
@@ -114,6 +122,39 @@ int gqa_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
                        float scale, int n_splits, int in_dtype, int out_dtype,
                        int64_t s_kv_hint, void* workspace, size_t workspace_bytes,
                        hipStream_t stream, int flags);
+
+/*
+ * The two halves of gqa_decode_attn_ex, for callers that combine partial
+ * results from several sources (e.g. KV sharded across GPUs along the
+ * sequence: each GPU writes its triplets, they are exchanged, one merge
+ * follows) or that time the kernels separately.
+ *
+ * gqa_decode_partial runs only the split kernel: for every sequence b, query
+ * head h and chunk s < n_active(b) it writes, in `workspace`,
+ *   o[((b*h_q + h)*n + s)*d_head + i]   unnormalised sum_t 2^(x_t - m) V_t[i]  (fp32)
+ *   ml[(b*h_q + h)*n + s] = (m, l)      m = max_t x_t, l = sum_t 2^(x_t - m)  (fp32 pairs)
+ * where x_t = scale * log2(e) * <q, K_t> (scores in log2 units), n is the
+ * split count used, and `o` and `ml` sit where gqa_decode_workspace_bytes
+ * describes. Chunk s covers tokens
+ * [s*c, min(S_b, (s+1)*c)) with c = max(ceil(S_b / n), f), f = 1 when
+ * n_splits > 0 and 128 otherwise; n_active(b) = ceil(S_b / c). Other slots
+ * are left untouched. A workspace is required.
+ *
+ * gqa_decode_merge reads those triplets and writes out = o / l per (b, h),
+ * merged exactly over the chunks. It must be given the seq_lens, shape,
+ * n_splits and s_kv_hint of the gqa_decode_partial call that filled the
+ * workspace (they fix n and the chunking), and run after it on the stream.
+ * Arguments otherwise as in gqa_decode_attn_ex.
+ */
+int gqa_decode_partial(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* seq_lens, const int64_t* kv_token_offsets,
+                       int B, int h_q, int h_kv, int d_head, float scale, int n_splits,
+                       int in_dtype, int64_t s_kv_hint, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream, int flags);
+
+int gqa_decode_merge(const int32_t* seq_lens, const void* workspace, size_t workspace_bytes,
+                     void* out, int B, int h_q, int h_kv, int d_head, int n_splits,
+                     int64_t s_kv_hint, int out_dtype, hipStream_t stream);
 
 /*
  * Split count the library uses when n_splits <= 0: enough workgroups that
@@ -124,8 +165,14 @@ int gqa_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
  */
 int gqa_decode_pick_splits(int B, int h_kv, int64_t s_kv_max, int num_cus);
 
-/* Workspace bytes for n_splits chunks: B*h_q*n_splits*(d_head + 2) floats,
- * rounded up to 256 bytes. 0 for invalid arguments. */
+/* Workspace bytes for n_splits chunks. Layout, each part starting on a
+ * 256-byte boundary:
+ *   counters  B*h_q uint64 at byte 0 (arrival counters of GQA_FLAG_FUSED calls;
+ *             any initial contents are fine, each call tags its counts)
+ *   o         [B, h_q, n_splits, d_head] fp32 at C = round_up(B*h_q*8, 256)
+ *   (m, l)    [B, h_q, n_splits] fp32 pairs at C + round_up(B*h_q*n_splits*d_head*4, 256)
+ * Calls that share a workspace must not overlap in time.
+ * 0 for invalid arguments. */
 size_t gqa_decode_workspace_bytes(int B, int h_q, int d_head, int n_splits);
 
 /*

@@ -21,7 +21,7 @@ def to_device(inp: workloads.Inputs, device="cuda"):
 
 
 def run_gpu(inp: workloads.Inputs, n_splits=0, out_dtype="f32", valu=False, poison=True,
-            hint=True, dev=None, stream=None):
+            hint=True, dev=None, stream=None, fused=False):
     """Run the library on `inp`; returns (out as float64 numpy, split count used).
 
     The workspace is filled with NaN first, so a chunk the merge reads but no
@@ -36,12 +36,12 @@ def run_gpu(inp: workloads.Inputs, n_splits=0, out_dtype="f32", valu=False, pois
     hint_v = s_max if hint else 0
     ns = n_splits if n_splits > 0 else gqa.gqa_decode_pick_splits(w.B, w.h_kv, hint_v)
     ws = torch.empty(gqa.gqa_decode_workspace_bytes(w.B, w.h_q, w.d, ns), dtype=torch.uint8, device=q.device)
-    if poison:
+    if poison:   # every byte, the arrival counters included
         ws.view(torch.float32).fill_(float("nan"))
     odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
     out = gqa.gqa_decode_attn_ex(q, k, v, lens, scale=float(inp.scale), n_splits=n_splits,
                                  out_dtype=odt, s_kv_hint=hint_v, workspace=ws, valu=valu,
-                                 stream=stream)
+                                 stream=stream, fused=fused)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), ns
 

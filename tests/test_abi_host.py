@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert names == sorted(["gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_pick_splits",
+    assert names == sorted(["gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_partial",
+                            "gqa_decode_merge", "gqa_decode_pick_splits",
                             "gqa_decode_workspace_bytes", "gqa_status_string", "gqa_last_error",
                             "gqa_decode_set_split_events"])
 
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol(gqa):
 def test_status_constants_match_header(gqa):
     src = open(HEADER).read()
     for name in ["GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_WORKSPACE",
-                 "GQA_ERR_HIP", "GQA_DTYPE_F32", "GQA_DTYPE_BF16", "GQA_FLAG_VALU"]:
+                 "GQA_ERR_HIP", "GQA_DTYPE_F32", "GQA_DTYPE_BF16", "GQA_FLAG_VALU", "GQA_FLAG_FUSED"]:
         m = re.search(rf"\b{name}\s*=\s*(-?\d+)", src)
         assert m and int(m.group(1)) == getattr(gqa, name), name
     assert int(re.search(r"#define GQA_MAX_SPLITS (\d+)", src).group(1)) == gqa.GQA_MAX_SPLITS
@@ -78,7 +79,7 @@ def call(gqa, **kw):
     (dict(d=96), -2), (dict(d=256), -2),
     (dict(scale=math.inf), -1), (dict(scale=math.nan), -1),
     (dict(in_dt=2), -2), (dict(out_dt=7), -2),
-    (dict(flags=2), -1),
+    (dict(flags=4), -1),
     (dict(n_splits=4097), -1),
     (dict(hint=-1), -1),
     (dict(q=Q + 8), -1),                              # misaligned
@@ -107,11 +108,11 @@ def test_no_device_is_reported_not_crashed(gqa):
 
 
 def test_workspace_bytes(gqa):
+    r = lambda x: (x + 255) // 256 * 256
     for B, h_q, d, n in [(1, 64, 128, 64), (8, 64, 128, 37), (1, 8, 64, 4), (3, 5, 64, 1)]:
-        o = B * h_q * n * d * 4
-        o = (o + 255) // 256 * 256
-        want = (o + B * h_q * n * 8 + 255) // 256 * 256
+        want = r(B * h_q * 8) + r(B * h_q * n * d * 4) + r(B * h_q * n * 8)
         assert gqa.gqa_decode_workspace_bytes(B, h_q, d, n) == want
+        assert gqa.workspace_layout(B, h_q, d, n)["total"] == want
     assert gqa.gqa_decode_workspace_bytes(0, 64, 128, 4) == 0
     assert gqa.gqa_decode_workspace_bytes(1, 64, 128, 0) == 0
 
@@ -152,3 +153,17 @@ def test_binding_rejects_cpu_tensors(gqa):
 def test_split_events_need_both_or_neither(gqa):
     assert gqa.lib.gqa_decode_set_split_events(0x1000, None) == gqa.GQA_ERR_INVALID_ARG
     assert gqa.lib.gqa_decode_set_split_events(None, None) == gqa.GQA_OK
+
+
+def test_partial_and_merge_check_on_the_host(gqa):
+    L_ = gqa.lib
+    # partial needs a workspace, and the usual shape checks apply
+    assert L_.gqa_decode_partial(Q, K, V, L, None, 1, 64, 8, 128, 0.088, 0, 1, 0, None, 0, None, 0) == -1
+    assert L_.gqa_decode_partial(Q, K, V, L, None, 1, 64, 8, 96, 0.088, 0, 1, 0, W, 1 << 20, None, 0) == -2
+    assert L_.gqa_decode_partial(Q, K, V, L, None, 1, 64, 8, 128, 0.088, 8, 1, 0, W, 16, None, 0) == -3
+    assert L_.gqa_decode_partial(Q, K, V, L, None, 1, 64, 8, 128, 0.088, 8, 1, 0, W, 1 << 20, None, 2) == -1
+    assert L_.gqa_decode_merge(L, None, 0, O, 1, 64, 8, 128, 0, 0, 0, None) == -1
+    assert L_.gqa_decode_merge(L, W, 1 << 20, O, 1, 60, 8, 128, 8, 0, 0, None) == -1
+    assert L_.gqa_decode_merge(L, W, 1 << 20, O, 1, 64, 8, 128, 8, 0, 5, None) == -2
+    assert L_.gqa_decode_merge(L, W, 16, O, 1, 64, 8, 128, 8, 0, 0, None) == -3
+    assert L_.gqa_decode_merge(L, W, 1 << 20, W + 256, 1, 64, 8, 128, 8, 0, 0, None) == -1   # out in workspace

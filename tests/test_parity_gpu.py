@@ -183,3 +183,25 @@ def test_runs_on_a_side_stream():
     with torch.cuda.stream(s):
         got, ns = run_gpu(inp, stream=s)
     report("side stream", max_err(got, ref_of(inp)), ns, TOL_F32)
+
+
+@pytest.mark.parametrize("ns", [0, 5])
+def test_partial_then_merge_equals_full_call(ns):
+    """The two halves give the same bits as the one-call path."""
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    inp = workloads.make_inputs("llama70b_gqa_b8_ragged")
+    q, k, v, dl = to_device(inp)
+    w = inp.w
+    hint = int(inp.seq_lens.max())
+    n = ns if ns > 0 else gqa.gqa_decode_pick_splits(w.B, w.h_kv, hint)
+    ws = torch.empty(gqa.gqa_decode_workspace_bytes(w.B, w.h_q, w.d, n), dtype=torch.uint8, device="cuda")
+    full = gqa.gqa_decode_attn_ex(q, k, v, dl, scale=float(inp.scale), n_splits=ns, s_kv_hint=hint, workspace=ws)
+    out = torch.empty_like(full)
+    ws2 = torch.full_like(ws, 255)
+    gqa.gqa_decode_partial(q, k, v, dl, ws2, scale=float(inp.scale), n_splits=ns, s_kv_hint=hint)
+    gqa.gqa_decode_merge(dl, ws2, out, h_kv=w.h_kv, n_splits=ns, s_kv_hint=hint)
+    torch.cuda.synchronize()
+    assert torch.equal(full, out)
+    report(f"partial+merge ns={ns}", max_err(out.cpu().numpy().astype(np.float64), ref_of(inp)), n, TOL_F32)
