@@ -16,7 +16,7 @@
 // max reduction. Query heads n_rep..15 of the 16-wide tile are zero padding.
 //
 // Data movement: K and V go straight from HBM to registers with 16-byte
-// loads (nothing is staged in LDS; the group's heads share each K/V register
+// non-temporal loads (nothing is staged in LDS; the group's heads share each K/V register
 // inside the MFMA). A lane's 8 V loads are 8 tokens x 8 consecutive
 // dimensions; an in-register 8x8 transpose of 16-bit values turns them into
 // the MFMA A operand (8 tokens of one dimension). K is used in its natural
@@ -64,7 +64,7 @@ __device__ __forceinline__ void load_block(KVRegs<D>& r, const __bf16* kblk, con
     if (tail) t = min(t, nv - 1);     // clamped rows are read but masked out of the softmax
     const __bf16* row = kblk + (int64_t)t * rs + 8 * grp;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) r.k[x][kk] = *reinterpret_cast<const uint4*>(row + 32 * kk);
+    for (int kk = 0; kk < KS; ++kk) r.k[x][kk] = load_stream16(row + 32 * kk);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -72,10 +72,10 @@ __device__ __forceinline__ void load_block(KVRegs<D>& r, const __bf16* kblk, con
     if (tail) t = min(t, nv - 1);
     const __bf16* row = vblk + (int64_t)t * rs + NT * n;
     if constexpr (VW == 4) {
-      uint4 u = *reinterpret_cast<const uint4*>(row);
+      const uint4 u = load_stream16(row);
       r.v[j][0] = u.x; r.v[j][1] = u.y; r.v[j][2] = u.z; r.v[j][3] = u.w;
     } else {
-      uint2 u = *reinterpret_cast<const uint2*>(row);
+      const uint2 u = load_stream8(row);
       r.v[j][0] = u.x; r.v[j][1] = u.y;
     }
   }

@@ -22,18 +22,40 @@ template <>
 struct Elem<float> {
   static __device__ __forceinline__ float get(const float* p, int i) { return p[i]; }
   // 8 consecutive values starting at p (16-byte aligned for bf16, 32 for fp32)
+  // the N (1 or 2) consecutive values at p, which is N-element aligned
+  template <int N>
+  static __device__ __forceinline__ void get_lane(const float* p, float (&f)[N]) {
+    if constexpr (N == 2) {
+      const uint2 u = load_stream8(p);
+      f[0] = __uint_as_float(u.x);
+      f[1] = __uint_as_float(u.y);
+    } else {
+      f[0] = __uint_as_float(load_stream4(p));
+    }
+  }
   static __device__ __forceinline__ void get8(const float* p, float (&f)[8]) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    const uint4 a = load_stream16(p);
+    const uint4 b = load_stream16(p + 4);
+    f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y); f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
+    f[4] = __uint_as_float(b.x); f[5] = __uint_as_float(b.y); f[6] = __uint_as_float(b.z); f[7] = __uint_as_float(b.w);
   }
 };
 template <>
 struct Elem<__bf16> {
   static __device__ __forceinline__ float get(const __bf16* p, int i) { return (float)p[i]; }
+  template <int N>
+  static __device__ __forceinline__ void get_lane(const __bf16* p, float (&f)[N]) {
+    if constexpr (N == 2) {
+      const uint32_t w = load_stream4(p);
+      f[0] = __uint_as_float(w << 16);
+      f[1] = __uint_as_float(w & 0xFFFF0000u);
+    } else {
+      const unsigned short h = __builtin_nontemporal_load(reinterpret_cast<const unsigned short*>(p));
+      f[0] = __uint_as_float((uint32_t)h << 16);
+    }
+  }
   static __device__ __forceinline__ void get8(const __bf16* p, float (&f)[8]) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint4 u = load_stream16(p);
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -128,8 +150,7 @@ __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
     const T* vblk = vbase + (int64_t)blk * TB * rs + lane * DPL;
     for (int t = 0; t < nv; ++t) {
       float vv[DPL];
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) vv[e] = Elem<T>::get(vblk + (int64_t)t * rs, e);
+      Elem<T>::template get_lane<DPL>(vblk + (int64_t)t * rs, vv);
 #pragma unroll
       for (int h = 0; h < NREP; ++h) {
         const float p = sp[w][h][t];
