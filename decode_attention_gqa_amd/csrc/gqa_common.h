@@ -62,17 +62,34 @@ __device__ __forceinline__ void chunking(int S, int n_splits, int min_chunk, int
   n_active = (int)(((unsigned)S + uc - 1u) / uc);
 }
 
-// First token row of sequence b: explicit offsets, or the packed prefix sum
-// sum_{j<b} S_j computed by the calling wave (every lane gets the result).
-__device__ __forceinline__ int64_t seq_offset(const int32_t* seq_lens, const int64_t* kv_off,
-                                              int b, int lane) {
-  if (kv_off) return kv_off[b];
-  if (b == 0) return 0;
+// Length S_b and first token row of sequence b, with one round of loads:
+// explicit offsets are loaded next to seq_lens[b]; for the packed layout the
+// wave reads seq_lens[0..b] (lane j holds S_j of its 64-sequence slice),
+// takes S_b from lane b and sums the lanes below b (every lane gets both).
+__device__ __forceinline__ void seq_info(const int32_t* seq_lens, const int64_t* kv_off, int b,
+                                         int lane, int& S, int64_t& off) {
+  if (kv_off) {
+    S = seq_lens[b];
+    off = kv_off[b];
+    return;
+  }
+  if (b == 0) {
+    S = seq_lens[0];
+    off = 0;
+    return;
+  }
   int64_t acc = 0;
-  for (int j = lane; j < b; j += 64) acc += seq_lens[j];
+  int sb = 0;
+  for (int base = 0; base <= b; base += 64) {     // one pass when b < 64
+    const int j = base + lane;
+    const int v = (j <= b) ? seq_lens[j] : 0;
+    if (j < b) acc += v;
+    if (base + 64 > b) sb = __builtin_amdgcn_readlane(v, b - base);
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-  return acc;
+  S = sb;
+  off = acc;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

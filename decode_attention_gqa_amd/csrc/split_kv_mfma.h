@@ -163,7 +163,9 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = lane >> 4, n = lane & 15;
 
-  const int S = a.seq_lens[b];
+  int S;
+  int64_t off;
+  seq_info(a.seq_lens, a.kv_off, b, lane, S, off);
   int c, n_active;
   chunking(S, a.n_splits, a.min_chunk, c, n_active);
   if (s >= n_active) {                             // the merge reads chunks < n_active only
@@ -172,7 +174,6 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
   }
   const int64_t t0 = (int64_t)s * c;
   const int ntok = (int)min<int64_t>((int64_t)S - t0, c);
-  const int64_t off = seq_offset(a.seq_lens, a.kv_off, b, lane);
 
   const int64_t rs = (int64_t)a.h_kv * D;          // elements between consecutive tokens
   const __bf16* kbase = static_cast<const __bf16*>(a.k) + ((off + t0) * a.h_kv + g) * D;

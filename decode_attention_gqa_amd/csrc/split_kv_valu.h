@@ -84,7 +84,9 @@ __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
   const int s = wc.s, g = wc.g, b = wc.b;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
-  const int S = a.seq_lens[b];
+  int S;
+  int64_t off;
+  seq_info(a.seq_lens, a.kv_off, b, lane, S, off);
   int c, n_active;
   chunking(S, a.n_splits, a.min_chunk, c, n_active);
   if (s >= n_active) {
@@ -93,7 +95,6 @@ __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
   }
   const int64_t t0 = (int64_t)s * c;
   const int ntok = (int)min<int64_t>((int64_t)S - t0, c);
-  const int64_t off = seq_offset(a.seq_lens, a.kv_off, b, lane);
   const int64_t rs = (int64_t)a.h_kv * D;
   const T* kbase = static_cast<const T*>(a.k) + ((off + t0) * a.h_kv + g) * D;
   const T* vbase = static_cast<const T*>(a.v) + ((off + t0) * a.h_kv + g) * D;

@@ -205,3 +205,18 @@ def test_partial_then_merge_equals_full_call(ns):
     torch.cuda.synchronize()
     assert torch.equal(full, out)
     report(f"partial+merge ns={ns}", max_err(out.cpu().numpy().astype(np.float64), ref_of(inp)), n, TOL_F32)
+
+
+@pytest.mark.parametrize("B", [63, 64, 65, 130])
+def test_many_sequences_packed(B):
+    """Sequence offsets are prefix sums over seq_lens; more than 64 sequences
+    take more than one pass of the wave."""
+    rng = np.random.default_rng(80 + B)
+    lens = rng.integers(0, 300, size=B)
+    lens[B // 2] = 0
+    inp = workloads.custom(f"many{B}", B=B, h_q=16, h_kv=4, d=128, seq_lens=lens, seed=80 + B)
+    ref = ref_of(inp)
+    for ns in (0, 3):
+        for valu in (False, True):
+            got, used = run_gpu(inp, n_splits=ns, valu=valu)
+            report(f"B={B} ns={ns} valu={valu}", max_err(got, ref), used, TOL_F32)
