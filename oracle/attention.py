@@ -112,6 +112,44 @@ def attend(q, k, v, seq_lens, scale, h_kv: int, dtype: str = "bf16",
     return out
 
 
+def attend_multi(q, k, v, seq_lens, scale, h_kv: int, dtype: str = "bf16") -> np.ndarray:
+    """Several new query tokens per sequence, causal among themselves, fp64.
+
+    q [B, S_q, h_q, d]; the S_q tokens are the last S_q positions of sequence
+    b, whose K/V rows are already in the cache: token i sits at position
+    p = S_b - S_q + i and attends cache positions [0, p]. A token with p < 0
+    (fewer cached positions than query tokens) attends nothing: zeros. With
+    S_q = 1 this is `attend`. This extension has no source on the pages; it is
+    the plain causal-attention definition applied to the decode layout.
+    Returns out [B, S_q, h_q, d].
+    """
+    q = np.asarray(q)
+    B, S_q, h_q, d = q.shape
+    if h_q % h_kv:
+        raise ValueError("h_q must be a multiple of h_kv")
+    n_rep = h_q // h_kv
+    sc = float(np.float32(scale))
+    off = token_offsets(seq_lens)
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    out = np.zeros((B, S_q, h_q, d))
+    for b in range(B):
+        S = int(lens[b])
+        for g in range(h_kv):
+            hs = list(range(g * n_rep, (g + 1) * n_rep))
+            Kg = widen(k[off[b]:off[b] + S, g, :], dtype)
+            Vg = widen(v[off[b]:off[b] + S, g, :], dtype)
+            for i in range(S_q):
+                p = S - S_q + i
+                if p < 0:
+                    continue
+                Qi = widen(q[b, i, hs, :], dtype)                   # [r, d]
+                s = sc * (Qi @ Kg[:p + 1].T)                          # [r, p+1]
+                s -= s.max(axis=1, keepdims=True)
+                e = np.exp(s)
+                out[b, i, hs, :] = (e / e.sum(axis=1, keepdims=True)) @ Vg[:p + 1]
+    return out
+
+
 # ------------------------------------------- triplets, merge, final o / l
 def scores(q_row: np.ndarray, k_rows: np.ndarray, scale) -> np.ndarray:
     """s_t = scale * <q, K_t> for one query head (float64 inputs)."""

@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 import test_oracle_merge as M
+import test_oracle_multi as MM
 import test_oracle_pins as P
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
@@ -42,6 +43,10 @@ MUTANTS = {
     "finalize_no_division": ("    return o / l", "    return o"),
     "fanout_forwards_merge": ("east = [inbox_w[i] if i < n - 1 else None for i in range(n)]",
                               "east = [state[i] if i < n - 1 else None for i in range(n)]"),
+    "multi_causal_off_by_one": ("s = sc * (Qi @ Kg[:p + 1].T)", "s = sc * (Qi @ Kg[:p].T)"),
+    "multi_position_from_start": ("p = S - S_q + i", "p = min(S - 1, i + S // 2)"),
+    "multi_values_not_causal": ("out[b, i, hs, :] = (e / e.sum(axis=1, keepdims=True)) @ Vg[:p + 1]",
+                                "out[b, i, hs, :] = (e / e.sum(axis=1, keepdims=True)) @ Vg[S - p - 1:]"),
     "fanout_east_first": ("            if inbox_w[i] is not None:\n                state[i] = merge(state[i], inbox_w[i])\n                order[i].append(inbox_w_org[i])\n            if inbox_e[i] is not None:\n                state[i] = merge(state[i], inbox_e[i])\n                order[i].append(inbox_e_org[i])",
                           "            if inbox_e[i] is not None:\n                state[i] = merge(state[i], inbox_e[i])\n                order[i].append(inbox_e_org[i])\n            if inbox_w[i] is not None:\n                state[i] = merge(state[i], inbox_w[i])\n                order[i].append(inbox_w_org[i])"),
 }
@@ -76,10 +81,14 @@ def pin_checks():
           lambda: M.test_fanout_every_rank_gets_the_unsplit_answer(5),
           lambda: M.test_fanout_arrival_step_is_rank_distance(4),
           M.test_triplet_matches_definition]
+    c += [MM.test_single_query_token_is_attend, lambda: MM.test_each_token_is_brute_force_on_its_prefix(3),
+          MM.test_future_positions_do_not_matter, MM.test_last_token_sees_everything,
+          MM.test_more_query_tokens_than_cached_positions]
     return c
 
 
-NAMES = ["NEG_INF", "attend", "fanout", "finalize", "merge", "scores", "token_offsets", "triplet", "widen"]
+NAMES = ["NEG_INF", "attend", "attend_multi", "fanout", "finalize", "merge", "scores", "token_offsets",
+         "triplet", "widen"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
