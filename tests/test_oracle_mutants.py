@@ -23,11 +23,11 @@ MUTANTS = {
                             "hs = [h for h in range(g, h_q, h_kv)"),
     "scale_dropped": ("s = sc * (Qg @ Kg.T)", "s = (Qg @ Kg.T)"),
     "scale_inverted": ("s = sc * (Qg @ Kg.T)", "s = (Qg @ Kg.T) / sc"),
-    "no_max_subtraction": ("s -= s.max(axis=1, keepdims=True)", "pass"),
+    "no_max_subtraction": ("# [r, S]\n            s -= s.max(axis=1, keepdims=True)", "# [r, S]\n            pass"),
     "not_normalised": ("p = e / e.sum(axis=1, keepdims=True)", "p = e"),
     "offsets_shifted": ("off[1:] = np.cumsum(lens[:-1])", "off[1:] = np.cumsum(lens[1:])"),
-    "k_and_v_swapped": ("Kg = widen(k[off[b]:off[b] + S, g, :], dtype)",
-                        "Kg = widen(v[off[b]:off[b] + S, g, :], dtype)"),
+    "k_and_v_swapped": ("Kg = widen(k[off[b]:off[b] + S, g, :], dtype)          # [S, d]",
+                        "Kg = widen(v[off[b]:off[b] + S, g, :], dtype)          # [S, d]"),
     "q_k_transposed": ("s = sc * (Qg @ Kg.T)", "s = sc * (Kg[:Qg.shape[0], :Qg.shape[0]] @ Qg)"),
     "empty_seq_not_zero": ("                out[b, hs, :] = 0.0", "                out[b, hs, :] = 1.0"),
     "bf16_widen_shift": ("bits = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)",
