@@ -145,6 +145,8 @@ def main() -> int:
     ap.add_argument("--n-splits", type=int, default=0)
     ap.add_argument("--valu", action="store_true", help="vector-ALU split kernel (comparison)")
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of a HIP graph")
+    ap.add_argument("--s-q", type=int, default=1,
+                    help="query tokens per sequence (> 1: multi-token decode, causal among them)")
     ap.add_argument("--fused", action="store_true",
                     help="single-launch form (GQA_FLAG_FUSED) instead of split + merge kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -203,8 +205,22 @@ def main() -> int:
     out = torch.empty((w.B, w.h_q, w.d), dtype=torch.float32, device=dev)
     scale = float(inp.scale)
 
+    if args.s_q > 1:
+        # several query tokens per sequence: q [B, S_q, h_q, d], seeded like the rest
+        qm = workloads.normals(w.seed, 9, w.B * args.s_q * w.h_q * w.d, 1.0, w.dtype).reshape(
+            w.B, args.s_q, w.h_q, w.d)
+        qms = [up(qm)] + [up(qm) for _ in range(R - 1)]
+        ns = gqa.multi_splits(w.B, args.s_q, w.h_q, w.h_kv, s_max, args.n_splits)
+        ws = torch.empty(gqa.gqa_decode_workspace_bytes(w.B * args.s_q, w.h_q, w.d, ns),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty((w.B, args.s_q, w.h_q, w.d), dtype=torch.float32, device=dev)
+
     def call(i):
         q, k, v = sets[i % R]
+        if args.s_q > 1:
+            gqa.gqa_decode_attn_multi(qms[i % R], k, v, lens, out, scale=scale, n_splits=args.n_splits,
+                                      s_kv_hint=s_max, workspace=ws)
+            return
         gqa.gqa_decode_attn_ex(q, k, v, lens, out, scale=scale, n_splits=args.n_splits,
                                s_kv_hint=s_max, workspace=ws, valu=args.valu, fused=args.fused)
 
@@ -246,7 +262,9 @@ def main() -> int:
             gqa.gqa_decode_partial(q, k, v, lens, ws, scale=scale, n_splits=args.n_splits,
                                    s_kv_hint=s_max, valu=args.valu)
 
-        if args.eager:
+        if args.s_q > 1:
+            graph_p = None                           # no split-only entry point for S_q > 1
+        elif args.eager:
             graph_p = None
         else:
             graph_p = torch.cuda.CUDAGraph()
@@ -259,6 +277,9 @@ def main() -> int:
         hip.lib.hipEventRecord(e0, ctypes.c_void_p(stream.cuda_stream))
         if graph_p is not None:
             graph_p.replay()
+        elif args.s_q > 1:
+            for i in range(args.steps):
+                call(i)
         else:
             for i in range(args.steps):
                 partial(i)
@@ -297,13 +318,15 @@ def main() -> int:
             "split_kernel": "valu" if args.valu else ("mfma" if w.dtype == "bf16" else "valu"),
             "timing": "eager calls" if args.eager else "one HIP graph holding the K calls",
             "launches_per_call": 1 if args.fused else 2,
+            "query_tokens_per_sequence": args.s_q,
             "rotating_input_sets": R,
         },
         "us_per_call": sec_per_call * 1e6,
         "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
         "roofline": {
             "bound": "hbm",
-            "kernel": "split_kv_mfma" if (w.dtype == "bf16" and not args.valu) else "split_kv_valu",
+            "kernel": ("split_kv_mfma" if (w.dtype == "bf16" and not args.valu) else "split_kv_valu")
+                      + (" (whole call, eager: no split-only path for S_q > 1)" if args.s_q > 1 else ""),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -16,12 +16,13 @@ import math
 import os
 
 __all__ = [
-    "gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_partial", "gqa_decode_merge",
+    "gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_attn_multi", "gqa_decode_partial",
+    "gqa_decode_merge", "GQA_MAX_QUERY_TOKENS",
     "gqa_decode_pick_splits",
     "gqa_decode_workspace_bytes", "gqa_status_string", "GQAError", "lib", "LIB_PATH",
     "GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_WORKSPACE", "GQA_ERR_HIP",
     "GQA_DTYPE_F32", "GQA_DTYPE_BF16", "GQA_FLAG_VALU", "GQA_FLAG_FUSED", "GQA_MAX_SPLITS",
-    "workspace_layout",
+    "workspace_layout", "multi_splits",
 ]
 
 GQA_OK = 0
@@ -34,6 +35,7 @@ GQA_DTYPE_BF16 = 1
 GQA_FLAG_VALU = 1
 GQA_FLAG_FUSED = 2
 GQA_MAX_SPLITS = 4096
+GQA_MAX_QUERY_TOKENS = 64
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_decode.so")
 
@@ -57,6 +59,9 @@ lib.gqa_decode_attn.restype = _i32
 lib.gqa_decode_attn_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32,
                                    _i32, _i32, _i64, _vp, _sz, _vp, _i32]
 lib.gqa_decode_attn_ex.restype = _i32
+lib.gqa_decode_attn_multi.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                      _i32, _i64, _vp, _sz, _vp]
+lib.gqa_decode_attn_multi.restype = _i32
 lib.gqa_decode_partial.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i64,
                                    _vp, _sz, _vp, _i32]
 lib.gqa_decode_partial.restype = _i32
@@ -164,8 +169,9 @@ def gqa_decode_attn_ex(q, k_cache, v_cache, seq_lens, out=None, *, scale=None, n
 
 
 def _check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets):
+    """q is [B, h_q, d] or [B, S_q, h_q, d]."""
     torch = _torch()
-    B, h_q, d = q.shape
+    B, d = q.shape[0], q.shape[-1]
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
@@ -180,6 +186,56 @@ def _check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets):
     if kv_token_offsets is not None and (kv_token_offsets.dtype != torch.int64
                                          or kv_token_offsets.shape != (B,) or not kv_token_offsets.is_cuda):
         raise ValueError("kv_token_offsets must be an int64 [B] GPU tensor")
+
+
+def multi_splits(B: int, S_q: int, h_q: int, h_kv: int, s_kv_hint: int = 0, n_splits: int = 0) -> int:
+    """Split count gqa_decode_attn_multi uses (for sizing its workspace)."""
+    if n_splits > 0:
+        return n_splits
+    n_rep = h_q // h_kv
+    tpt = min(S_q, 16 // n_rep)
+    return gqa_decode_pick_splits(B * ((S_q + tpt - 1) // tpt), h_kv, s_kv_hint, 0)
+
+
+def gqa_decode_attn_multi(q, k_cache, v_cache, seq_lens, out=None, *, scale=None, n_splits=0,
+                          out_dtype=None, s_kv_hint=0, kv_token_offsets=None, workspace=None,
+                          stream=None):
+    """S_q new query tokens per sequence, causal among themselves.
+
+    q [B, S_q, h_q, d] bf16; k_cache / v_cache [T, h_kv, d] bf16 holding the
+    new tokens' K/V already; seq_lens [B] int32 counts them. Token i of
+    sequence b attends positions [0, S_b - S_q + i]. Returns [B, S_q, h_q, d].
+    """
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, S_q, h_q, d_head]")
+    B, S_q, h_q, d = q.shape
+    h_kv = k_cache.shape[1]
+    _check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets)
+    if q.dtype != torch.bfloat16:
+        raise TypeError("gqa_decode_attn_multi takes bf16 q/k/v")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((B, S_q, h_q, d), dtype=out_dtype, device=q.device)
+    elif out.shape != (B, S_q, h_q, d) or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, S_q, h_q, d_head] tensor of out_dtype")
+    with torch.cuda.device(q.device):
+        if workspace is None:
+            ns = multi_splits(B, S_q, h_q, h_kv, int(s_kv_hint), n_splits)
+            workspace = torch.empty(gqa_decode_workspace_bytes(B * S_q, h_q, d, ns), dtype=torch.uint8,
+                                    device=q.device)
+        st = stream if stream is not None else torch.cuda.current_stream(q.device)
+        r = lib.gqa_decode_attn_multi(
+            q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+            kv_token_offsets.data_ptr() if kv_token_offsets is not None else None,
+            out.data_ptr(), B, S_q, h_q, h_kv, d, float(scale), int(n_splits), _dtype_code(out_dtype),
+            int(s_kv_hint), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            ctypes.c_void_p(st.cuda_stream))
+    if r != GQA_OK:
+        raise GQAError(r, "gqa_decode_attn_multi")
+    return out
 
 
 def gqa_decode_partial(q, k_cache, v_cache, seq_lens, workspace, *, scale=None, n_splits=0,

@@ -33,9 +33,14 @@ struct SplitArgs {
   void* out;                  // [B, h_q, D]
   unsigned long long* counters;   // [B * h_kv] arrival counters: (call tag << 16) | arrivals
   unsigned long long tag;     // this call's tag (48 bits), see fused_tail.h
+  // several query tokens per sequence (matrix-core kernel only)
+  int s_q;                    // query tokens per sequence (1: single-token decode)
+  int tpt;                    // query tokens per 16-column tile: min(s_q, 16 / n_rep)
+  int qtiles;                 // tiles per sequence: ceil(s_q / tpt); grid z = B * qtiles
 };
 
 struct MergeArgs {
+  int s_q;                    // query tokens per sequence: rows are (b, token, head)
   const int32_t* seq_lens;
   const float* ws_o;
   const float2* ws_ml;

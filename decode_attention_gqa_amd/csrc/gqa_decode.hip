@@ -237,6 +237,12 @@ int check_out(const void* out, int out_dtype, size_t qo_elems) {
   return GQA_OK;
 }
 
+// Query tokens per 16-column tile and tiles per sequence for s_q query tokens.
+void query_tiles(int s_q, int nrep, int* tpt, int* qtiles) {
+  *tpt = s_q < 16 / nrep ? s_q : 16 / nrep;
+  *qtiles = (s_q + *tpt - 1) / *tpt;
+}
+
 // Split count, chunk floor and workspace partition of one call.
 struct Plan {
   int ns, min_chunk;
@@ -247,7 +253,8 @@ struct Plan {
 };
 
 int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_hint,
-              void* workspace, size_t workspace_bytes, bool allow_library_ws, Plan* pl) {
+              void* workspace, size_t workspace_bytes, bool allow_library_ws, Plan* pl,
+              int s_q = 1) {
   if (workspace && reinterpret_cast<uintptr_t>(workspace) % 256)
     return fail(GQA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
   if (!workspace && !allow_library_ws) return fail(GQA_ERR_INVALID_ARG, "this entry point needs a workspace");
@@ -256,11 +263,13 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
     int num_cus = 0;
     int st = device_cus(&num_cus);
     if (st != GQA_OK) return st;
-    ns = pick_splits_host(B, h_kv, s_kv_hint, num_cus);
+    int tpt, qtiles;
+    query_tiles(s_q, h_q / h_kv, &tpt, &qtiles);
+    ns = pick_splits_host(B * qtiles, h_kv, s_kv_hint, num_cus);
   }
   pl->ns = ns;
   pl->min_chunk = n_splits > 0 ? 1 : kMinChunk;
-  pl->need = ws_bytes(B, h_q, d_head, ns);
+  pl->need = ws_bytes(B * s_q, h_q, d_head, ns);
   if (workspace) {
     if (workspace_bytes < pl->need)
       return fail(GQA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, pl->need);
@@ -268,7 +277,7 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
     int st = library_workspace(pl->need, &workspace);
     if (st != GQA_OK) return st;
   }
-  const WsLayout lay = ws_layout(B, h_q, d_head, ns);
+  const WsLayout lay = ws_layout(B * s_q, h_q, d_head, ns);
   pl->counters = static_cast<unsigned long long*>(workspace);
   pl->ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.o_off);
   pl->ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + lay.ml_off);
@@ -278,13 +287,16 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
 int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* seq_lens, const int64_t* kv_token_offsets, int B, int h_q, int h_kv,
               int d_head, float scale, int in_dtype, hipStream_t stream, int flags,
-              void* out = nullptr, int out_dtype = GQA_DTYPE_F32) {
+              void* out = nullptr, int out_dtype = GQA_DTYPE_F32, int s_q = 1) {
   const int fused = (flags & GQA_FLAG_FUSED) ? 1 : 0;
+  int tpt, qtiles;
+  query_tiles(s_q, h_q / h_kv, &tpt, &qtiles);
   gqa::SplitArgs sa{q, k_cache, v_cache, seq_lens, kv_token_offsets, pl.ws_o, pl.ws_ml,
                     h_q, h_kv, pl.ns, pl.min_chunk, scale * gqa::kLog2e,
                     fused, out_dtype == GQA_DTYPE_BF16 ? 1 : 0, out, pl.counters,
-                    fused ? (g_call_tag.fetch_add(1) & 0xFFFFFFFFFFFFull) : 0ull};
-  const dim3 grid = gqa::split_grid(pl.ns, h_kv, B);
+                    fused ? (g_call_tag.fetch_add(1) & 0xFFFFFFFFFFFFull) : 0ull,
+                    s_q, tpt, qtiles};
+  const dim3 grid = gqa::split_grid(pl.ns, h_kv, B * qtiles);
   const bool bf16 = in_dtype == GQA_DTYPE_BF16;
   const bool valu = (flags & GQA_FLAG_VALU) != 0;
   const int nrep = h_q / h_kv;
@@ -300,11 +312,11 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
 }
 
 int run_merge(const Plan& pl, const int32_t* seq_lens, void* out, int B, int h_q, int d_head,
-              int out_dtype, hipStream_t stream) {
-  gqa::MergeArgs ma{seq_lens, pl.ws_o, pl.ws_ml, out, h_q, pl.ns, pl.min_chunk};
+              int out_dtype, hipStream_t stream, int s_q = 1) {
+  gqa::MergeArgs ma{s_q, seq_lens, pl.ws_o, pl.ws_ml, out, h_q, pl.ns, pl.min_chunk};
   const bool obf16 = out_dtype == GQA_DTYPE_BF16;
-  hipError_t e = d_head == 128 ? launch_merge<128>(obf16, B, h_q, stream, ma)
-                               : launch_merge<64>(obf16, B, h_q, stream, ma);
+  hipError_t e = d_head == 128 ? launch_merge<128>(obf16, B * s_q, h_q, stream, ma)
+                               : launch_merge<64>(obf16, B * s_q, h_q, stream, ma);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
   return GQA_OK;
 }
@@ -372,6 +384,37 @@ int gqa_decode_merge(const int32_t* seq_lens, const void* workspace, size_t work
                       false, &pl)))
     return st;
   return run_merge(pl, seq_lens, out, B, h_q, d_head, out_dtype, stream);
+}
+
+int gqa_decode_attn_multi(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* seq_lens, const int64_t* kv_token_offsets, void* out,
+                          int B, int S_q, int h_q, int h_kv, int d_head, float scale, int n_splits,
+                          int out_dtype, int64_t s_kv_hint, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  int st;
+  if (!out) return fail(GQA_ERR_INVALID_ARG, "null tensor pointer");
+  if (S_q < 1 || S_q > GQA_MAX_QUERY_TOKENS)
+    return fail(GQA_ERR_INVALID_ARG, "S_q %d not in [1, %d]", S_q, GQA_MAX_QUERY_TOKENS);
+  if ((st = check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets, scale, GQA_DTYPE_BF16, 0))) return st;
+  if ((st = check_shape(B, h_q, h_kv, d_head, n_splits, s_kv_hint))) return st;
+  int tpt, qtiles;
+  query_tiles(S_q, h_q / h_kv, &tpt, &qtiles);
+  if ((int64_t)B * qtiles > 65535) return fail(GQA_ERR_INVALID_ARG, "B * query tiles must be <= 65535");
+  const size_t qo = (size_t)B * S_q * h_q * d_head;
+  if ((st = check_out(out, out_dtype, qo))) return st;
+  const size_t out_el = out_dtype == GQA_DTYPE_BF16 ? 2 : 4;
+  if (overlap(out, qo * out_el, q, qo * 2) || overlap(out, qo * out_el, seq_lens, (size_t)B * 4) ||
+      out == k_cache || out == v_cache)
+    return fail(GQA_ERR_INVALID_ARG, "out overlaps an input");
+  if (workspace && overlap(out, qo * out_el, workspace, workspace_bytes))
+    return fail(GQA_ERR_INVALID_ARG, "out overlaps workspace");
+  Plan pl;
+  if ((st = make_plan(B, h_q, h_kv, d_head, n_splits, s_kv_hint, workspace, workspace_bytes, true, &pl, S_q)))
+    return st;
+  if ((st = run_split(pl, q, k_cache, v_cache, seq_lens, kv_token_offsets, B, h_q, h_kv, d_head, scale,
+                      GQA_DTYPE_BF16, stream, 0, out, out_dtype, S_q)))
+    return st;
+  return run_merge(pl, seq_lens, out, B, h_q, d_head, out_dtype, stream, S_q);
 }
 
 int gqa_decode_attn(const void* q, const void* k_cache, const void* v_cache,

@@ -42,8 +42,8 @@ __global__ __launch_bounds__(256) void merge_splits(MergeArgs a) {
   constexpr int LPS = D / 4;                 // lanes per chunk row (float4 each)
   constexpr int SLOTS = 256 / LPS;           // chunks processed side by side
   constexpr int U = 8;                       // chunks per slot per round
-  const int bh = blockIdx.x;
-  const int b = bh / a.h_q;
+  const int bh = blockIdx.x;                 // row (b, query token, head)
+  const int b = bh / (a.h_q * a.s_q);
   const int tid = threadIdx.x;
   TO* out = static_cast<TO*>(a.out) + (int64_t)bh * D;
   const float2* ml = a.ws_ml + (int64_t)bh * a.n_splits;
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void merge_splits(MergeArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (act[u]) {
-        const float f = fast_exp2(mv[u].x - mn);
+        const float f = rescale(mv[u].x, mn);     // a causal column can have empty chunks
         acc.x += f * ov[u].x;
         acc.y += f * ov[u].y;
         acc.z += f * ov[u].z;

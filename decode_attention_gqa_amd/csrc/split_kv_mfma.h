@@ -103,7 +103,7 @@ struct SoftmaxState {
 template <int D>
 __device__ __forceinline__ void compute_block(const KVRegs<D>& r, const bf16x8 (&qop)[MfmaTile<D>::KS],
                                               f32x4 (&acc)[MfmaTile<D>::NT], SoftmaxState& st,
-                                              float scale_log2, int grp, int nv) {
+                                              float scale_log2, int grp, bool mask, int nvl) {
   constexpr int KS = MfmaTile<D>::KS, NT = MfmaTile<D>::NT;
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -117,23 +117,26 @@ __device__ __forceinline__ void compute_block(const KVRegs<D>& r, const bf16x8 (
     x[i] = s0[i] * scale_log2;
     x[4 + i] = s1[i] * scale_log2;
   }
-  if (nv < 32) {
+  if (mask) {                                // tail of the chunk, or causal limit of the column
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (slot_token(grp, j) >= nv) x[j] = -INFINITY;
+      if (slot_token(grp, j) >= nvl) x[j] = -INFINITY;
   }
   float mb = x[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) mb = fmaxf(mb, x[j]);
   mb = fmaxf(mb, __shfl_xor(mb, 16));
   mb = fmaxf(mb, __shfl_xor(mb, 32));
-  const float mn = fmaxf(st.m, mb);          // finite: token 0 of a block is always valid
-  const float alpha = fast_exp2(st.m - mn);  // 0 on the first block (m = -inf)
+  const float mn = fmaxf(st.m, mb);
+  // mn = -inf only while every position this column has seen is masked (a
+  // causal column before its first position); keep alpha and p at 0 then.
+  const float mref = (mn == -INFINITY) ? 0.f : mn;
+  const float alpha = fast_exp2(st.m - mref);  // 0 on the first block (m = -inf)
   st.m = mn;
   float p[8], ls = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    p[j] = fast_exp2(x[j] - mn);
+    p[j] = fast_exp2(x[j] - mref);
     ls += p[j];
   }
   st.l = st.l * alpha + ls;
@@ -159,9 +162,15 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
   constexpr int KS = MfmaTile<D>::KS, NT = MfmaTile<D>::NT;
   static_assert(NREP >= 1 && NREP <= 16, "one 16-wide MFMA tile holds the query heads of a group");
   const WgCoord wc = wg_coord();
-  const int s = wc.s, g = wc.g, b = wc.b;
+  const int s = wc.s, g = wc.g;
+  const int b = wc.b / a.qtiles, tile = wc.b - b * a.qtiles;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int grp = lane >> 4, n = lane & 15;
+  // Column n of the 16-wide tile: query token qi, head g*NREP + hh.
+  const int ti = n / NREP, hh = n % NREP;
+  const int qi = tile * a.tpt + ti;
+  const bool col = ti < a.tpt && qi < a.s_q;
+  const bool causal = a.s_q > 1;
 
   int S;
   int64_t off;
@@ -179,18 +188,21 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
   const __bf16* kbase = static_cast<const __bf16*>(a.k) + ((off + t0) * a.h_kv + g) * D;
   const __bf16* vbase = static_cast<const __bf16*>(a.v) + ((off + t0) * a.h_kv + g) * D;
 
-  // Q^T as the B operand: lane (grp, n) holds q[head n][32*kk + 8*grp .. +8].
+  // Q^T as the B operand: lane (grp, n) holds q[token qi][head g*NREP + hh][32*kk + 8*grp .. +8].
   bf16x8 qop[KS];
   {
-    const int h = g * NREP + n;
-    const __bf16* qrow = static_cast<const __bf16*>(a.q) + ((int64_t)b * a.h_q + h) * D + 8 * grp;
+    const int h = g * NREP + hh;
+    const __bf16* qrow =
+        static_cast<const __bf16*>(a.q) + (((int64_t)b * a.s_q + qi) * a.h_q + h) * D + 8 * grp;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       uint4 u = make_uint4(0u, 0u, 0u, 0u);
-      if (n < NREP) u = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
+      if (col) u = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
       qop[kk] = __builtin_bit_cast(bf16x8, u);
     }
   }
+  // Last position this lane's query token attends (causal among the new tokens).
+  const int lim = S - a.s_q + qi;
 
   f32x4 acc[NT];
 #pragma unroll
@@ -211,7 +223,8 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
         nvn = min(32, ntok - nb * 32);
         load_block<D>(nxt, kbase + (int64_t)nb * 32 * rs, vbase + (int64_t)nb * 32 * rs, rs, grp, n, nvn);
       }
-      compute_block<D>(cur, qop, acc, st, a.scale_log2, grp, nv);
+      const int nvl = causal ? min(nv, lim - ((int)t0 + blk * 32) + 1) : nv;
+      compute_block<D>(cur, qop, acc, st, a.scale_log2, grp, nv < 32 || causal, nvl);
       if (!more) break;
       cur = nxt;
       nv = nvn;
@@ -225,14 +238,15 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
 
   // Merge the 4 waves' states in LDS and write the workgroup's triplets.
   constexpr int OP = D + 4;                        // padded row (fewer bank conflicts)
+  const int cols = NREP * a.tpt;                                      // columns in use (<= 16)
   __shared__ float sm_m[kWaves][16], sm_l[kWaves][16];
-  __shared__ float sm_o[kWaves][NREP][OP];
+  __shared__ float sm_o[kWaves][16][OP];
   if (grp == 0) {
     sm_m[w][n] = st.m;
     sm_l[w][n] = st.l;
   }
-  if (n < NREP) {
-    // lane (grp, n) holds o[head n][NT*(4*grp + r) + nt]
+  if (n < cols) {
+    // lane (grp, n) holds o[column n][NT*(4*grp + r) + nt]
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -240,8 +254,10 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
   }
   __syncthreads();
   constexpr int Q4 = D / 4;
-  for (int idx = tid; idx < NREP * Q4; idx += kThreads) {
-    const int h = idx / Q4, d4 = (idx % Q4) * 4;
+  for (int idx = tid; idx < cols * Q4; idx += kThreads) {
+    const int h = idx / Q4, d4 = (idx % Q4) * 4;      // h: column of the tile
+    const int cqi = tile * a.tpt + h / NREP;
+    if (cqi >= a.s_q) continue;
     float M = sm_m[0][h];
 #pragma unroll
     for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][h]);
@@ -257,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
       o.z += f * sm_o[ww][h][d4 + 2];
       o.w += f * sm_o[ww][h][d4 + 3];
     }
-    const int64_t row = ((int64_t)b * a.h_q + g * NREP + h) * a.n_splits + s;
+    const int64_t row = (((int64_t)b * a.s_q + cqi) * a.h_q + g * NREP + h % NREP) * a.n_splits + s;
     *reinterpret_cast<float4*>(a.ws_o + row * D + d4) = o;
     if (d4 == 0) a.ws_ml[row] = make_float2(M, L);
   }

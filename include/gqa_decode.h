@@ -85,6 +85,9 @@ enum {
 /* Largest split count. */
 #define GQA_MAX_SPLITS 4096
 
+/* Largest number of query tokens per sequence of gqa_decode_attn_multi. */
+#define GQA_MAX_QUERY_TOKENS 64
+
 /*
  * Attention for bf16 q/k_cache/v_cache in the packed layout, fp32 `out`, on
  * the null stream, with a library-owned workspace (allocated on first use on
@@ -122,6 +125,27 @@ int gqa_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
                        float scale, int n_splits, int in_dtype, int out_dtype,
                        int64_t s_kv_hint, void* workspace, size_t workspace_bytes,
                        hipStream_t stream, int flags);
+
+/*
+ * Several new query tokens per sequence (e.g. verifying speculated tokens):
+ * q and out are [B, S_q, h_q, d_head]; the S_q tokens are the last S_q
+ * positions of sequence b, their K/V rows already in the cache, and token i
+ * (position S_b - S_q + i) attends cache positions [0, S_b - S_q + i] - causal
+ * among the new tokens. A token with S_b - S_q + i < 0 gets zeros. With
+ * S_q = 1 this equals gqa_decode_attn_ex. bf16 inputs (matrix-core kernel),
+ * fp32 or bf16 out, 1 <= S_q <= GQA_MAX_QUERY_TOKENS. Up to 16 / n_rep query
+ * tokens share one pass over the KV range (they fill the columns of the
+ * 16-wide MFMA tile that single-token decode leaves empty when n_rep < 16);
+ * more tokens take more passes. Workspace: gqa_decode_workspace_bytes(B * S_q,
+ * h_q, d_head, n) with n = n_splits if > 0, else
+ * gqa_decode_pick_splits(B * ceil(S_q / t), h_kv, s_kv_hint, 0) where
+ * t = min(S_q, 16 / n_rep). Other arguments as in gqa_decode_attn_ex.
+ */
+int gqa_decode_attn_multi(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* seq_lens, const int64_t* kv_token_offsets, void* out,
+                          int B, int S_q, int h_q, int h_kv, int d_head, float scale, int n_splits,
+                          int out_dtype, int64_t s_kv_hint, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /*
  * The two halves of gqa_decode_attn_ex, for callers that combine partial

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert names == sorted(["gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_partial",
+    assert names == sorted(["gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_attn_multi", "gqa_decode_partial",
                             "gqa_decode_merge", "gqa_decode_pick_splits",
                             "gqa_decode_workspace_bytes", "gqa_status_string", "gqa_last_error",
                             "gqa_decode_set_split_events"])
@@ -46,6 +46,7 @@ def test_status_constants_match_header(gqa):
         m = re.search(rf"\b{name}\s*=\s*(-?\d+)", src)
         assert m and int(m.group(1)) == getattr(gqa, name), name
     assert int(re.search(r"#define GQA_MAX_SPLITS (\d+)", src).group(1)) == gqa.GQA_MAX_SPLITS
+    assert int(re.search(r"#define GQA_MAX_QUERY_TOKENS (\d+)", src).group(1)) == gqa.GQA_MAX_QUERY_TOKENS
 
 
 def test_status_strings(gqa):
@@ -167,3 +168,17 @@ def test_partial_and_merge_check_on_the_host(gqa):
     assert L_.gqa_decode_merge(L, W, 1 << 20, O, 1, 64, 8, 128, 8, 0, 5, None) == -2
     assert L_.gqa_decode_merge(L, W, 16, O, 1, 64, 8, 128, 8, 0, 0, None) == -3
     assert L_.gqa_decode_merge(L, W, 1 << 20, W + 256, 1, 64, 8, 128, 8, 0, 0, None) == -1   # out in workspace
+
+
+def test_multi_token_checks_on_the_host(gqa):
+    L_ = gqa.lib
+    f = lambda **kw: L_.gqa_decode_attn_multi(
+        kw.get("q", Q), K, V, L, None, kw.get("out", O), kw.get("B", 2), kw.get("S_q", 4), kw.get("h_q", 64),
+        8, kw.get("d", 128), 0.088, 0, 0, 0, None, 0, None)
+    assert f(S_q=0) == -1
+    assert f(S_q=65) == -1
+    assert f(q=None) == -1
+    assert f(d=80) == -2
+    assert f(h_q=48) == -2
+    assert f(out=Q) == -1
+    assert f(B=40000, S_q=64) == -1          # B * query tiles > 65535

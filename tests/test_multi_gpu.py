@@ -1,0 +1,87 @@
+"""GPU parity of multi-token decode (S_q query tokens per sequence, causal
+among themselves) against oracle.attend_multi."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import TOL_BF16, TOL_F32, max_err, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def make(name, B, S_q, h_q, h_kv, d, lens, seed):
+    inp = workloads.custom(name, B=B, h_q=h_q, h_kv=h_kv, d=d, seq_lens=lens, seed=seed)
+    qm = workloads.normals(seed, 9, B * S_q * h_q * d).reshape(B, S_q, h_q, d)
+    return inp, qm
+
+
+def run(inp, qm, n_splits=0, out_dtype="f32", poison=True, hint=True):
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    _, k, v, dl = to_device(inp)
+    q = torch.from_numpy(qm.view(np.int16)).cuda().view(torch.bfloat16)
+    w = inp.w
+    B, S_q = qm.shape[0], qm.shape[1]
+    s_max = int(inp.seq_lens.max()) if hint else 0
+    ns = gqa.multi_splits(B, S_q, w.h_q, w.h_kv, s_max, n_splits)
+    ws = torch.empty(gqa.gqa_decode_workspace_bytes(B * S_q, w.h_q, w.d, ns), dtype=torch.uint8, device="cuda")
+    if poison:
+        ws.view(torch.float32).fill_(float("nan"))
+    odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    out = gqa.gqa_decode_attn_multi(q, k, v, dl, scale=float(inp.scale), n_splits=n_splits,
+                                    out_dtype=odt, s_kv_hint=s_max, workspace=ws)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), ns
+
+
+def check(name, inp, qm, **kw):
+    ref = oracle.attend_multi(qm, inp.k, inp.v, inp.seq_lens, inp.scale, inp.w.h_kv, dtype="bf16")
+    got, ns = run(inp, qm, **kw)
+    tol = TOL_BF16 if kw.get("out_dtype") == "bf16" else TOL_F32
+    err = max_err(got, ref)
+    print(f"[multi] {name}: n_splits={ns} max_abs_err={err:.3e}", flush=True)
+    assert err <= tol, f"{name}: {err} > {tol}"
+    return got, ref
+
+
+@pytest.mark.parametrize("n_rep,S_q", [(8, 2), (8, 4), (8, 7), (4, 4), (4, 9), (2, 8), (1, 16), (1, 5), (16, 3)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_multi_parity(n_rep, S_q, d):
+    h_kv = 2
+    lens = [700, 37, 1500]
+    inp, qm = make(f"multi_r{n_rep}_q{S_q}_d{d}", 3, S_q, n_rep * h_kv, h_kv, d, lens, 90 + n_rep + S_q + d)
+    for ns in (0, 5, 64):
+        check(f"n_rep={n_rep} S_q={S_q} d={d} ns={ns}", inp, qm, n_splits=ns)
+
+
+def test_multi_70b_shape_and_bf16_out():
+    inp, qm = make("multi70b", 2, 2, 64, 8, 128, [8192, 3000], 95)
+    check("70B S_q=2", inp, qm)
+    check("70B S_q=2 bf16-out", inp, qm, out_dtype="bf16")
+
+
+def test_multi_short_sequences():
+    """Sequences shorter than S_q (early tokens attend nothing: zeros) and
+    chunks that lie entirely after some tokens' causal limit."""
+    lens = [0, 1, 2, 3, 5, 33, 64]
+    S_q = 4
+    inp, qm = make("multi_short", len(lens), S_q, 16, 2, 128, lens, 96)
+    for ns in (0, 1, 8, 40):
+        got, ref = check(f"short ns={ns}", inp, qm, n_splits=ns)
+        assert np.all(got[0] == 0)                           # S_b = 0
+        assert np.all(got[1, :3] == 0) and np.all(got[2, :2] == 0)
+
+
+def test_single_query_token_equals_one_token_path():
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    inp, qm = make("multi_one", 3, 1, 64, 8, 128, [4000, 77, 1234], 97)
+    got, _ = run(inp, qm)
+    q, k, v, dl = to_device(inp)
+    q1 = torch.from_numpy(qm[:, 0].copy().view(np.int16)).cuda().view(torch.bfloat16)
+    one = gqa.gqa_decode_attn_ex(q1, k, v, dl, scale=float(inp.scale), s_kv_hint=4000)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got[:, 0], one.cpu().numpy().astype(np.float64))
