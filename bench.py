@@ -34,7 +34,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E datasheet peak
 DEFAULT_WORKLOAD = "llama70b_gqa_b1_s8192"
 ROTATE_BYTES = 1 << 30
-KERNEL_SOURCES = ["gqa_common.h", "split_kv_mfma.h", "split_kv_valu.h", "merge.h", "gqa_decode.hip"]
+KERNEL_SOURCES = ["gqa_common.h", "split_kv_mfma.h", "split_kv_valu.h", "merge.h", "fused_tail.h",
+                  "kv_append.h", "gqa_decode.hip"]
 
 
 def log(*a):
@@ -136,6 +137,89 @@ def traffic_from_profile(name: str, src_hash: str):
     return d.get("hbm_bytes_per_launch"), d
 
 
+def bench_append_or_step(args) -> int:
+    """KV-cache append (gqa_kv_append) alone, or a decode step: append one
+    token per sequence, then attend with the new lengths. Padded caches with
+    capacity S_max + n_new rows per sequence, R copies rotated as above."""
+    import numpy as np
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        raise SystemExit("--op append/step use the bf16 workloads")
+    lens0 = workloads.seq_lens_for(w)
+    n_new = args.n_new if args.op == "append" else 1
+    cap = int(lens0.max()) + n_new
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] {args.op}: {w.name}, capacity {cap} rows per sequence")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    cache_bytes = 2 * w.B * cap * w.h_kv * w.d * 2
+    free, _ = torch.cuda.mem_get_info()
+    R = max(1, min(math.ceil(ROTATE_BYTES / cache_bytes), int(0.4 * free // cache_bytes)))
+    caches = [(torch.randn((w.B * cap, w.h_kv, w.d), generator=gen, device=dev, dtype=torch.bfloat16),
+               torch.randn((w.B * cap, w.h_kv, w.d), generator=gen, device=dev, dtype=torch.bfloat16))
+              for _ in range(R)]
+    kn = torch.randn((w.B, n_new, w.h_kv, w.d), generator=gen, device=dev, dtype=torch.bfloat16)
+    vn = torch.randn_like(kn)
+    q = torch.randn((w.B, w.h_q, w.d), generator=gen, device=dev, dtype=torch.bfloat16)
+    lens_in = torch.from_numpy(lens0).to(dev)
+    lens_out = torch.empty_like(lens_in)
+    offs = torch.arange(w.B, dtype=torch.int64, device=dev) * cap
+    ns = gqa.gqa_decode_pick_splits(w.B, w.h_kv, cap)
+    ws = torch.empty(gqa.gqa_decode_workspace_bytes(w.B, w.h_q, w.d, ns), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.B, w.h_q, w.d), dtype=torch.float32, device=dev)
+
+    def step(i):
+        k, v = caches[i % R]
+        # every step appends at the same positions (lens_in is not advanced), so
+        # the timed work is the same in every step
+        gqa.gqa_kv_append(kn, vn, k, v, lens_in, capacity=cap, seq_lens_out=lens_out, kv_token_offsets=offs)
+        if args.op == "step":
+            gqa.gqa_decode_attn_ex(q, k, v, lens_out, out, kv_token_offsets=offs, s_kv_hint=cap, workspace=ws)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(args.steps):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    sec = (t1 - t0) / args.steps
+    appended = 2 * w.B * n_new * w.h_kv * w.d * 2          # bytes written (and read from k_new/v_new)
+    attended = 2 * int((lens0.astype(np.int64) + 1).sum()) * w.h_kv * w.d * 2
+    res = {
+        "metric": "decode step (KV append + attention) us" if args.op == "step" else "KV-cache append bytes/s",
+        "value": round(sec * 1e6, 3) if args.op == "step" else round(2 * appended / sec / 1e9, 3),
+        "unit": "us" if args.op == "step" else "GB/s (read + write)",
+        "higher_is_better": args.op != "step",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": sec * 1e3,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "op": args.op, "B": w.B, "h_kv": w.h_kv, "d_head": w.d,
+                   "new_tokens_per_sequence": n_new, "capacity": cap, "rotating_caches": R,
+                   "timing": "one HIP graph holding the K steps"},
+        "us_per_call": sec * 1e6,
+        "append_bytes_written": appended,
+    }
+    if args.op == "step":
+        res["attended_kv_bytes"] = attended
+        res["effective_kv_gbs"] = attended / sec / 1e9
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +231,10 @@ def main() -> int:
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of a HIP graph")
     ap.add_argument("--s-q", type=int, default=1,
                     help="query tokens per sequence (> 1: multi-token decode, causal among them)")
+    ap.add_argument("--op", choices=["attend", "append", "step"], default="attend",
+                    help="attend (default): the attention call; append: KV-cache append of "
+                         "--n-new tokens per sequence; step: append one token, then attend")
+    ap.add_argument("--n-new", type=int, default=1, help="tokens per sequence for --op append")
     ap.add_argument("--fused", action="store_true",
                     help="single-launch form (GQA_FLAG_FUSED) instead of split + merge kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -168,6 +256,8 @@ def main() -> int:
     import decode_attention_gqa_amd as gqa
     import workloads
 
+    if args.op != "attend":
+        return bench_append_or_step(args)
     src_hash = kernel_source_hash()
     w = workloads.WORKLOADS[args.workload]
     log(f"[bench] workload {w.name}: generating inputs")

@@ -17,7 +17,7 @@ import os
 
 __all__ = [
     "gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_attn_multi", "gqa_decode_partial",
-    "gqa_decode_merge", "GQA_MAX_QUERY_TOKENS",
+    "gqa_decode_merge", "gqa_kv_append", "GQA_MAX_QUERY_TOKENS",
     "gqa_decode_pick_splits",
     "gqa_decode_workspace_bytes", "gqa_status_string", "GQAError", "lib", "LIB_PATH",
     "GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_WORKSPACE", "GQA_ERR_HIP",
@@ -62,6 +62,8 @@ lib.gqa_decode_attn_ex.restype = _i32
 lib.gqa_decode_attn_multi.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                       _i32, _i64, _vp, _sz, _vp]
 lib.gqa_decode_attn_multi.restype = _i32
+lib.gqa_kv_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _vp]
+lib.gqa_kv_append.restype = _i32
 lib.gqa_decode_partial.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i64,
                                    _vp, _sz, _vp, _i32]
 lib.gqa_decode_partial.restype = _i32
@@ -236,6 +238,35 @@ def gqa_decode_attn_multi(q, k_cache, v_cache, seq_lens, out=None, *, scale=None
     if r != GQA_OK:
         raise GQAError(r, "gqa_decode_attn_multi")
     return out
+
+
+def gqa_kv_append(k_new, v_new, k_cache, v_cache, seq_lens, *, capacity, seq_lens_out=None,
+                  kv_token_offsets=None, stream=None):
+    """Write new tokens' K/V rows ([B, n_new, h_kv, d]) into a padded cache at
+    positions seq_lens[b] + i; optionally write the new lengths to
+    seq_lens_out (a different int32 [B] tensor)."""
+    torch = _torch()
+    B, n_new, h_kv, d = k_new.shape
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("seq_lens", seq_lens)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if v_new.shape != k_new.shape or k_cache.dtype != k_new.dtype or v_cache.dtype != k_new.dtype:
+        raise ValueError("k_new/v_new shapes or dtypes do not match the cache")
+    if k_cache.shape[1:] != (h_kv, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [T, h_kv, d_head]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    with torch.cuda.device(k_new.device):
+        st = stream if stream is not None else torch.cuda.current_stream(k_new.device)
+        r = lib.gqa_kv_append(k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                              kv_token_offsets.data_ptr() if kv_token_offsets is not None else None,
+                              seq_lens.data_ptr(),
+                              seq_lens_out.data_ptr() if seq_lens_out is not None else None,
+                              B, n_new, h_kv, d, _dtype_code(k_new.dtype), int(capacity),
+                              ctypes.c_void_p(st.cuda_stream))
+    if r != GQA_OK:
+        raise GQAError(r, "gqa_kv_append")
 
 
 def gqa_decode_partial(q, k_cache, v_cache, seq_lens, workspace, *, scale=None, n_splits=0,

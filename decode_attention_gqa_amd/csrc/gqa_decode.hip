@@ -14,6 +14,7 @@
 
 #include "gqa_common.h"
 #include "fused_tail.h"
+#include "kv_append.h"
 #include "merge.h"
 #include "split_kv_mfma.h"
 #include "split_kv_valu.h"
@@ -415,6 +416,33 @@ int gqa_decode_attn_multi(const void* q, const void* k_cache, const void* v_cach
                       GQA_DTYPE_BF16, stream, 0, out, out_dtype, S_q)))
     return st;
   return run_merge(pl, seq_lens, out, B, h_q, d_head, out_dtype, stream, S_q);
+}
+
+int gqa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                  const int64_t* kv_token_offsets, const int32_t* seq_lens, int32_t* seq_lens_out,
+                  int B, int n_new, int h_kv, int d_head, int dtype, int64_t capacity,
+                  hipStream_t stream) {
+  if (!k_new || !v_new || !k_cache || !v_cache || !seq_lens) return fail(GQA_ERR_INVALID_ARG, "null pointer");
+  if (B < 1 || B > 65535 || n_new < 1 || h_kv < 1 || capacity < 1)
+    return fail(GQA_ERR_INVALID_ARG, "B, n_new, h_kv, capacity must be >= 1 (B <= 65535)");
+  if (d_head != 64 && d_head != 128) return fail(GQA_ERR_UNSUPPORTED, "d_head %d not in {64, 128}", d_head);
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16) return fail(GQA_ERR_UNSUPPORTED, "dtype %d", dtype);
+  for (const void* p : {k_new, v_new, (const void*)k_cache, (const void*)v_cache})
+    if (reinterpret_cast<uintptr_t>(p) % 16) return fail(GQA_ERR_INVALID_ARG, "tensor pointer not 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(seq_lens) % 4 || reinterpret_cast<uintptr_t>(seq_lens_out) % 4 ||
+      reinterpret_cast<uintptr_t>(kv_token_offsets) % 8)
+    return fail(GQA_ERR_INVALID_ARG, "seq_lens / offsets misaligned");
+  if (seq_lens_out && overlap(seq_lens_out, (size_t)B * 4, seq_lens, (size_t)B * 4))
+    return fail(GQA_ERR_INVALID_ARG, "seq_lens_out overlaps seq_lens");
+  const size_t el = dtype == GQA_DTYPE_BF16 ? 2 : 4;
+  const int64_t row_bytes = (int64_t)h_kv * d_head * (int64_t)el;
+  if (row_bytes / 16 > INT32_MAX) return fail(GQA_ERR_INVALID_ARG, "token row too large");
+  gqa::AppendArgs aa{k_new, v_new, k_cache, v_cache, kv_token_offsets, seq_lens, seq_lens_out,
+                     n_new, (int)(row_bytes / 16), capacity};
+  hipLaunchKernelGGL(gqa::kv_append_rows, dim3((unsigned)n_new, (unsigned)B), dim3(256), 0, stream, aa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "append kernel launch: %s", hipGetErrorString(e));
+  return GQA_OK;
 }
 
 int gqa_decode_attn(const void* q, const void* k_cache, const void* v_cache,

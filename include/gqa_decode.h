@@ -148,6 +148,23 @@ int gqa_decode_attn_multi(const void* q, const void* k_cache, const void* v_cach
                           hipStream_t stream);
 
 /*
+ * KV-cache append, the step before attention at each decode step (the
+ * tt-metal Llama burndown's update_cache): for every sequence b and new token
+ * i < n_new, copy k_new[b, i] and v_new[b, i] ([B, n_new, h_kv, d_head], the
+ * cache's dtype) to token row off_b + seq_lens[b] + i of k_cache / v_cache,
+ * where off_b = kv_token_offsets[b], or b * capacity if kv_token_offsets is
+ * NULL (a padded [B, capacity, h_kv, d_head] cache). Each sequence owns
+ * `capacity` rows: new rows at positions >= capacity are dropped. If
+ * seq_lens_out is not NULL it receives min(seq_lens[b] + n_new, capacity);
+ * it must not overlap seq_lens (alternate two length buffers across steps).
+ * dtype: GQA_DTYPE_BF16 or GQA_DTYPE_F32. Asynchronous on `stream`.
+ */
+int gqa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                  const int64_t* kv_token_offsets, const int32_t* seq_lens, int32_t* seq_lens_out,
+                  int B, int n_new, int h_kv, int d_head, int dtype, int64_t capacity,
+                  hipStream_t stream);
+
+/*
  * The two halves of gqa_decode_attn_ex, for callers that combine partial
  * results from several sources (e.g. KV sharded across GPUs along the
  * sequence: each GPU writes its triplets, they are exchanged, one merge

@@ -150,6 +150,30 @@ def attend_multi(q, k, v, seq_lens, scale, h_kv: int, dtype: str = "bf16") -> np
     return out
 
 
+def kv_append(k_cache, v_cache, k_new, v_new, seq_lens, capacity: int, kv_offsets=None):
+    """Write new tokens' K/V rows into a padded cache (a copy is returned).
+
+    Sequence b owns token rows [off_b, off_b + capacity) with off_b =
+    kv_offsets[b], or b * capacity; its cached length is seq_lens[b]. New row
+    i (k_new[b, i]) goes to row off_b + seq_lens[b] + i when that position is
+    below `capacity`, and is dropped otherwise. Returns (k_cache', v_cache',
+    new lengths = min(seq_lens + n_new, capacity)). The step the tt-metal
+    burndown calls update_cache, run before attention at every decode step.
+    """
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    B, n_new = k_new.shape[0], k_new.shape[1]
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    for b in range(B):
+        off = int(kv_offsets[b]) if kv_offsets is not None else b * capacity
+        for i in range(n_new):
+            pos = int(lens[b]) + i
+            if pos < capacity:
+                kc[off + pos] = k_new[b, i]
+                vc[off + pos] = v_new[b, i]
+    return kc, vc, np.minimum(lens + n_new, capacity).astype(np.int32)
+
+
 # ------------------------------------------- triplets, merge, final o / l
 def scores(q_row: np.ndarray, k_rows: np.ndarray, scale) -> np.ndarray:
     """s_t = scale * <q, K_t> for one query head (float64 inputs)."""

@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_attn_multi", "gqa_decode_partial",
-                            "gqa_decode_merge", "gqa_decode_pick_splits",
+                            "gqa_decode_merge", "gqa_kv_append", "gqa_decode_pick_splits",
                             "gqa_decode_workspace_bytes", "gqa_status_string", "gqa_last_error",
                             "gqa_decode_set_split_events"])
 
@@ -182,3 +182,15 @@ def test_multi_token_checks_on_the_host(gqa):
     assert f(h_q=48) == -2
     assert f(out=Q) == -1
     assert f(B=40000, S_q=64) == -1          # B * query tiles > 65535
+
+
+def test_kv_append_checks_on_the_host(gqa):
+    f = lambda **kw: gqa.lib.gqa_kv_append(kw.get("kn", Q), V, K, O, None, L, kw.get("lo", None), kw.get("B", 2),
+                                           kw.get("n", 1), 8, kw.get("d", 128), kw.get("dt", 1), kw.get("cap", 100), None)
+    assert f(kn=None) == -1
+    assert f(n=0) == -1
+    assert f(cap=0) == -1
+    assert f(d=96) == -2
+    assert f(dt=5) == -2
+    assert f(lo=L) == -1                       # lengths out overlaps lengths in
+    assert f(kn=Q + 4) == -1
