@@ -17,7 +17,8 @@ import os
 
 __all__ = [
     "gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_attn_multi", "gqa_decode_partial",
-    "gqa_decode_merge", "gqa_kv_append", "GQA_MAX_QUERY_TOKENS",
+    "gqa_decode_merge", "gqa_kv_append", "gqa_decode_attn_triplet", "gqa_merge_triplets",
+    "GQA_MAX_QUERY_TOKENS",
     "gqa_decode_pick_splits",
     "gqa_decode_workspace_bytes", "gqa_status_string", "GQAError", "lib", "LIB_PATH",
     "GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_WORKSPACE", "GQA_ERR_HIP",
@@ -62,6 +63,11 @@ lib.gqa_decode_attn_ex.restype = _i32
 lib.gqa_decode_attn_multi.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                       _i32, _i64, _vp, _sz, _vp]
 lib.gqa_decode_attn_multi.restype = _i32
+lib.gqa_decode_attn_triplet.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32,
+                                        _i32, _i64, _vp, _sz, _vp, _i32]
+lib.gqa_decode_attn_triplet.restype = _i32
+lib.gqa_merge_triplets.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp]
+lib.gqa_merge_triplets.restype = _i32
 lib.gqa_kv_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _vp]
 lib.gqa_kv_append.restype = _i32
 lib.gqa_decode_partial.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i64,
@@ -237,6 +243,56 @@ def gqa_decode_attn_multi(q, k_cache, v_cache, seq_lens, out=None, *, scale=None
             ctypes.c_void_p(st.cuda_stream))
     if r != GQA_OK:
         raise GQAError(r, "gqa_decode_attn_multi")
+    return out
+
+
+def gqa_decode_attn_triplet(q, k_cache, v_cache, seq_lens, *, scale=None, n_splits=0, s_kv_hint=0,
+                            kv_token_offsets=None, workspace=None, stream=None):
+    """This shard's (m, l, o) per (b, h) over its own KV: returns
+    (ml [B, h_q, 2] fp32, o [B, h_q, d] fp32), m and the exponentials in log2
+    units (see include/gqa_decode.h)."""
+    torch = _torch()
+    _check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets)
+    B, h_q, d = q.shape
+    h_kv = k_cache.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ml = torch.empty((B, h_q, 2), dtype=torch.float32, device=q.device)
+    o = torch.empty((B, h_q, d), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        ns = n_splits if n_splits > 0 else gqa_decode_pick_splits(B, h_kv, int(s_kv_hint), 0)
+        if workspace is None:
+            workspace = torch.empty(gqa_decode_workspace_bytes(B, h_q, d, ns), dtype=torch.uint8, device=q.device)
+        st = stream if stream is not None else torch.cuda.current_stream(q.device)
+        r = lib.gqa_decode_attn_triplet(
+            q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+            kv_token_offsets.data_ptr() if kv_token_offsets is not None else None,
+            ml.data_ptr(), o.data_ptr(), B, h_q, h_kv, d, float(scale), int(n_splits),
+            _dtype_code(q.dtype), int(s_kv_hint), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), ctypes.c_void_p(st.cuda_stream), 0)
+    if r != GQA_OK:
+        raise GQAError(r, "gqa_decode_attn_triplet")
+    return ml, o
+
+
+def gqa_merge_triplets(ml, o, out_dtype=None, stream=None):
+    """Merge triplet sets stacked part-major: ml [P, ..., 2], o [P, ..., d]
+    (the leading dims after P are the rows). Returns out [..., d]."""
+    torch = _torch()
+    P, d = ml.shape[0], o.shape[-1]
+    rows = ml[0].numel() // 2
+    if o.shape[0] != P or o[0].numel() != rows * d or ml.dtype != torch.float32 or o.dtype != torch.float32:
+        raise ValueError("ml must be [P, rows..., 2] and o [P, rows..., d], fp32")
+    if not ml.is_contiguous() or not o.is_contiguous():
+        raise ValueError("ml and o must be contiguous")
+    out_dtype = out_dtype or torch.float32
+    out = torch.empty(o.shape[1:], dtype=out_dtype, device=o.device)
+    with torch.cuda.device(o.device):
+        st = stream if stream is not None else torch.cuda.current_stream(o.device)
+        r = lib.gqa_merge_triplets(ml.data_ptr(), o.data_ptr(), P, rows, d, out.data_ptr(),
+                                   _dtype_code(out_dtype), ctypes.c_void_p(st.cuda_stream))
+    if r != GQA_OK:
+        raise GQAError(r, "gqa_merge_triplets")
     return out
 
 

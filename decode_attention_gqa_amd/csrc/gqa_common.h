@@ -41,13 +41,16 @@ struct SplitArgs {
 
 struct MergeArgs {
   int s_q;                    // query tokens per sequence: rows are (b, token, head)
-  const int32_t* seq_lens;
-  const float* ws_o;
-  const float2* ws_ml;
-  void* out;                  // [B, h_q, D] fp32 or bf16
+  const int32_t* seq_lens;    // nullptr: every one of the n_splits parts is present
+  const float* ws_o;          // part i of row r: o at ((r * row_stride + i * part_stride) * D)
+  const float2* ws_ml;        //                  (m, l) at r * row_stride + i * part_stride
+  void* out;                  // [rows, D] fp32 or bf16 (o / l), unless tri_ml is set
   int h_q;
   int n_splits;
   int min_chunk;
+  int64_t row_stride, part_stride;
+  float2* tri_ml;             // if set: write the merged (m, l) per row here ...
+  float* tri_o;               // ... and the merged unnormalised o [rows, D], instead of out
 };
 
 // Chunk length and number of non-empty chunks of a sequence of S tokens.

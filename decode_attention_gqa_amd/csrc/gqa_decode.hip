@@ -313,8 +313,10 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
 }
 
 int run_merge(const Plan& pl, const int32_t* seq_lens, void* out, int B, int h_q, int d_head,
-              int out_dtype, hipStream_t stream, int s_q = 1) {
-  gqa::MergeArgs ma{s_q, seq_lens, pl.ws_o, pl.ws_ml, out, h_q, pl.ns, pl.min_chunk};
+              int out_dtype, hipStream_t stream, int s_q = 1, float2* tri_ml = nullptr,
+              float* tri_o = nullptr) {
+  gqa::MergeArgs ma{s_q, seq_lens, pl.ws_o, pl.ws_ml, out, h_q, pl.ns, pl.min_chunk,
+                    pl.ns, 1, tri_ml, tri_o};
   const bool obf16 = out_dtype == GQA_DTYPE_BF16;
   hipError_t e = d_head == 128 ? launch_merge<128>(obf16, B * s_q, h_q, stream, ma)
                                : launch_merge<64>(obf16, B * s_q, h_q, stream, ma);
@@ -442,6 +444,54 @@ int gqa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_c
   hipLaunchKernelGGL(gqa::kv_append_rows, dim3((unsigned)n_new, (unsigned)B), dim3(256), 0, stream, aa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "append kernel launch: %s", hipGetErrorString(e));
+  return GQA_OK;
+}
+
+int gqa_decode_attn_triplet(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, const int64_t* kv_token_offsets,
+                            float* ml_out, float* o_out, int B, int h_q, int h_kv, int d_head,
+                            float scale, int n_splits, int in_dtype, int64_t s_kv_hint,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream, int flags) {
+  int st;
+  if (!ml_out || !o_out) return fail(GQA_ERR_INVALID_ARG, "null pointer");
+  if ((st = check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets, scale, in_dtype, flags))) return st;
+  if (flags & GQA_FLAG_FUSED) return fail(GQA_ERR_INVALID_ARG, "GQA_FLAG_FUSED does not apply here");
+  if ((st = check_shape(B, h_q, h_kv, d_head, n_splits, s_kv_hint))) return st;
+  if (reinterpret_cast<uintptr_t>(ml_out) % 8 || reinterpret_cast<uintptr_t>(o_out) % 16)
+    return fail(GQA_ERR_INVALID_ARG, "ml_out / o_out misaligned");
+  const size_t rows = (size_t)B * h_q;
+  if (overlap(ml_out, rows * 8, o_out, rows * d_head * 4) ||
+      (workspace && (overlap(ml_out, rows * 8, workspace, workspace_bytes) ||
+                     overlap(o_out, rows * d_head * 4, workspace, workspace_bytes))))
+    return fail(GQA_ERR_INVALID_ARG, "outputs overlap");
+  Plan pl;
+  if ((st = make_plan(B, h_q, h_kv, d_head, n_splits, s_kv_hint, workspace, workspace_bytes, true, &pl))) return st;
+  if ((st = run_split(pl, q, k_cache, v_cache, seq_lens, kv_token_offsets, B, h_q, h_kv, d_head, scale,
+                      in_dtype, stream, flags)))
+    return st;
+  return run_merge(pl, seq_lens, nullptr, B, h_q, d_head, GQA_DTYPE_F32, stream, 1,
+                   reinterpret_cast<float2*>(ml_out), o_out);
+}
+
+int gqa_merge_triplets(const float* ml, const float* o, int parts, int rows, int d_head,
+                       void* out, int out_dtype, hipStream_t stream) {
+  int st;
+  if (!ml || !o) return fail(GQA_ERR_INVALID_ARG, "null pointer");
+  if (parts < 1 || rows < 1) return fail(GQA_ERR_INVALID_ARG, "parts and rows must be >= 1");
+  if (d_head != 64 && d_head != 128) return fail(GQA_ERR_UNSUPPORTED, "d_head %d not in {64, 128}", d_head);
+  if (reinterpret_cast<uintptr_t>(ml) % 8 || reinterpret_cast<uintptr_t>(o) % 16)
+    return fail(GQA_ERR_INVALID_ARG, "ml / o misaligned");
+  if ((st = check_out(out, out_dtype, (size_t)rows * d_head))) return st;
+  const size_t out_el = out_dtype == GQA_DTYPE_BF16 ? 2 : 4, n = (size_t)parts * rows;
+  if (overlap(out, (size_t)rows * d_head * out_el, ml, n * 8) ||
+      overlap(out, (size_t)rows * d_head * out_el, o, n * d_head * 4))
+    return fail(GQA_ERR_INVALID_ARG, "out overlaps an input");
+  gqa::MergeArgs ma{1, nullptr, o, reinterpret_cast<const float2*>(ml), out, 1, parts, 1,
+                    1, rows, nullptr, nullptr};
+  const bool obf16 = out_dtype == GQA_DTYPE_BF16;
+  hipError_t e = d_head == 128 ? launch_merge<128>(obf16, rows, 1, stream, ma)
+                               : launch_merge<64>(obf16, rows, 1, stream, ma);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
   return GQA_OK;
 }
 

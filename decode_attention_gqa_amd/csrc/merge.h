@@ -45,9 +45,9 @@ __global__ __launch_bounds__(256) void merge_splits(MergeArgs a) {
   const int bh = blockIdx.x;                 // row (b, query token, head)
   const int b = bh / (a.h_q * a.s_q);
   const int tid = threadIdx.x;
-  TO* out = static_cast<TO*>(a.out) + (int64_t)bh * D;
-  const float2* ml = a.ws_ml + (int64_t)bh * a.n_splits;
-  const float* o = a.ws_o + (int64_t)bh * a.n_splits * D;
+  const int64_t ps = a.part_stride;
+  const float2* ml = a.ws_ml + (int64_t)bh * a.row_stride;
+  const float* o = a.ws_o + (int64_t)bh * a.row_stride * D;
   const int slot = tid / LPS, q = tid % LPS;
 
   // The loads of a round do not wait for seq_lens: indices are clamped into
@@ -62,8 +62,8 @@ __global__ __launch_bounds__(256) void merge_splits(MergeArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = min(base + u * SLOTS + slot, a.n_splits - 1);
-      mv[u] = ml[i];
-      ov[u] = *reinterpret_cast<const float4*>(o + (int64_t)i * D + 4 * q);
+      mv[u] = ml[i * ps];
+      ov[u] = *reinterpret_cast<const float4*>(o + i * ps * D + 4 * q);
     }
   };
   auto merge_round = [&](int base, int n_active) {
@@ -92,8 +92,8 @@ __global__ __launch_bounds__(256) void merge_splits(MergeArgs a) {
   };
   load_round(0);
   __builtin_amdgcn_sched_barrier(0);           // keep the first loads ahead of the seq_lens wait
-  int c, n_active;
-  chunking(a.seq_lens[b], a.n_splits, a.min_chunk, c, n_active);
+  int c, n_active = a.n_splits;
+  if (a.seq_lens) chunking(a.seq_lens[b], a.n_splits, a.min_chunk, c, n_active);
   merge_round(0, n_active);
   for (int base = SLOTS * U; base < n_active; base += SLOTS * U) {
     load_round(base);
@@ -124,9 +124,15 @@ __global__ __launch_bounds__(256) void merge_splits(MergeArgs a) {
       r.w += f * y.w;
       Lt += f * sl[k];
     }
-    // Lt = 0 only for an empty sequence (S = 0): nothing attended, out = 0.
-    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
-    store4<TO>(out + 4 * tid, make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv));
+    if (a.tri_ml) {                          // merged triplet, relative to M
+      if (tid == 0) a.tri_ml[bh] = make_float2(M, Lt);
+      *reinterpret_cast<float4*>(a.tri_o + (int64_t)bh * D + 4 * tid) = r;
+    } else {
+      // Lt = 0 only when nothing was attended (empty sequence): out = 0.
+      const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+      TO* out = static_cast<TO*>(a.out) + (int64_t)bh * D;
+      store4<TO>(out + 4 * tid, make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv));
+    }
   }
 }
 

@@ -165,6 +165,32 @@ int gqa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_c
                   hipStream_t stream);
 
 /*
+ * Sequence-sharded attention (the kernbench2 page's scheme: every shard
+ * holds a slice of each sequence's KV and all of q; shards exchange (m, l, o)
+ * triplets and merge them exactly).
+ *
+ * gqa_decode_attn_triplet computes this shard's attention over its own KV
+ * (same arguments as gqa_decode_attn_ex) but, instead of o / l, writes the
+ * shard's merged triplet per (b, h): ml_out[2*(b*h_q + h) + {0, 1}] = (m, l)
+ * and o_out[(b*h_q + h)*d_head + i], with m = max_t x_t, l = sum_t 2^(x_t - m),
+ * o = sum_t 2^(x_t - m) V_t and x_t = scale * log2(e) * <q, K_t> (log2 units).
+ * A shard with no tokens of a sequence gives (-inf, 0, 0).
+ *
+ * gqa_merge_triplets merges `parts` such triplet sets laid out part-major
+ * (ml [parts][rows][2], o [parts][rows][d_head], e.g. gathered from the
+ * shards) into out [rows, d_head] = (sum_p 2^(m_p - M) o_p) / (sum_p 2^(m_p - M) l_p),
+ * M = max_p m_p; rows with nothing attended give zeros. fp32 or bf16 out.
+ */
+int gqa_decode_attn_triplet(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, const int64_t* kv_token_offsets,
+                            float* ml_out, float* o_out, int B, int h_q, int h_kv, int d_head,
+                            float scale, int n_splits, int in_dtype, int64_t s_kv_hint,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream, int flags);
+
+int gqa_merge_triplets(const float* ml, const float* o, int parts, int rows, int d_head,
+                       void* out, int out_dtype, hipStream_t stream);
+
+/*
  * The two halves of gqa_decode_attn_ex, for callers that combine partial
  * results from several sources (e.g. KV sharded across GPUs along the
  * sequence: each GPU writes its triplets, they are exchanged, one merge

@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_attn_multi", "gqa_decode_partial",
-                            "gqa_decode_merge", "gqa_kv_append", "gqa_decode_pick_splits",
+                            "gqa_decode_merge", "gqa_kv_append", "gqa_decode_attn_triplet",
+                            "gqa_merge_triplets", "gqa_decode_pick_splits",
                             "gqa_decode_workspace_bytes", "gqa_status_string", "gqa_last_error",
                             "gqa_decode_set_split_events"])
 
@@ -194,3 +195,21 @@ def test_kv_append_checks_on_the_host(gqa):
     assert f(dt=5) == -2
     assert f(lo=L) == -1                       # lengths out overlaps lengths in
     assert f(kn=Q + 4) == -1
+
+
+def test_sharded_entry_points_check_on_the_host(gqa):
+    L_ = gqa.lib
+    t = lambda **kw: L_.gqa_decode_attn_triplet(Q, K, V, L, None, kw.get("ml", W), kw.get("o", W + 4096), 1, 64, 8,
+                                                kw.get("d", 128), 0.088, 0, 1, 0, None, 0, None, kw.get("fl", 0))
+    assert t(ml=None) == -1
+    assert t(d=96) == -2
+    assert t(fl=2) == -1
+    assert t(o=W + 8) == -1                  # misaligned
+    assert t(o=W) == -1                      # ml and o overlap
+    m = lambda **kw: L_.gqa_merge_triplets(kw.get("ml", W), kw.get("o", W + (1 << 16)), kw.get("p", 4),
+                                           kw.get("r", 64), kw.get("d", 128), kw.get("out", O), kw.get("dt", 0), None)
+    assert m(ml=None) == -1
+    assert m(p=0) == -1
+    assert m(d=80) == -2
+    assert m(dt=3) == -2
+    assert m(out=W + (1 << 16)) == -1        # out overlaps o
