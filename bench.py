@@ -226,6 +226,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seq-lens", default="",
+                    help="comma-separated lengths overriding the workload's (B = their count)")
     ap.add_argument("--n-splits", type=int, default=0)
     ap.add_argument("--valu", action="store_true", help="vector-ALU split kernel (comparison)")
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of a HIP graph")
@@ -260,8 +262,15 @@ def main() -> int:
         return bench_append_or_step(args)
     src_hash = kernel_source_hash()
     w = workloads.WORKLOADS[args.workload]
-    log(f"[bench] workload {w.name}: generating inputs")
-    inp = workloads.make_inputs(w)
+    if args.seq_lens:
+        lens_o = [int(x) for x in args.seq_lens.split(",")]
+        inp = workloads.custom(f"{w.name}_lens", B=len(lens_o), h_q=w.h_q, h_kv=w.h_kv, d=w.d,
+                               seq_lens=lens_o, dtype=w.dtype, seed=w.seed, k_sigma=w.k_sigma)
+        w = inp.w
+        log(f"[bench] custom lengths {lens_o} with the shapes of {args.workload}")
+    else:
+        log(f"[bench] workload {w.name}: generating inputs")
+        inp = workloads.make_inputs(w)
     kv_bytes = inp.kv_bytes()
     s_max = int(inp.seq_lens.max())
     dev = torch.device("cuda:0")
