@@ -38,7 +38,9 @@ int fail(int status, const char* fmt, ...) {
 // Heuristic constants (see gqa_decode_pick_splits).
 constexpr int kTargetWgPerCu = 2;    // resident split workgroups per CU the grid aims for
 constexpr int kMinChunk = 128;       // tokens: one 32-token block per wave of a workgroup
-constexpr int kBalance = 4;          // workgroups per resident slot for the longest sequence
+constexpr int kRoundsOne = 2;        // B = 1: rounds of resident slots the workgroups fill
+constexpr int kRoundsMany = 4;       // B > 1: rounds the longest sequence is spread over
+constexpr int64_t kMaxChunk = 4096;  // tokens: longer chunks leave too few workgroups
 
 // Library-owned fallback workspace, one grow-only buffer per device.
 std::mutex g_ws_mu;
@@ -128,14 +130,25 @@ hipError_t launch_split_nrep(int nrep, bool bf16, bool valu, dim3 grid, hipStrea
   }
 }
 
+template <int D, typename TO>
+hipError_t launch_merge_t(int rows, hipStream_t st, const gqa::MergeArgs& a) {
+  // chunks per slot in the first round: one round covers up to 32 * U chunks
+  const dim3 grid((unsigned)rows, D / 32);
+  if (a.n_splits <= 32)
+    hipLaunchKernelGGL((gqa::merge_splits<D, TO, 1>), grid, dim3(256), 0, st, a);
+  else if (a.n_splits <= 64)
+    hipLaunchKernelGGL((gqa::merge_splits<D, TO, 2>), grid, dim3(256), 0, st, a);
+  else if (a.n_splits <= 128)
+    hipLaunchKernelGGL((gqa::merge_splits<D, TO, 4>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((gqa::merge_splits<D, TO, 8>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_merge(bool out_bf16, int B, int h_q, hipStream_t st, const gqa::MergeArgs& a) {
-  dim3 grid((unsigned)((int64_t)B * h_q));
-  if (out_bf16)
-    hipLaunchKernelGGL((gqa::merge_splits<D, __bf16>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((gqa::merge_splits<D, float>), grid, dim3(256), 0, st, a);
-  return hipGetLastError();
+  const int64_t rows = (int64_t)B * h_q;
+  return out_bf16 ? launch_merge_t<D, __bf16>((int)rows, st, a) : launch_merge_t<D, float>((int)rows, st, a);
 }
 
 int pick_splits_host(int B, int h_kv, int64_t s_kv_max, int num_cus) {
@@ -145,9 +158,15 @@ int pick_splits_host(int B, int h_kv, int64_t s_kv_max, int num_cus) {
   int64_t n = (slots + units - 1) / units;
   if (s_kv_max > 0) {
     // ... and, when the longest sequence is known, chunks short enough that
-    // its workgroups are spread over about kBalance rounds of the resident
-    // slots (ragged batches stay balanced), never shorter than kMinChunk.
-    int64_t chunk = (s_kv_max * units + kBalance * slots - 1) / (kBalance * slots);
+    // its workgroups are spread over a few rounds of the resident slots:
+    // two for a single sequence (every chunk is equally long, and a second
+    // round hides each workgroup's start-up behind another's streaming),
+    // four when there are several (only the longest length is known, so
+    // more rounds keep a ragged batch balanced); chunks stay within
+    // [kMinChunk, kMaxChunk] tokens.
+    const int64_t rounds = B == 1 ? kRoundsOne : kRoundsMany;
+    int64_t chunk = (s_kv_max * units + rounds * slots - 1) / (rounds * slots);
+    if (chunk > kMaxChunk) chunk = kMaxChunk;
     if (chunk < kMinChunk) chunk = kMinChunk;
     const int64_t by_len = (s_kv_max + chunk - 1) / chunk;
     if (by_len > n) n = by_len;

@@ -8,11 +8,13 @@
 // Every chunk below n_active is non-empty, so M is finite and l > 0 unless
 // the sequence is empty.
 //
-// One workgroup per (sequence, head). Its threads form SLOTS row slots of
-// D/4 lanes (a float4 of the row each); a slot takes every SLOTS-th chunk,
-// U chunks per round with all their loads issued before any is used, and
-// keeps its own running (m, l, o) - the same merge rule applied
-// incrementally. The slots' states are merged once more through LDS.
+// Grid (row, 32-column slice of d). A workgroup's 256 threads form 32 chunk
+// slots of 8 lanes (a float4 of the slice each); slot j takes chunks j,
+// j + 32, ... U of them per round, with every load of a round issued before
+// any is used, so up to 32 * U chunks cost one memory latency. The global
+// max M is taken first (over the m values of all chunks), so each chunk's
+// weight is final when its o arrives and the slots' partial sums add up
+// without rescaling: in-wave shuffles, then one LDS step over the 4 waves.
 #pragma once
 
 #include "gqa_common.h"
@@ -37,100 +39,104 @@ __device__ __forceinline__ float rescale(float m, float M) {
   return (m == -INFINITY) ? 0.f : fast_exp2(m - M);
 }
 
-template <int D, typename TO>
+template <int D, typename TO, int U>
 __global__ __launch_bounds__(256) void merge_splits(MergeArgs a) {
-  constexpr int LPS = D / 4;                 // lanes per chunk row (float4 each)
+  constexpr int LPS = 8;                     // lanes per chunk: a float4 each of a 32-column slice
   constexpr int SLOTS = 256 / LPS;           // chunks processed side by side
-  constexpr int U = 8;                       // chunks per slot per round
+  constexpr int R = SLOTS * U;               // chunks per round
   const int bh = blockIdx.x;                 // row (b, query token, head)
+  const int d0 = blockIdx.y * 4 * LPS;       // first column of the slice
   const int b = bh / (a.h_q * a.s_q);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6;
   const int64_t ps = a.part_stride;
   const float2* ml = a.ws_ml + (int64_t)bh * a.row_stride;
-  const float* o = a.ws_o + (int64_t)bh * a.row_stride * D;
   const int slot = tid / LPS, q = tid % LPS;
+  const float* o = a.ws_o + (int64_t)bh * a.row_stride * D + d0 + 4 * q;
 
-  // The loads of a round do not wait for seq_lens: indices are clamped into
-  // [0, n_splits), so every load is in bounds and none sits in a branch, and
-  // rows of chunks that turn out to be empty (never written by the split
+  // The first round's loads do not wait for seq_lens: indices are clamped
+  // into [0, n_splits), so every load is in bounds and none sits in a branch,
+  // and rows of chunks that turn out to be empty (never written by the split
   // kernel) are discarded, before any use, once seq_lens has arrived.
-  float m = -INFINITY, L = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float2 mv[U];
   float4 ov[U];
   auto load_round = [&](int base) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = min(base + u * SLOTS + slot, a.n_splits - 1);
-      mv[u] = ml[i * ps];
-      ov[u] = *reinterpret_cast<const float4*>(o + i * ps * D + 4 * q);
-    }
-  };
-  auto merge_round = [&](int base, int n_active) {
-    bool act[U];
-    float mn = m;
+    for (int u = 0; u < U; ++u) mv[u] = ml[min(base + u * SLOTS + slot, a.n_splits - 1) * ps];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      act[u] = base + u * SLOTS + slot < n_active;
-      if (act[u]) mn = fmaxf(mn, mv[u].x);
-    }
-    const float f0 = rescale(m, mn);
-    acc.x *= f0; acc.y *= f0; acc.z *= f0; acc.w *= f0;
-    L *= f0;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (act[u]) {
-        const float f = rescale(mv[u].x, mn);     // a causal column can have empty chunks
-        acc.x += f * ov[u].x;
-        acc.y += f * ov[u].y;
-        acc.z += f * ov[u].z;
-        acc.w += f * ov[u].w;
-        L += f * mv[u].y;
-      }
-    }
-    m = mn;
+    for (int u = 0; u < U; ++u)
+      ov[u] = *reinterpret_cast<const float4*>(o + min(base + u * SLOTS + slot, a.n_splits - 1) * ps * D);
   };
   load_round(0);
   __builtin_amdgcn_sched_barrier(0);           // keep the first loads ahead of the seq_lens wait
   int c, n_active = a.n_splits;
   if (a.seq_lens) chunking(a.seq_lens[b], a.n_splits, a.min_chunk, c, n_active);
-  merge_round(0, n_active);
-  for (int base = SLOTS * U; base < n_active; base += SLOTS * U) {
+
+  // M = max over the row's chunks (a causal column can hold empty chunks, m = -inf).
+  __shared__ float s_max[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (u * SLOTS + slot < n_active) mx = fmaxf(mx, mv[u].x);
+  for (int i = R + tid; i < n_active; i += 256) mx = fmaxf(mx, ml[i * ps].x);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((tid & 63) == 0) s_max[wave] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.f;
+  auto accumulate = [&](int base) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (base + u * SLOTS + slot < n_active) {
+        const float w = rescale(mv[u].x, M);
+        acc.x += w * ov[u].x;
+        acc.y += w * ov[u].y;
+        acc.z += w * ov[u].z;
+        acc.w += w * ov[u].w;
+        L += w * mv[u].y;
+      }
+    }
+  };
+  accumulate(0);
+  for (int base = R; base < n_active; base += R) {
     load_round(base);
-    merge_round(base, n_active);
+    accumulate(base);
   }
 
-  __shared__ float sm[SLOTS], sl[SLOTS];
-  __shared__ float4 sacc[SLOTS][LPS];
-  sacc[slot][q] = acc;
-  if (q == 0) {
-    sm[slot] = m;
-    sl[slot] = L;
+  // Sum over the 8 slots of each wave (lane bits 3..5), then over the 4 waves.
+#pragma unroll
+  for (int off = 8; off < 64; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off);
+    acc.y += __shfl_xor(acc.y, off);
+    acc.z += __shfl_xor(acc.z, off);
+    acc.w += __shfl_xor(acc.w, off);
+    L += __shfl_xor(L, off);
   }
+  __shared__ float4 s_acc[4][LPS];
+  __shared__ float s_l[4];
+  if ((tid & 63) < LPS) s_acc[wave][q] = acc;
+  if ((tid & 63) == 0) s_l[wave] = L;
   __syncthreads();
   if (tid < LPS) {
-    float M = sm[0];
+    float4 r = s_acc[0][tid];
 #pragma unroll
-    for (int k = 1; k < SLOTS; ++k) M = fmaxf(M, sm[k]);
-    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-    float Lt = 0.f;
-#pragma unroll
-    for (int k = 0; k < SLOTS; ++k) {
-      const float f = rescale(sm[k], M);
-      const float4 y = sacc[k][tid];
-      r.x += f * y.x;
-      r.y += f * y.y;
-      r.z += f * y.z;
-      r.w += f * y.w;
-      Lt += f * sl[k];
+    for (int w = 1; w < 4; ++w) {
+      const float4 y = s_acc[w][tid];
+      r.x += y.x;
+      r.y += y.y;
+      r.z += y.z;
+      r.w += y.w;
     }
+    const float Lt = (s_l[0] + s_l[1]) + (s_l[2] + s_l[3]);
     if (a.tri_ml) {                          // merged triplet, relative to M
-      if (tid == 0) a.tri_ml[bh] = make_float2(M, Lt);
-      *reinterpret_cast<float4*>(a.tri_o + (int64_t)bh * D + 4 * tid) = r;
+      if (tid == 0 && blockIdx.y == 0) a.tri_ml[bh] = make_float2(M, Lt);
+      *reinterpret_cast<float4*>(a.tri_o + (int64_t)bh * D + d0 + 4 * tid) = r;
     } else {
       // Lt = 0 only when nothing was attended (empty sequence): out = 0.
       const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
-      TO* out = static_cast<TO*>(a.out) + (int64_t)bh * D;
+      TO* out = static_cast<TO*>(a.out) + (int64_t)bh * D + d0;
       store4<TO>(out + 4 * tid, make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv));
     }
   }

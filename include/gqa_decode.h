@@ -225,8 +225,10 @@ int gqa_decode_merge(const int32_t* seq_lens, const void* workspace, size_t work
 
 /*
  * Split count the library uses when n_splits <= 0: enough workgroups that
- * every compute unit has work at B = 1, no more chunks than the longest
- * sequence can fill (when s_kv_max > 0 is known), at most GQA_MAX_SPLITS.
+ * every compute unit has work at B = 1; when s_kv_max > 0 is known, also
+ * enough that the longest sequence's chunks fill about two rounds of the
+ * resident workgroup slots (B = 1) or four (B > 1, where lengths may differ),
+ * with chunks of 128 to 4096 tokens; at most GQA_MAX_SPLITS.
  * num_cus <= 0 queries the current device (returns a negative status if that
  * fails). Pure host arithmetic otherwise.
  */

@@ -139,7 +139,13 @@ def test_split_heuristic_contract(gqa, B, h_kv, S):
 def test_split_heuristic_values(gqa):
     # 70B GQA at B = 1: 8 kv heads x 64 chunks = 512 workgroups of 128 tokens at 8k
     assert gqa.gqa_decode_pick_splits(1, 8, 8192, 256) == 64
+    # one sequence: two rounds of the 512 resident slots (chunks of 256 to 1024 tokens)
+    assert gqa.gqa_decode_pick_splits(1, 8, 32768, 256) == 128
+    assert gqa.gqa_decode_pick_splits(1, 8, 131072, 256) == 128
+    # chunks of at most 4096 tokens
     assert gqa.gqa_decode_pick_splits(1, 8, 1 << 20, 256) == 256
+    assert gqa.gqa_decode_pick_splits(1, 8, 1 << 22, 256) == 1024
+    # several sequences: the longest over four rounds
     assert gqa.gqa_decode_pick_splits(8, 8, 32768, 256) == 32
 
 
