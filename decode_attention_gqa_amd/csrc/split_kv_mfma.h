@@ -53,29 +53,43 @@ __device__ __forceinline__ int slot_token(int grp, int j) {
   return (j < 4) ? (4 * grp + j) : (16 + 4 * grp + (j - 4));
 }
 
+// Byte offsets, from the first K (or V) row of a block, of the 16-byte
+// pieces a lane loads: K row of token 16x + n at dims 8*grp (+32*kk through
+// the instruction's immediate offset), V row of token slot_token(grp, j) at
+// dims NT*n. Tokens at or past nv (a chunk's last, partial block) are clamped
+// to nv - 1: read again, and masked out of the softmax.
 template <int D>
-__device__ __forceinline__ void load_block(KVRegs<D>& r, const __bf16* kblk, const __bf16* vblk,
-                                           int64_t rs, int grp, int n, int nv) {
-  constexpr int KS = MfmaTile<D>::KS, NT = MfmaTile<D>::NT, VW = MfmaTile<D>::VW;
-  const bool tail = nv < 32;
+struct LaneOffsets {
+  uint32_t k[2];
+  uint32_t v[8];
+};
+
+template <int D>
+__device__ __forceinline__ LaneOffsets<D> lane_offsets(uint32_t row_bytes, int grp, int n, int nv) {
+  constexpr int NT = MfmaTile<D>::NT;
+  LaneOffsets<D> o;
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    int t = 16 * x + n;
-    if (tail) t = min(t, nv - 1);     // clamped rows are read but masked out of the softmax
-    const __bf16* row = kblk + (int64_t)t * rs + 8 * grp;
+  for (int x = 0; x < 2; ++x) o.k[x] = (uint32_t)min(16 * x + n, nv - 1) * row_bytes + 16u * grp;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) r.k[x][kk] = load_stream16(row + 32 * kk);
-  }
+  for (int j = 0; j < 8; ++j) o.v[j] = (uint32_t)min(slot_token(grp, j), nv - 1) * row_bytes + 2u * NT * n;
+  return o;
+}
+
+template <int D>
+__device__ __forceinline__ void load_block(KVRegs<D>& r, const char* kb, const char* vb,
+                                           const LaneOffsets<D>& o) {
+  constexpr int KS = MfmaTile<D>::KS, VW = MfmaTile<D>::VW;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) r.k[x][kk] = load_stream16(kb + o.k[x] + 64 * kk);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    int t = slot_token(grp, j);
-    if (tail) t = min(t, nv - 1);
-    const __bf16* row = vblk + (int64_t)t * rs + NT * n;
     if constexpr (VW == 4) {
-      const uint4 u = load_stream16(row);
+      const uint4 u = load_stream16(vb + o.v[j]);
       r.v[j][0] = u.x; r.v[j][1] = u.y; r.v[j][2] = u.z; r.v[j][3] = u.w;
     } else {
-      const uint2 u = load_stream8(row);
+      const uint2 u = load_stream8(vb + o.v[j]);
       r.v[j][0] = u.x; r.v[j][1] = u.y;
     }
   }
@@ -84,14 +98,15 @@ __device__ __forceinline__ void load_block(KVRegs<D>& r, const __bf16* kblk, con
 // A operand of output tile nt: dimension NT*(lane%16) + nt of the 8 slot tokens.
 template <int D>
 __device__ __forceinline__ bf16x8 v_tile(const KVRegs<D>& r, int nt) {
+  // Even nt: the low 16-bit halves of slots 2i, 2i+1; odd nt: the high
+  // halves. One byte permute each (selector bytes 0-3 pick from the second
+  // operand, 4-7 from the first).
   const int w = nt >> 1;
+  const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;
   uint4 a;
   uint32_t* pa = reinterpret_cast<uint32_t*>(&a);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t x = r.v[2 * i][w], y = r.v[2 * i + 1][w];
-    pa[i] = (nt & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
-  }
+  for (int i = 0; i < 4; ++i) pa[i] = __builtin_amdgcn_perm(r.v[2 * i + 1][w], r.v[2 * i][w], sel);
   return __builtin_bit_cast(bf16x8, a);
 }
 
@@ -132,6 +147,7 @@ __device__ __forceinline__ void compute_block(const KVRegs<D>& r, const bf16x8 (
   // causal column before its first position); keep alpha and p at 0 then.
   const float mref = (mn == -INFINITY) ? 0.f : mn;
   const float alpha = fast_exp2(st.m - mref);  // 0 on the first block (m = -inf)
+  const bool grew = mn > st.m;
   st.m = mn;
   float p[8], ls = 0.f;
 #pragma unroll
@@ -140,8 +156,13 @@ __device__ __forceinline__ void compute_block(const KVRegs<D>& r, const bf16x8 (
     ls += p[j];
   }
   st.l = st.l * alpha + ls;
+  // alpha is exactly 1 in every lane whose max did not grow: the rescale of
+  // the accumulators is skipped unless some lane's max grew (rare after the
+  // first blocks). A lane whose state was empty has acc = 0 either way.
+  if (__builtin_amdgcn_ballot_w64(grew)) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
+    for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
+  }
   bf16x8 ph, pl;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -158,13 +179,14 @@ __device__ __forceinline__ void compute_block(const KVRegs<D>& r, const bf16x8 (
 }
 
 template <int D, int NREP>
-__global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void split_kv_mfma(SplitArgs a) {
   constexpr int KS = MfmaTile<D>::KS, NT = MfmaTile<D>::NT;
   static_assert(NREP >= 1 && NREP <= 16, "one 16-wide MFMA tile holds the query heads of a group");
   const WgCoord wc = wg_coord();
   const int s = wc.s, g = wc.g;
   const int b = wc.b / a.qtiles, tile = wc.b - b * a.qtiles;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int grp = lane >> 4, n = lane & 15;
   // Column n of the 16-wide tile: query token qi, head g*NREP + hh.
   const int ti = n / NREP, hh = n % NREP;
@@ -175,6 +197,11 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
   int S;
   int64_t off;
   seq_info(a.seq_lens, a.kv_off, b, lane, S, off);
+  // Every lane holds the same S and off; saying so keeps the block base
+  // addresses in scalar registers (loads then add only a 32-bit lane offset).
+  S = __builtin_amdgcn_readfirstlane(S);
+  off = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(off >> 32)) << 32) |
+                  (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)off));
   int c, n_active;
   chunking(S, a.n_splits, a.min_chunk, c, n_active);
   if (s >= n_active) {                             // the merge reads chunks < n_active only
@@ -210,24 +237,39 @@ __global__ __launch_bounds__(kThreads) void split_kv_mfma(SplitArgs a) {
   SoftmaxState st{-INFINITY, 0.f};
 
   const int nblk = (ntok >> 5) + ((ntok & 31) != 0);
-  int blk = w;
-  if (blk < nblk) {
-    KVRegs<D> cur, nxt;
-    int nv = min(32, ntok - blk * 32);
-    load_block<D>(cur, kbase + (int64_t)blk * 32 * rs, vbase + (int64_t)blk * 32 * rs, rs, grp, n, nv);
+  if (w < nblk) {
+    const uint32_t row_bytes = (uint32_t)(rs * 2);   // <= 65535 * 256 < 2^24: 32 rows fit 32 bits
+    const char* kb0 = reinterpret_cast<const char*>(kbase);
+    const char* vb0 = reinterpret_cast<const char*>(vbase);
+    const LaneOffsets<D> full = lane_offsets<D>(row_bytes, grp, n, 32);
+    auto load = [&](KVRegs<D>& r, int bk) {
+      const int64_t base = (int64_t)bk * 32 * row_bytes;
+      const int nvb = min(32, ntok - bk * 32);
+      if (nvb == 32)
+        load_block<D>(r, kb0 + base, vb0 + base, full);
+      else
+        load_block<D>(r, kb0 + base, vb0 + base, lane_offsets<D>(row_bytes, grp, n, nvb));
+    };
+    auto step = [&](const KVRegs<D>& r, int bk) {
+      const int nv = min(32, ntok - bk * 32);
+      const int nvl = causal ? min(nv, lim - ((int)t0 + bk * 32) + 1) : nv;
+      compute_block<D>(r, qop, acc, st, a.scale_log2, grp, nv < 32 || causal, nvl);
+    };
+    // Two register buffers in turn: the next block of this wave is in flight
+    // while the current one is computed.
+    KVRegs<D> ra, rb;
+    int blk = w;
+    load(ra, blk);
     while (true) {
-      const int nb = blk + kWaves;
-      const bool more = nb < nblk;
-      int nvn = 0;
-      if (more) {                                  // prefetch the next block before computing
-        nvn = min(32, ntok - nb * 32);
-        load_block<D>(nxt, kbase + (int64_t)nb * 32 * rs, vbase + (int64_t)nb * 32 * rs, rs, grp, n, nvn);
-      }
-      const int nvl = causal ? min(nv, lim - ((int)t0 + blk * 32) + 1) : nv;
-      compute_block<D>(cur, qop, acc, st, a.scale_log2, grp, nv < 32 || causal, nvl);
-      if (!more) break;
-      cur = nxt;
-      nv = nvn;
+      int nb = blk + kWaves;
+      if (nb < nblk) load(rb, nb);
+      step(ra, blk);
+      if (nb >= nblk) break;
+      blk = nb;
+      nb = blk + kWaves;
+      if (nb < nblk) load(ra, nb);
+      step(rb, blk);
+      if (nb >= nblk) break;
       blk = nb;
     }
   }
