@@ -85,11 +85,22 @@ def test_fp32_inputs(n_rep, d):
     report(f"fp32 n_rep={n_rep} d={d}", max_err(got, ref_of(inp)), ns, TOL_F32)
 
 
-@pytest.mark.parametrize("ns", [1, 2, 7, 64, 300, 0])
+# The merge takes up to 32 * U chunks per load round, U = 1, 2, 4, 8 by split
+# count: 1..32, 33..64, 65..128, 129..256; 300 and 600 take 2 and 3 rounds
+# (600 chunks of 14 tokens over 8192: only 586 are non-empty).
+@pytest.mark.parametrize("ns", [1, 2, 7, 64, 100, 200, 300, 600, 0])
 def test_split_counts_agree(ns):
     inp = workloads.make_inputs("llama70b_gqa_b1_s8192")
     got, used = run_gpu(inp, n_splits=ns)
     report(f"70B S=8192 ns={ns}", max_err(got, ref_of(inp)), used, TOL_F32)
+
+
+@pytest.mark.parametrize("ns", [33, 129, 300])
+def test_split_counts_d64(ns):
+    """d = 64: two 32-column slices per merged row; several load rounds."""
+    inp = workloads.custom("d64", B=2, h_q=16, h_kv=4, d=64, seq_lens=[5000, 2100], seed=61)
+    got, used = run_gpu(inp, n_splits=ns)
+    report(f"d=64 ns={ns}", max_err(got, ref_of(inp)), used, TOL_F32)
 
 
 def test_empty_short_and_block_edge_sequences():
