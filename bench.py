@@ -139,8 +139,10 @@ def traffic_from_profile(name: str, src_hash: str):
 
 def bench_append_or_step(args) -> int:
     """KV-cache append (gqa_kv_append) alone, or a decode step: append one
-    token per sequence, then attend with the new lengths. Padded caches with
-    capacity S_max + n_new rows per sequence, R copies rotated as above."""
+    token per sequence, then attend with the new lengths - as two calls
+    (`step`) or as one gqa_decode_step with the append folded into the split
+    kernel (`step1`). Padded caches with capacity S_max + n_new rows per
+    sequence, R copies rotated as above."""
     import numpy as np
     import torch
 
@@ -152,6 +154,7 @@ def bench_append_or_step(args) -> int:
         raise SystemExit("--op append/step use the bf16 workloads")
     lens0 = workloads.seq_lens_for(w)
     n_new = args.n_new if args.op == "append" else 1
+    is_step = args.op in ("step", "step1")
     cap = int(lens0.max()) + n_new
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -178,6 +181,10 @@ def bench_append_or_step(args) -> int:
         k, v = caches[i % R]
         # every step appends at the same positions (lens_in is not advanced), so
         # the timed work is the same in every step
+        if args.op == "step1":
+            gqa.gqa_decode_step(q, kn, vn, k, v, lens_in, lens_out, out, capacity=cap, kv_token_offsets=offs,
+                                workspace=ws)
+            return
         gqa.gqa_kv_append(kn, vn, k, v, lens_in, capacity=cap, seq_lens_out=lens_out, kv_token_offsets=offs)
         if args.op == "step":
             gqa.gqa_decode_attn_ex(q, k, v, lens_out, out, kv_token_offsets=offs, s_kv_hint=cap, workspace=ws)
@@ -201,10 +208,10 @@ def bench_append_or_step(args) -> int:
     appended = 2 * w.B * n_new * w.h_kv * w.d * 2          # bytes written (and read from k_new/v_new)
     attended = 2 * int((lens0.astype(np.int64) + 1).sum()) * w.h_kv * w.d * 2
     res = {
-        "metric": "decode step (KV append + attention) us" if args.op == "step" else "KV-cache append bytes/s",
-        "value": round(sec * 1e6, 3) if args.op == "step" else round(2 * appended / sec / 1e9, 3),
-        "unit": "us" if args.op == "step" else "GB/s (read + write)",
-        "higher_is_better": args.op != "step",
+        "metric": "decode step (KV append + attention) us" if is_step else "KV-cache append bytes/s",
+        "value": round(sec * 1e6, 3) if is_step else round(2 * appended / sec / 1e9, 3),
+        "unit": "us" if is_step else "GB/s (read + write)",
+        "higher_is_better": not is_step,
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": sec * 1e3,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "op": args.op, "B": w.B, "h_kv": w.h_kv, "d_head": w.d,
@@ -213,7 +220,8 @@ def bench_append_or_step(args) -> int:
         "us_per_call": sec * 1e6,
         "append_bytes_written": appended,
     }
-    if args.op == "step":
+    if is_step:
+        res["launches_per_step"] = 2 if args.op == "step1" else 3
         res["attended_kv_bytes"] = attended
         res["effective_kv_gbs"] = attended / sec / 1e9
     print(json.dumps(res), flush=True)
@@ -233,9 +241,10 @@ def main() -> int:
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of a HIP graph")
     ap.add_argument("--s-q", type=int, default=1,
                     help="query tokens per sequence (> 1: multi-token decode, causal among them)")
-    ap.add_argument("--op", choices=["attend", "append", "step"], default="attend",
+    ap.add_argument("--op", choices=["attend", "append", "step", "step1"], default="attend",
                     help="attend (default): the attention call; append: KV-cache append of "
-                         "--n-new tokens per sequence; step: append one token, then attend")
+                         "--n-new tokens per sequence; step: append one token, then attend (two "
+                         "calls); step1: the same as one gqa_decode_step")
     ap.add_argument("--n-new", type=int, default=1, help="tokens per sequence for --op append")
     ap.add_argument("--fused", action="store_true",
                     help="single-launch form (GQA_FLAG_FUSED) instead of split + merge kernels")

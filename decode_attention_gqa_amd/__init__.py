@@ -17,7 +17,7 @@ import os
 
 __all__ = [
     "gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_attn_multi", "gqa_decode_partial",
-    "gqa_decode_merge", "gqa_kv_append", "gqa_decode_attn_triplet", "gqa_merge_triplets",
+    "gqa_decode_merge", "gqa_kv_append", "gqa_decode_step", "gqa_decode_attn_triplet", "gqa_merge_triplets",
     "GQA_MAX_QUERY_TOKENS",
     "gqa_decode_pick_splits",
     "gqa_decode_workspace_bytes", "gqa_status_string", "GQAError", "lib", "LIB_PATH",
@@ -70,6 +70,9 @@ lib.gqa_merge_triplets.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp]
 lib.gqa_merge_triplets.restype = _i32
 lib.gqa_kv_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _vp]
 lib.gqa_kv_append.restype = _i32
+lib.gqa_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32,
+                                _i32, _i32, _i64, _vp, _sz, _vp]
+lib.gqa_decode_step.restype = _i32
 lib.gqa_decode_partial.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i64,
                                    _vp, _sz, _vp, _i32]
 lib.gqa_decode_partial.restype = _i32
@@ -323,6 +326,48 @@ def gqa_kv_append(k_new, v_new, k_cache, v_cache, seq_lens, *, capacity, seq_len
                               ctypes.c_void_p(st.cuda_stream))
     if r != GQA_OK:
         raise GQAError(r, "gqa_kv_append")
+
+
+def gqa_decode_step(q, k_new, v_new, k_cache, v_cache, seq_lens, seq_lens_out, out=None, *, capacity,
+                    scale=None, n_splits=0, out_dtype=None, kv_token_offsets=None, workspace=None, stream=None):
+    """One decode step: append each sequence's new token (k_new / v_new
+    [B, h_kv, d] or [B, 1, h_kv, d] bf16) to the padded cache at position
+    seq_lens[b] (dropped at capacity), write min(seq_lens + 1, capacity) to
+    seq_lens_out, and attend q [B, h_q, d] over the grown sequences.
+    Returns out [B, h_q, d] (fp32 unless out_dtype=torch.bfloat16)."""
+    torch = _torch()
+    B, h_q, d = q.shape
+    h_kv = k_cache.shape[1]
+    _check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets)
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("seq_lens_out", seq_lens_out)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if k_new.numel() != B * h_kv * d or v_new.shape != k_new.shape or k_new.dtype != q.dtype \
+            or v_new.dtype != q.dtype:
+        raise ValueError("k_new / v_new must be [B, h_kv, d_head] (or [B, 1, h_kv, d_head]) of q's dtype")
+    if seq_lens_out.dtype != torch.int32 or seq_lens_out.shape != (B,):
+        raise ValueError("seq_lens_out must be int32 [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((B, h_q, d), dtype=out_dtype, device=q.device)
+    elif out.shape != (B, h_q, d) or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, h_q, d_head] tensor of out_dtype")
+    with torch.cuda.device(q.device):
+        st = stream if stream is not None else torch.cuda.current_stream(q.device)
+        r = lib.gqa_decode_step(
+            q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            seq_lens.data_ptr(), seq_lens_out.data_ptr(),
+            kv_token_offsets.data_ptr() if kv_token_offsets is not None else None,
+            out.data_ptr(), B, h_q, h_kv, d, float(scale), int(n_splits),
+            _dtype_code(q.dtype), _dtype_code(out_dtype), int(capacity),
+            workspace.data_ptr() if workspace is not None else None,
+            workspace.numel() * workspace.element_size() if workspace is not None else 0,
+            ctypes.c_void_p(st.cuda_stream))
+    if r != GQA_OK:
+        raise GQAError(r, "gqa_decode_step")
+    return out
 
 
 def gqa_decode_partial(q, k_cache, v_cache, seq_lens, workspace, *, scale=None, n_splits=0,

@@ -37,6 +37,11 @@ struct SplitArgs {
   int s_q;                    // query tokens per sequence (1: single-token decode)
   int tpt;                    // query tokens per 16-column tile: min(s_q, 16 / n_rep)
   int qtiles;                 // tiles per sequence: ceil(s_q / tpt); grid z = B * qtiles
+  // decode step with the new token appended on the way (APPEND kernels only)
+  const void* k_new;          // [B, h_kv, D] the new token's K and V rows
+  const void* v_new;
+  int32_t* lens_out;          // [B] lengths after the append: min(S_b + 1, capacity)
+  int capacity;               // token rows per sequence; rows start at kv_off[b] or b * capacity
 };
 
 struct MergeArgs {

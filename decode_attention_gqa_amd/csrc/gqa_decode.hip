@@ -130,6 +130,18 @@ hipError_t launch_split_nrep(int nrep, bool bf16, bool valu, dim3 grid, hipStrea
   }
 }
 
+template <int D>
+hipError_t launch_split_append(int nrep, dim3 grid, hipStream_t st, const gqa::SplitArgs& a) {
+  switch (nrep) {
+    case 1: hipLaunchKernelGGL((gqa::split_kv_mfma<D, 1, true>), grid, dim3(gqa::kThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((gqa::split_kv_mfma<D, 2, true>), grid, dim3(gqa::kThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((gqa::split_kv_mfma<D, 4, true>), grid, dim3(gqa::kThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((gqa::split_kv_mfma<D, 8, true>), grid, dim3(gqa::kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((gqa::split_kv_mfma<D, 16, true>), grid, dim3(gqa::kThreads), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
 template <int D, typename TO>
 hipError_t launch_merge_t(int rows, hipStream_t st, const gqa::MergeArgs& a) {
   // chunks per slot in the first round: one round covers up to 32 * U chunks
@@ -464,6 +476,45 @@ int gqa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_c
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "append kernel launch: %s", hipGetErrorString(e));
   return GQA_OK;
+}
+
+int gqa_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                    const int32_t* seq_lens, int32_t* seq_lens_out, const int64_t* kv_token_offsets,
+                    void* out, int B, int h_q, int h_kv, int d_head, float scale, int n_splits,
+                    int in_dtype, int out_dtype, int64_t capacity, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  int st;
+  if (!out || !k_new || !v_new || !seq_lens_out) return fail(GQA_ERR_INVALID_ARG, "null pointer");
+  if ((st = check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets, scale, in_dtype, 0))) return st;
+  if (in_dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "gqa_decode_step takes bf16 (use gqa_kv_append + gqa_decode_attn_ex)");
+  if (capacity < 1 || capacity > INT32_MAX) return fail(GQA_ERR_INVALID_ARG, "capacity must be in [1, 2^31)");
+  if ((st = check_shape(B, h_q, h_kv, d_head, n_splits, capacity))) return st;
+  const size_t qo = (size_t)B * h_q * d_head;
+  if ((st = check_out(out, out_dtype, qo))) return st;
+  if (reinterpret_cast<uintptr_t>(k_new) % 16 || reinterpret_cast<uintptr_t>(v_new) % 16 ||
+      reinterpret_cast<uintptr_t>(seq_lens_out) % 4)
+    return fail(GQA_ERR_INVALID_ARG, "k_new / v_new / seq_lens_out misaligned");
+  const size_t out_el = out_dtype == GQA_DTYPE_BF16 ? 2 : 4, row = (size_t)B * h_kv * d_head * 2;
+  if (overlap(seq_lens_out, (size_t)B * 4, seq_lens, (size_t)B * 4))
+    return fail(GQA_ERR_INVALID_ARG, "seq_lens_out overlaps seq_lens");
+  if (overlap(out, qo * out_el, q, qo * 2) || overlap(out, qo * out_el, seq_lens, (size_t)B * 4) ||
+      overlap(out, qo * out_el, seq_lens_out, (size_t)B * 4) || overlap(out, qo * out_el, k_new, row) ||
+      overlap(out, qo * out_el, v_new, row) || out == k_cache || out == v_cache)
+    return fail(GQA_ERR_INVALID_ARG, "out overlaps an input");
+  Plan pl;
+  if ((st = make_plan(B, h_q, h_kv, d_head, n_splits, capacity, workspace, workspace_bytes, true, &pl)))
+    return st;
+  gqa::SplitArgs sa{q, k_cache, v_cache, seq_lens, kv_token_offsets, pl.ws_o, pl.ws_ml,
+                    h_q, h_kv, pl.ns, pl.min_chunk, scale * gqa::kLog2e,
+                    0, 0, nullptr, pl.counters, 0ull, 1, 1, 1,
+                    k_new, v_new, seq_lens_out, (int)capacity};
+  const dim3 grid = gqa::split_grid(pl.ns, h_kv, B);
+  const int nrep = h_q / h_kv;
+  hipError_t e = d_head == 128 ? launch_split_append<128>(nrep, grid, stream, sa)
+                               : launch_split_append<64>(nrep, grid, stream, sa);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
+  return run_merge(pl, seq_lens_out, out, B, h_q, d_head, out_dtype, stream);
 }
 
 int gqa_decode_attn_triplet(const void* q, const void* k_cache, const void* v_cache,

@@ -95,6 +95,35 @@ __device__ __forceinline__ void load_block(KVRegs<D>& r, const char* kb, const c
   }
 }
 
+// The block that holds a decode step's new token (its last valid token,
+// nv - 1): lanes whose (clamped) token is nv - 1 read the caller's new K/V
+// row instead of the cache; the others read the cache as in load_block.
+template <int D>
+__device__ __forceinline__ void load_block_new(KVRegs<D>& r, const char* kb, const char* vb,
+                                               uint32_t row_bytes, int grp, int n, int nv,
+                                               const char* k_row, const char* v_row) {
+  constexpr int KS = MfmaTile<D>::KS, NT = MfmaTile<D>::NT, VW = MfmaTile<D>::VW;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int t = min(16 * x + n, nv - 1);
+    const char* row = (t == nv - 1) ? k_row : kb + (uint32_t)t * row_bytes;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) r.k[x][kk] = load_stream16(row + 16 * grp + 64 * kk);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int t = min(slot_token(grp, j), nv - 1);
+    const char* row = ((t == nv - 1) ? v_row : vb + (uint32_t)t * row_bytes) + 2 * NT * n;
+    if constexpr (VW == 4) {
+      const uint4 u = load_stream16(row);
+      r.v[j][0] = u.x; r.v[j][1] = u.y; r.v[j][2] = u.z; r.v[j][3] = u.w;
+    } else {
+      const uint2 u = load_stream8(row);
+      r.v[j][0] = u.x; r.v[j][1] = u.y;
+    }
+  }
+}
+
 // A operand of output tile nt: dimension NT*(lane%16) + nt of the 8 slot tokens.
 template <int D>
 __device__ __forceinline__ bf16x8 v_tile(const KVRegs<D>& r, int nt) {
@@ -178,7 +207,12 @@ __device__ __forceinline__ void compute_block(const KVRegs<D>& r, const bf16x8 (
   }
 }
 
-template <int D, int NREP>
+// APPEND: one decode step with the new token appended on the way (single
+// query token; padded cache). The sequence is S = min(S_b + 1, capacity)
+// tokens long; when S_b < capacity its last token is the new one, read from
+// k_new / v_new by the workgroup whose chunk holds it, which also copies that
+// row into the cache (no other workgroup reads it), and lens_out[b] = S.
+template <int D, int NREP, bool APPEND = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void split_kv_mfma(SplitArgs a) {
   constexpr int KS = MfmaTile<D>::KS, NT = MfmaTile<D>::NT;
   static_assert(NREP >= 1 && NREP <= 16, "one 16-wide MFMA tile holds the query heads of a group");
@@ -196,7 +230,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   int S;
   int64_t off;
-  seq_info(a.seq_lens, a.kv_off, b, lane, S, off);
+  bool appended = false;                           // APPEND: the new token is position S - 1
+  if constexpr (APPEND) {
+    const int old = a.seq_lens[b];
+    off = a.kv_off ? a.kv_off[b] : (int64_t)b * a.capacity;
+    appended = old < a.capacity;                   // else the new row is dropped
+    S = appended ? old + 1 : a.capacity;
+    if (a.lens_out && s == 0 && g == 0 && tid == 0) a.lens_out[b] = S;
+  } else {
+    seq_info(a.seq_lens, a.kv_off, b, lane, S, off);
+  }
   // Every lane holds the same S and off; saying so keeps the block base
   // addresses in scalar registers (loads then add only a 32-bit lane offset).
   S = __builtin_amdgcn_readfirstlane(S);
@@ -236,16 +279,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   SoftmaxState st{-INFINITY, 0.f};
 
+  // APPEND: the workgroup whose chunk ends the sequence also copies the new
+  // token's K and V rows of head g into the cache: 16-byte pieces loaded
+  // before the block loop and stored after it (a store inside the loop would
+  // make every wait in it drain the prefetched block too).
+  const int64_t src_new = ((int64_t)b * a.h_kv + g) * D * 2;            // row in k_new / v_new (bytes)
+  const int64_t row_new = ((off + S - 1) * a.h_kv + g) * D * 2;         // its cache row (bytes)
+  constexpr int U16 = D * 2 / 16;                                       // 16-byte pieces per row
+  const bool copier = APPEND && appended && s == n_active - 1 && tid < 2 * U16;
+  uint4 piece = make_uint4(0u, 0u, 0u, 0u);
+  if (copier)
+    piece = *reinterpret_cast<const uint4*>(static_cast<const char*>(tid < U16 ? a.k_new : a.v_new) + src_new +
+                                            16 * (tid % U16));
+
   const int nblk = (ntok >> 5) + ((ntok & 31) != 0);
   if (w < nblk) {
     const uint32_t row_bytes = (uint32_t)(rs * 2);   // <= 65535 * 256 < 2^24: 32 rows fit 32 bits
     const char* kb0 = reinterpret_cast<const char*>(kbase);
     const char* vb0 = reinterpret_cast<const char*>(vbase);
     const LaneOffsets<D> full = lane_offsets<D>(row_bytes, grp, n, 32);
+    // APPEND: the block whose last token ends the sequence holds the new token.
+    auto holds_new = [&](int bk, int nvb) { return APPEND && appended && t0 + bk * 32 + nvb == S; };
     auto load = [&](KVRegs<D>& r, int bk) {
       const int64_t base = (int64_t)bk * 32 * row_bytes;
       const int nvb = min(32, ntok - bk * 32);
-      if (nvb == 32)
+      if (holds_new(bk, nvb))
+        load_block_new<D>(r, kb0 + base, vb0 + base, row_bytes, grp, n, nvb,
+                          static_cast<const char*>(a.k_new) + src_new, static_cast<const char*>(a.v_new) + src_new);
+      else if (nvb == 32)
         load_block<D>(r, kb0 + base, vb0 + base, full);
       else
         load_block<D>(r, kb0 + base, vb0 + base, lane_offsets<D>(row_bytes, grp, n, nvb));
@@ -273,6 +334,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       blk = nb;
     }
   }
+
+  if (copier)
+    *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(tid < U16 ? a.k : a.v)) + row_new +
+                              16 * (tid % U16)) = piece;
 
   // l: sum the 4 lane groups' partial sums (m is already shared by them).
   st.l += __shfl_xor(st.l, 16);

@@ -165,6 +165,36 @@ int gqa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_c
                   hipStream_t stream);
 
 /*
+ * One decode step in two launches instead of three: gqa_kv_append of one new
+ * token per sequence (the tt-metal burndown's update_cache, the step before
+ * attention) followed by gqa_decode_attn_ex on the new lengths, with the
+ * append folded into the split kernel.
+ *   k_new, v_new  [B, h_kv, d_head] bf16 device: the new token's K and V rows.
+ *   k_cache, v_cache  padded cache [T, h_kv, d_head] bf16 (written: row
+ *                 off_b + seq_lens[b] receives the new token when
+ *                 seq_lens[b] < capacity; otherwise the token is dropped).
+ *   seq_lens      [B] int32 device, lengths before the step (read only).
+ *   seq_lens_out  [B] int32 device, required, must not overlap seq_lens:
+ *                 receives min(seq_lens[b] + 1, capacity), the lengths the
+ *                 attention used.
+ *   kv_token_offsets  [B] int64 device first row of each sequence, or NULL
+ *                 for b * capacity.
+ *   out           [B, h_q, d_head] fp32 or bf16 (out_dtype).
+ * Same result, bit for bit, as gqa_kv_append followed by gqa_decode_attn_ex
+ * with explicit offsets (b * capacity when NULL here), s_kv_hint = capacity
+ * and the same n_splits. The split count defaults to gqa_decode_pick_splits(B, h_kv,
+ * capacity, 0), the workspace to gqa_decode_workspace_bytes for it (NULL:
+ * library-owned). bf16 only (GQA_ERR_UNSUPPORTED otherwise). Asynchronous on
+ * `stream`; no host synchronisation, allocation (given a workspace) or memset,
+ * so a graph of one step can be replayed while the lengths grow.
+ */
+int gqa_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                    const int32_t* seq_lens, int32_t* seq_lens_out, const int64_t* kv_token_offsets,
+                    void* out, int B, int h_q, int h_kv, int d_head, float scale, int n_splits,
+                    int in_dtype, int out_dtype, int64_t capacity, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/*
  * Sequence-sharded attention (the kernbench2 page's scheme: every shard
  * holds a slice of each sequence's KV and all of q; shards exchange (m, l, o)
  * triplets and merge them exactly).

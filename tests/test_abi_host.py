@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_attn_multi", "gqa_decode_partial",
-                            "gqa_decode_merge", "gqa_kv_append", "gqa_decode_attn_triplet",
+                            "gqa_decode_merge", "gqa_kv_append", "gqa_decode_step", "gqa_decode_attn_triplet",
                             "gqa_merge_triplets", "gqa_decode_pick_splits",
                             "gqa_decode_workspace_bytes", "gqa_status_string", "gqa_last_error",
                             "gqa_decode_set_split_events"])
@@ -201,6 +201,23 @@ def test_kv_append_checks_on_the_host(gqa):
     assert f(dt=5) == -2
     assert f(lo=L) == -1                       # lengths out overlaps lengths in
     assert f(kn=Q + 4) == -1
+
+
+def test_decode_step_checks_on_the_host(gqa):
+    # k_new, v_new at W and W + 0x4000 (B * h_kv * d * 2 = 4 KiB each); lengths out at W + 0x8000
+    f = lambda **kw: gqa.lib.gqa_decode_step(
+        Q, kw.get("kn", W), W + 0x4000, K, V, L, kw.get("lo", W + 0x8000), None, kw.get("out", O), 2, 64, 8,
+        kw.get("d", 128), 0.088, 0, kw.get("dt", 1), 0, kw.get("cap", 100), None, 0, None)
+    assert f(kn=None) == -1
+    assert f(lo=None) == -1                    # the new lengths are required
+    assert f(lo=L) == -1                       # and must not overlap the old ones
+    assert f(dt=0) == -2                       # bf16 only
+    assert f(cap=0) == -1
+    assert f(cap=1 << 31) == -1
+    assert f(d=96) == -2
+    assert f(kn=W + 4) == -1                   # misaligned
+    assert f(out=W) == -1                      # out overlaps k_new
+    assert f(out=Q) == -1                      # out overlaps q
 
 
 def test_sharded_entry_points_check_on_the_host(gqa):
