@@ -54,5 +54,28 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+C_SMOKE_SRC = os.path.join(ROOT, "tests", "c_abi", "gqa_c_smoke.c")
+C_SMOKE = os.path.join(ROOT, "tests", "c_abi", "gqa_c_smoke")
+
+
+def build_c_smoke(verbose: bool = False) -> str:
+    """Compile the plain-C user of the boundary (tests/c_abi/gqa_c_smoke.c)
+    against the built library and the HIP runtime, with gcc: no hipcc, no
+    Python, no PyTorch."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", INCLUDE, C_SMOKE_SRC,
+           "-L", PKG, "-lgqa_decode", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../decode_attention_gqa_amd", "-Wl,-rpath," + os.path.join(rocm, "lib"),
+           "-o", C_SMOKE]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("gcc failed:\n" + r.stdout + r.stderr)
+    return C_SMOKE
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_smoke(verbose=True))
