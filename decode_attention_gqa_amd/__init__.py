@@ -80,6 +80,8 @@ lib.gqa_decode_merge.argtypes = [_vp, _vp, _sz, _vp, _i32, _i32, _i32, _i32, _i3
 lib.gqa_decode_merge.restype = _i32
 lib.gqa_decode_pick_splits.argtypes = [_i32, _i32, _i64, _i32]
 lib.gqa_decode_pick_splits.restype = _i32
+lib.gqa_decode_multi_splits.argtypes = [_i32, _i32, _i32, _i32, _i64, _i32]
+lib.gqa_decode_multi_splits.restype = _i32
 lib.gqa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
 lib.gqa_decode_workspace_bytes.restype = _sz
 lib.gqa_status_string.argtypes = [_i32]
@@ -203,9 +205,10 @@ def multi_splits(B: int, S_q: int, h_q: int, h_kv: int, s_kv_hint: int = 0, n_sp
     """Split count gqa_decode_attn_multi uses (for sizing its workspace)."""
     if n_splits > 0:
         return n_splits
-    n_rep = h_q // h_kv
-    tpt = min(S_q, 16 // n_rep)
-    return gqa_decode_pick_splits(B * ((S_q + tpt - 1) // tpt), h_kv, s_kv_hint, 0)
+    r = lib.gqa_decode_multi_splits(B, S_q, h_q, h_kv, int(s_kv_hint), 0)
+    if r < 1:
+        raise GQAError(r, "gqa_decode_multi_splits")
+    return r
 
 
 def gqa_decode_attn_multi(q, k_cache, v_cache, seq_lens, out=None, *, scale=None, n_splits=0,

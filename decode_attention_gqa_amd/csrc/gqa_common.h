@@ -36,7 +36,8 @@ struct SplitArgs {
   // several query tokens per sequence (matrix-core kernel only)
   int s_q;                    // query tokens per sequence (1: single-token decode)
   int tpt;                    // query tokens per 16-column tile: min(s_q, 16 / n_rep)
-  int qtiles;                 // tiles per sequence: ceil(s_q / tpt); grid z = B * qtiles
+  int qtiles;                 // tiles per sequence: ceil(s_q / tpt)
+  int passes;                 // tile groups per sequence (qtiles / tiles per workgroup); grid z = B * passes
   // decode step with the new token appended on the way (APPEND kernels only)
   const void* k_new;          // [B, h_kv, D] the new token's K and V rows
   const void* v_new;

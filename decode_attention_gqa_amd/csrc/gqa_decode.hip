@@ -36,11 +36,23 @@ int fail(int status, const char* fmt, ...) {
 }
 
 // Heuristic constants (see gqa_decode_pick_splits).
-constexpr int kTargetWgPerCu = 2;    // resident split workgroups per CU the grid aims for
 constexpr int kMinChunk = 128;       // tokens: one 32-token block per wave of a workgroup
-constexpr int kRoundsOne = 2;        // B = 1: rounds of resident slots the workgroups fill
-constexpr int kRoundsMany = 4;       // B > 1: rounds the longest sequence is spread over
-constexpr int64_t kMaxChunk = 4096;  // tokens: longer chunks leave too few workgroups
+// How a split kernel wants its grid: resident workgroups per CU, rounds of
+// those slots the longest sequence's chunks fill (one sequence / a batch, where
+// only the longest length is known and more rounds keep it balanced), and the
+// longest chunk in tokens. Measured per kernel (70B shapes; see the sweeps in
+// the design notes).
+struct SplitPolicy {
+  int wg_per_cu;
+  int rounds_one, rounds_many;
+  int64_t max_chunk;
+};
+// One 16-column tile per workgroup, two workgroups per CU. A second round
+// hides each workgroup's start-up behind another's streaming.
+constexpr SplitPolicy kOneTile{2, 2, 4, 4096};
+// Two tiles per workgroup (multi-token decode), one workgroup per CU: one
+// round for a single sequence; chunks up to 16384 tokens.
+constexpr SplitPolicy kTwoTiles{1, 1, 4, 16384};
 
 // Library-owned fallback workspace, one grow-only buffer per device.
 std::mutex g_ws_mu;
@@ -112,6 +124,8 @@ hipError_t launch_split(bool bf16, bool valu, dim3 grid, hipStream_t st, const g
     hipLaunchKernelGGL((gqa::split_kv_valu<float, D, NREP>), grid, dim3(gqa::kThreads), 0, st, a);
   } else if (valu) {
     hipLaunchKernelGGL((gqa::split_kv_valu<__bf16, D, NREP>), grid, dim3(gqa::kThreads), 0, st, a);
+  } else if (a.qtiles > a.passes) {               // two column tiles per workgroup
+    hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, false, 2>), grid, dim3(gqa::kThreads), 0, st, a);
   } else {
     hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP>), grid, dim3(gqa::kThreads), 0, st, a);
   }
@@ -163,22 +177,28 @@ hipError_t launch_merge(bool out_bf16, int B, int h_q, hipStream_t st, const gqa
   return out_bf16 ? launch_merge_t<D, __bf16>((int)rows, st, a) : launch_merge_t<D, float>((int)rows, st, a);
 }
 
-int pick_splits_host(int B, int h_kv, int64_t s_kv_max, int num_cus) {
+// Query tokens per 16-column tile, tiles per sequence, tiles per workgroup
+// (two once a sequence needs two or more: each K/V block is then read once
+// for both) and workgroup passes per sequence over the KV range.
+void query_tiles(int s_q, int nrep, int* tpt, int* qtiles, int* tpw, int* passes) {
+  *tpt = s_q < 16 / nrep ? s_q : 16 / nrep;
+  *qtiles = (s_q + *tpt - 1) / *tpt;
+  *tpw = *qtiles >= 2 ? 2 : 1;
+  *passes = (*qtiles + *tpw - 1) / *tpw;
+}
+
+int pick_splits_host(int B, int passes, int h_kv, int64_t s_kv_max, int num_cus, const SplitPolicy& p) {
   // Enough workgroups to fill every CU at B = 1 ...
-  const int64_t units = (int64_t)B * h_kv;
-  const int64_t slots = (int64_t)kTargetWgPerCu * num_cus;
+  const int64_t units = (int64_t)B * passes * h_kv;
+  const int64_t slots = (int64_t)p.wg_per_cu * num_cus;
   int64_t n = (slots + units - 1) / units;
   if (s_kv_max > 0) {
     // ... and, when the longest sequence is known, chunks short enough that
-    // its workgroups are spread over a few rounds of the resident slots:
-    // two for a single sequence (every chunk is equally long, and a second
-    // round hides each workgroup's start-up behind another's streaming),
-    // four when there are several (only the longest length is known, so
-    // more rounds keep a ragged batch balanced); chunks stay within
-    // [kMinChunk, kMaxChunk] tokens.
-    const int64_t rounds = B == 1 ? kRoundsOne : kRoundsMany;
+    // its workgroups are spread over the policy's rounds of the resident
+    // slots; chunks stay within [kMinChunk, max_chunk] tokens.
+    const int64_t rounds = B == 1 ? p.rounds_one : p.rounds_many;
     int64_t chunk = (s_kv_max * units + rounds * slots - 1) / (rounds * slots);
-    if (chunk > kMaxChunk) chunk = kMaxChunk;
+    if (chunk > p.max_chunk) chunk = p.max_chunk;
     if (chunk < kMinChunk) chunk = kMinChunk;
     const int64_t by_len = (s_kv_max + chunk - 1) / chunk;
     if (by_len > n) n = by_len;
@@ -226,7 +246,20 @@ int gqa_decode_pick_splits(int B, int h_kv, int64_t s_kv_max, int num_cus) {
     int st = device_cus(&num_cus);
     if (st != GQA_OK) return st;
   }
-  return pick_splits_host(B, h_kv, s_kv_max, num_cus);
+  return pick_splits_host(B, 1, h_kv, s_kv_max, num_cus, kOneTile);
+}
+
+int gqa_decode_multi_splits(int B, int S_q, int h_q, int h_kv, int64_t s_kv_max, int num_cus) {
+  if (B < 1 || h_kv < 1 || h_q < h_kv || h_q % h_kv) return fail(GQA_ERR_INVALID_ARG, "bad B / h_q / h_kv");
+  if (S_q < 1 || S_q > GQA_MAX_QUERY_TOKENS)
+    return fail(GQA_ERR_INVALID_ARG, "S_q %d not in [1, %d]", S_q, GQA_MAX_QUERY_TOKENS);
+  if (num_cus <= 0) {
+    int st = device_cus(&num_cus);
+    if (st != GQA_OK) return st;
+  }
+  int tpt, qtiles, tpw, passes;
+  query_tiles(S_q, h_q / h_kv, &tpt, &qtiles, &tpw, &passes);
+  return pick_splits_host(B, passes, h_kv, s_kv_max, num_cus, tpw == 2 ? kTwoTiles : kOneTile);
 }
 
 }  // extern "C"
@@ -270,10 +303,6 @@ int check_out(const void* out, int out_dtype, size_t qo_elems) {
 }
 
 // Query tokens per 16-column tile and tiles per sequence for s_q query tokens.
-void query_tiles(int s_q, int nrep, int* tpt, int* qtiles) {
-  *tpt = s_q < 16 / nrep ? s_q : 16 / nrep;
-  *qtiles = (s_q + *tpt - 1) / *tpt;
-}
 
 // Split count, chunk floor and workspace partition of one call.
 struct Plan {
@@ -295,9 +324,9 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
     int num_cus = 0;
     int st = device_cus(&num_cus);
     if (st != GQA_OK) return st;
-    int tpt, qtiles;
-    query_tiles(s_q, h_q / h_kv, &tpt, &qtiles);
-    ns = pick_splits_host(B * qtiles, h_kv, s_kv_hint, num_cus);
+    int tpt, qtiles, tpw, passes;
+    query_tiles(s_q, h_q / h_kv, &tpt, &qtiles, &tpw, &passes);
+    ns = pick_splits_host(B, passes, h_kv, s_kv_hint, num_cus, tpw == 2 ? kTwoTiles : kOneTile);
   }
   pl->ns = ns;
   pl->min_chunk = n_splits > 0 ? 1 : kMinChunk;
@@ -321,14 +350,14 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
               int d_head, float scale, int in_dtype, hipStream_t stream, int flags,
               void* out = nullptr, int out_dtype = GQA_DTYPE_F32, int s_q = 1) {
   const int fused = (flags & GQA_FLAG_FUSED) ? 1 : 0;
-  int tpt, qtiles;
-  query_tiles(s_q, h_q / h_kv, &tpt, &qtiles);
+  int tpt, qtiles, tpw, passes;
+  query_tiles(s_q, h_q / h_kv, &tpt, &qtiles, &tpw, &passes);
   gqa::SplitArgs sa{q, k_cache, v_cache, seq_lens, kv_token_offsets, pl.ws_o, pl.ws_ml,
                     h_q, h_kv, pl.ns, pl.min_chunk, scale * gqa::kLog2e,
                     fused, out_dtype == GQA_DTYPE_BF16 ? 1 : 0, out, pl.counters,
                     fused ? (g_call_tag.fetch_add(1) & 0xFFFFFFFFFFFFull) : 0ull,
-                    s_q, tpt, qtiles};
-  const dim3 grid = gqa::split_grid(pl.ns, h_kv, B * qtiles);
+                    s_q, tpt, qtiles, passes};
+  const dim3 grid = gqa::split_grid(pl.ns, h_kv, B * passes);
   const bool bf16 = in_dtype == GQA_DTYPE_BF16;
   const bool valu = (flags & GQA_FLAG_VALU) != 0;
   const int nrep = h_q / h_kv;
@@ -431,9 +460,10 @@ int gqa_decode_attn_multi(const void* q, const void* k_cache, const void* v_cach
     return fail(GQA_ERR_INVALID_ARG, "S_q %d not in [1, %d]", S_q, GQA_MAX_QUERY_TOKENS);
   if ((st = check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets, scale, GQA_DTYPE_BF16, 0))) return st;
   if ((st = check_shape(B, h_q, h_kv, d_head, n_splits, s_kv_hint))) return st;
-  int tpt, qtiles;
-  query_tiles(S_q, h_q / h_kv, &tpt, &qtiles);
-  if ((int64_t)B * qtiles > 65535) return fail(GQA_ERR_INVALID_ARG, "B * query tiles must be <= 65535");
+  int tpt, qtiles, tpw, passes;
+  query_tiles(S_q, h_q / h_kv, &tpt, &qtiles, &tpw, &passes);
+  if ((int64_t)B * passes > 65535)
+    return fail(GQA_ERR_INVALID_ARG, "B * ceil(query tiles / 2) must be <= 65535");
   const size_t qo = (size_t)B * S_q * h_q * d_head;
   if ((st = check_out(out, out_dtype, qo))) return st;
   const size_t out_el = out_dtype == GQA_DTYPE_BF16 ? 2 : 4;
@@ -507,7 +537,7 @@ int gqa_decode_step(const void* q, const void* k_new, const void* v_new, void* k
     return st;
   gqa::SplitArgs sa{q, k_cache, v_cache, seq_lens, kv_token_offsets, pl.ws_o, pl.ws_ml,
                     h_q, h_kv, pl.ns, pl.min_chunk, scale * gqa::kLog2e,
-                    0, 0, nullptr, pl.counters, 0ull, 1, 1, 1,
+                    0, 0, nullptr, pl.counters, 0ull, 1, 1, 1, 1,
                     k_new, v_new, seq_lens_out, (int)capacity};
   const dim3 grid = gqa::split_grid(pl.ns, h_kv, B);
   const int nrep = h_q / h_kv;

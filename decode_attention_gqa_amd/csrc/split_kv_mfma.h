@@ -144,10 +144,14 @@ struct SoftmaxState {
   float l;   // partial sum of exponentials over this lane's tokens
 };
 
+// Scores of one 16-column tile for a block and the online-softmax update of
+// its state (running max, sum, and the rescale of its accumulators); gives
+// P^T as bf16 hi + lo parts in the B-operand layout.
 template <int D>
-__device__ __forceinline__ void compute_block(const KVRegs<D>& r, const bf16x8 (&qop)[MfmaTile<D>::KS],
+__device__ __forceinline__ void softmax_block(const KVRegs<D>& r, const bf16x8 (&qop)[MfmaTile<D>::KS],
                                               f32x4 (&acc)[MfmaTile<D>::NT], SoftmaxState& st,
-                                              float scale_log2, int grp, bool mask, int nvl) {
+                                              float scale_log2, int grp, bool mask, int nvl,
+                                              bf16x8& ph, bf16x8& pl) {
   constexpr int KS = MfmaTile<D>::KS, NT = MfmaTile<D>::NT;
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -192,18 +196,28 @@ __device__ __forceinline__ void compute_block(const KVRegs<D>& r, const bf16x8 (
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
   }
-  bf16x8 ph, pl;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const __bf16 h = (__bf16)p[j];
     ph[j] = h;
     pl[j] = (__bf16)(p[j] - (float)h);
   }
+}
+
+// O^T += V^T P^T for TILES column tiles that share the block's V: each V^T
+// operand is formed once and multiplied with every tile's P^T (hi and lo).
+template <int D, int TILES>
+__device__ __forceinline__ void pv_block(const KVRegs<D>& r, f32x4 (&acc)[TILES][MfmaTile<D>::NT],
+                                         const bf16x8 (&ph)[TILES], const bf16x8 (&pl)[TILES]) {
+  constexpr int NT = MfmaTile<D>::NT;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const bf16x8 a = v_tile<D>(r, nt);
-    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph, acc[nt], 0, 0, 0);
-    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl, acc[nt], 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[t], acc[t][nt], 0, 0, 0);
+      acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[t], acc[t][nt], 0, 0, 0);
+    }
   }
 }
 
@@ -212,20 +226,33 @@ __device__ __forceinline__ void compute_block(const KVRegs<D>& r, const bf16x8 (
 // tokens long; when S_b < capacity its last token is the new one, read from
 // k_new / v_new by the workgroup whose chunk holds it, which also copies that
 // row into the cache (no other workgroup reads it), and lens_out[b] = S.
-template <int D, int NREP, bool APPEND = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void split_kv_mfma(SplitArgs a) {
+//
+// TILES = 2 (several query tokens): the workgroup carries two 16-column tiles
+// of (query token, head) columns through the chunk, so each K/V block is read
+// once for both; each tile has its own softmax state and accumulators, and
+// they share the block's V^T operands. Twice the accumulators leave room for
+// one workgroup per CU only (one wave per SIMD).
+template <int D, int NREP, bool APPEND = false, int TILES = 1>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TILES == 1 ? 2 : 1)))
+void split_kv_mfma(SplitArgs a) {
   constexpr int KS = MfmaTile<D>::KS, NT = MfmaTile<D>::NT;
   static_assert(NREP >= 1 && NREP <= 16, "one 16-wide MFMA tile holds the query heads of a group");
+  static_assert(TILES == 1 || (TILES == 2 && !APPEND), "two tiles serve multi-token decode only");
   const WgCoord wc = wg_coord();
   const int s = wc.s, g = wc.g;
-  const int b = wc.b / a.qtiles, tile = wc.b - b * a.qtiles;
+  const int b = wc.b / a.passes, pass = wc.b - b * a.passes;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int grp = lane >> 4, n = lane & 15;
-  // Column n of the 16-wide tile: query token qi, head g*NREP + hh.
+  // Column n of tile t: query token qi[t], head g*NREP + hh.
   const int ti = n / NREP, hh = n % NREP;
-  const int qi = tile * a.tpt + ti;
-  const bool col = ti < a.tpt && qi < a.s_q;
+  int qi[TILES];
+  bool col[TILES];
+#pragma unroll
+  for (int t = 0; t < TILES; ++t) {
+    qi[t] = (pass * TILES + t) * a.tpt + ti;
+    col[t] = ti < a.tpt && qi[t] < a.s_q;
+  }
   const bool causal = a.s_q > 1;
 
   int S;
@@ -259,25 +286,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const __bf16* vbase = static_cast<const __bf16*>(a.v) + ((off + t0) * a.h_kv + g) * D;
 
   // Q^T as the B operand: lane (grp, n) holds q[token qi][head g*NREP + hh][32*kk + 8*grp .. +8].
-  bf16x8 qop[KS];
-  {
+  bf16x8 qop[TILES][KS];
+  int lim[TILES];                                  // last position each column's token attends
+#pragma unroll
+  for (int t = 0; t < TILES; ++t) {
     const int h = g * NREP + hh;
     const __bf16* qrow =
-        static_cast<const __bf16*>(a.q) + (((int64_t)b * a.s_q + qi) * a.h_q + h) * D + 8 * grp;
+        static_cast<const __bf16*>(a.q) + (((int64_t)b * a.s_q + qi[t]) * a.h_q + h) * D + 8 * grp;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       uint4 u = make_uint4(0u, 0u, 0u, 0u);
-      if (col) u = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
-      qop[kk] = __builtin_bit_cast(bf16x8, u);
+      if (col[t]) u = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
+      qop[t][kk] = __builtin_bit_cast(bf16x8, u);
     }
+    lim[t] = S - a.s_q + qi[t];                    // causal among the new tokens
   }
-  // Last position this lane's query token attends (causal among the new tokens).
-  const int lim = S - a.s_q + qi;
 
-  f32x4 acc[NT];
+  f32x4 acc[TILES][NT];
+  SoftmaxState st[TILES];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  SoftmaxState st{-INFINITY, 0.f};
+  for (int t = 0; t < TILES; ++t) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st[t] = SoftmaxState{-INFINITY, 0.f};
+  }
 
   // APPEND: the workgroup whose chunk ends the sequence also copies the new
   // token's K and V rows of head g into the cache: 16-byte pieces loaded
@@ -313,8 +345,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     };
     auto step = [&](const KVRegs<D>& r, int bk) {
       const int nv = min(32, ntok - bk * 32);
-      const int nvl = causal ? min(nv, lim - ((int)t0 + bk * 32) + 1) : nv;
-      compute_block<D>(r, qop, acc, st, a.scale_log2, grp, nv < 32 || causal, nvl);
+      bf16x8 ph[TILES], pl[TILES];
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        const int nvl = causal ? min(nv, lim[t] - ((int)t0 + bk * 32) + 1) : nv;
+        softmax_block<D>(r, qop[t], acc[t], st[t], a.scale_log2, grp, nv < 32 || causal, nvl, ph[t], pl[t]);
+      }
+      pv_block<D, TILES>(r, acc, ph, pl);
     };
     // Two register buffers in turn: the next block of this wave is in flight
     // while the current one is computed.
@@ -339,50 +376,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(tid < U16 ? a.k : a.v)) + row_new +
                               16 * (tid % U16)) = piece;
 
-  // l: sum the 4 lane groups' partial sums (m is already shared by them).
-  st.l += __shfl_xor(st.l, 16);
-  st.l += __shfl_xor(st.l, 32);
-
-  // Merge the 4 waves' states in LDS and write the workgroup's triplets.
+  // Merge the 4 waves' states in LDS and write the workgroup's triplets, one
+  // tile at a time through the same LDS.
   constexpr int OP = D + 4;                        // padded row (fewer bank conflicts)
-  const int cols = NREP * a.tpt;                                      // columns in use (<= 16)
+  constexpr int Q4 = D / 4;
+  const int cols = NREP * a.tpt;                   // columns in use (<= 16)
   __shared__ float sm_m[kWaves][16], sm_l[kWaves][16];
   __shared__ float sm_o[kWaves][16][OP];
-  if (grp == 0) {
-    sm_m[w][n] = st.m;
-    sm_l[w][n] = st.l;
-  }
-  if (n < cols) {
-    // lane (grp, n) holds o[column n][NT*(4*grp + r) + nt]
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sm_o[w][n][NT * (4 * grp + r) + nt] = acc[nt][r];
-  }
-  __syncthreads();
-  constexpr int Q4 = D / 4;
-  for (int idx = tid; idx < cols * Q4; idx += kThreads) {
-    const int h = idx / Q4, d4 = (idx % Q4) * 4;      // h: column of the tile
-    const int cqi = tile * a.tpt + h / NREP;
-    if (cqi >= a.s_q) continue;
-    float M = sm_m[0][h];
-#pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][h]);
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    float L = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const float mw = sm_m[ww][h];
-      const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);   // a wave with no block
-      L += f * sm_l[ww][h];
-      o.x += f * sm_o[ww][h][d4 + 0];
-      o.y += f * sm_o[ww][h][d4 + 1];
-      o.z += f * sm_o[ww][h][d4 + 2];
-      o.w += f * sm_o[ww][h][d4 + 3];
+  for (int t = 0; t < TILES; ++t) {
+    // l: sum the 4 lane groups' partial sums (m is already shared by them).
+    float l = st[t].l;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (t > 0) __syncthreads();                    // the previous tile's reads are done
+    if (grp == 0) {
+      sm_m[w][n] = st[t].m;
+      sm_l[w][n] = l;
     }
-    const int64_t row = (((int64_t)b * a.s_q + cqi) * a.h_q + g * NREP + h % NREP) * a.n_splits + s;
-    *reinterpret_cast<float4*>(a.ws_o + row * D + d4) = o;
-    if (d4 == 0) a.ws_ml[row] = make_float2(M, L);
+    if (n < cols) {
+      // lane (grp, n) holds o[column n][NT*(4*grp + r) + nt]
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) sm_o[w][n][NT * (4 * grp + r) + nt] = acc[t][nt][r];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < cols * Q4; idx += kThreads) {
+      const int h = idx / Q4, d4 = (idx % Q4) * 4;      // h: column of the tile
+      const int cqi = (pass * TILES + t) * a.tpt + h / NREP;
+      if (cqi >= a.s_q) continue;
+      float M = sm_m[0][h];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][h]);
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+      float L = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float mw = sm_m[ww][h];
+        const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);   // a wave with no block
+        L += f * sm_l[ww][h];
+        o.x += f * sm_o[ww][h][d4 + 0];
+        o.y += f * sm_o[ww][h][d4 + 1];
+        o.z += f * sm_o[ww][h][d4 + 2];
+        o.w += f * sm_o[ww][h][d4 + 3];
+      }
+      const int64_t row = (((int64_t)b * a.s_q + cqi) * a.h_q + g * NREP + h % NREP) * a.n_splits + s;
+      *reinterpret_cast<float4*>(a.ws_o + row * D + d4) = o;
+      if (d4 == 0) a.ws_ml[row] = make_float2(M, L);
+    }
   }
   if (a.fused) fused_epilogue<D, NREP>(a, g, b, n_active);
 }

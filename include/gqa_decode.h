@@ -133,13 +133,14 @@ int gqa_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
  * (position S_b - S_q + i) attends cache positions [0, S_b - S_q + i] - causal
  * among the new tokens. A token with S_b - S_q + i < 0 gets zeros. With
  * S_q = 1 this equals gqa_decode_attn_ex. bf16 inputs (matrix-core kernel),
- * fp32 or bf16 out, 1 <= S_q <= GQA_MAX_QUERY_TOKENS. Up to 16 / n_rep query
- * tokens share one pass over the KV range (they fill the columns of the
- * 16-wide MFMA tile that single-token decode leaves empty when n_rep < 16);
- * more tokens take more passes. Workspace: gqa_decode_workspace_bytes(B * S_q,
- * h_q, d_head, n) with n = n_splits if > 0, else
- * gqa_decode_pick_splits(B * ceil(S_q / t), h_kv, s_kv_hint, 0) where
- * t = min(S_q, 16 / n_rep). Other arguments as in gqa_decode_attn_ex.
+ * fp32 or bf16 out, 1 <= S_q <= GQA_MAX_QUERY_TOKENS. The (token, head)
+ * columns fill 16-wide MFMA tiles of t = min(S_q, 16 / n_rep) tokens (the
+ * columns single-token decode leaves empty when n_rep < 16), and one pass over
+ * the KV range serves two tiles, so 2t tokens read the KV once; more tokens
+ * take more passes. Workspace: gqa_decode_workspace_bytes(B * S_q, h_q,
+ * d_head, n) with n = n_splits if > 0, else gqa_decode_multi_splits(B, S_q,
+ * h_q, h_kv, s_kv_hint, 0). B * ceil(ceil(S_q / t) / 2) <= 65535. Other
+ * arguments as in gqa_decode_attn_ex.
  */
 int gqa_decode_attn_multi(const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* seq_lens, const int64_t* kv_token_offsets, void* out,
@@ -263,6 +264,12 @@ int gqa_decode_merge(const int32_t* seq_lens, const void* workspace, size_t work
  * fails). Pure host arithmetic otherwise.
  */
 int gqa_decode_pick_splits(int B, int h_kv, int64_t s_kv_max, int num_cus);
+
+/* Split count gqa_decode_attn_multi uses when n_splits <= 0 (the same rule,
+ * for its kernels: with two column tiles per workgroup, one workgroup per CU,
+ * one round of them for a single sequence, chunks of up to 16384 tokens).
+ * Negative status on invalid arguments or a failed device query. */
+int gqa_decode_multi_splits(int B, int S_q, int h_q, int h_kv, int64_t s_kv_max, int num_cus);
 
 /* Workspace bytes for n_splits chunks. Layout, each part starting on a
  * 256-byte boundary:

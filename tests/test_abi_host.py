@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_attn_multi", "gqa_decode_partial",
                             "gqa_decode_merge", "gqa_kv_append", "gqa_decode_step", "gqa_decode_attn_triplet",
-                            "gqa_merge_triplets", "gqa_decode_pick_splits",
+                            "gqa_merge_triplets", "gqa_decode_pick_splits", "gqa_decode_multi_splits",
                             "gqa_decode_workspace_bytes", "gqa_status_string", "gqa_last_error",
                             "gqa_decode_set_split_events"])
 
@@ -147,6 +147,21 @@ def test_split_heuristic_values(gqa):
     assert gqa.gqa_decode_pick_splits(1, 8, 1 << 22, 256) == 1024
     # several sequences: the longest over four rounds
     assert gqa.gqa_decode_pick_splits(8, 8, 32768, 256) == 32
+
+
+def test_multi_split_heuristic_values(gqa):
+    f = lambda B, S_q, S, h_q=64, h_kv=8: gqa.lib.gqa_decode_multi_splits(B, S_q, h_q, h_kv, S, 256)
+    # one query token, or a single 16-column tile: the single-token rule
+    assert f(1, 1, 8192) == gqa.gqa_decode_pick_splits(1, 8, 8192, 256) == 64
+    assert f(1, 2, 8192) == 64
+    # two tiles per workgroup, one workgroup per CU: one round for one sequence
+    assert f(1, 4, 8192) == 32
+    assert f(1, 8, 8192) == 16                   # two passes of two tiles
+    assert f(1, 4, 1 << 20) == 64                # chunks of up to 16384 tokens
+    assert f(8, 4, 32768) == 16                  # a batch: the longest over four rounds
+    assert f(1, 32, 4096, 32, 32) == 8           # MHA: 16 tokens per tile
+    assert f(1, 4, 8192, 64, 0) == -1
+    assert f(1, 0, 8192) == -1
 
 
 def test_binding_rejects_cpu_tensors(gqa):

@@ -46,7 +46,8 @@ def check(name, inp, qm, **kw):
     return got, ref
 
 
-@pytest.mark.parametrize("n_rep,S_q", [(8, 2), (8, 4), (8, 7), (4, 4), (4, 9), (2, 8), (1, 16), (1, 5), (16, 3)])
+@pytest.mark.parametrize("n_rep,S_q", [(8, 2), (8, 3), (8, 4), (8, 7), (4, 4), (4, 9), (2, 8), (1, 16), (1, 5), (1, 32),
+                                      (16, 3), (8, 64)])
 @pytest.mark.parametrize("d", [64, 128])
 def test_multi_parity(n_rep, S_q, d):
     h_kv = 2
