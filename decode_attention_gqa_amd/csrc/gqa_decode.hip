@@ -192,17 +192,30 @@ int pick_splits_host(int B, int passes, int h_kv, int64_t s_kv_max, int num_cus,
   const int64_t units = (int64_t)B * passes * h_kv;
   const int64_t slots = (int64_t)p.wg_per_cu * num_cus;
   int64_t n = (slots + units - 1) / units;
-  if (s_kv_max > 0) {
-    // ... and, when the longest sequence is known, chunks short enough that
-    // its workgroups are spread over the policy's rounds of the resident
-    // slots; chunks stay within [kMinChunk, max_chunk] tokens.
-    const int64_t rounds = B == 1 ? p.rounds_one : p.rounds_many;
-    int64_t chunk = (s_kv_max * units + rounds * slots - 1) / (rounds * slots);
+  if (s_kv_max > 0 && B == 1) {
+    // ... one sequence: a whole number of such rounds, up to the policy's,
+    // as long as chunks stay at least kMinChunk tokens (a length just past a
+    // multiple of the chunk must not leave a few workgroups for a last,
+    // nearly empty round), and chunks of at most max_chunk tokens.
+    int64_t k = s_kv_max / (kMinChunk * n);
+    if (k > p.rounds_one) k = p.rounds_one;
+    if (k < 1) k = 1;
+    n *= k;
+    const int64_t by_max = (s_kv_max + p.max_chunk - 1) / p.max_chunk;
+    if (by_max > n) n = by_max;
+  } else if (s_kv_max > 0) {
+    // ... several sequences: chunks short enough that the longest one's
+    // workgroups are spread over the policy's rounds of the resident slots
+    // (only the longest length is known, and more rounds keep a ragged batch
+    // balanced); chunks within [kMinChunk, max_chunk] tokens.
+    int64_t chunk = (s_kv_max * units + p.rounds_many * slots - 1) / (p.rounds_many * slots);
     if (chunk > p.max_chunk) chunk = p.max_chunk;
     if (chunk < kMinChunk) chunk = kMinChunk;
     const int64_t by_len = (s_kv_max + chunk - 1) / chunk;
     if (by_len > n) n = by_len;
-    const int64_t cap = (s_kv_max + kMinChunk - 1) / kMinChunk;
+  }
+  if (s_kv_max > 0) {
+    const int64_t cap = (s_kv_max + kMinChunk - 1) / kMinChunk;   // no chunk shorter than kMinChunk
     if (n > cap) n = cap;
   }
   if (n < 1) n = 1;

@@ -14,6 +14,11 @@ and writes N MiB).
 Writes profiles/split_kv_<W>.md (durations, counters, scale factors and the
 commands) and profiles/counters_split_kv_<W>.json (the traffic figure bench.py
 reports while the kernel sources are unchanged).
+
+    python profile_summary.py --trace-only NAME --kt DIR --cmd-kt "..."
+
+writes profiles/NAME.md with the kernel durations of one kernel-trace run
+(for the other modes of bench.py: decode step, multi-token decode).
 """
 from __future__ import annotations
 
@@ -60,17 +65,23 @@ def pick(d: dict, key: str):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--workload", required=True)
+    ap.add_argument("--workload")
     ap.add_argument("--kt", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
-    ap.add_argument("--calib-mib", type=int, required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--calib-mib", type=int)
     ap.add_argument("--cmd-kt", required=True)
-    ap.add_argument("--cmd-fetch", required=True)
-    ap.add_argument("--cmd-write", required=True)
+    ap.add_argument("--cmd-fetch")
+    ap.add_argument("--cmd-write")
     ap.add_argument("--split-key", default="gqa::split_kv_")
     ap.add_argument("--merge-key", default="gqa::merge_splits")
+    ap.add_argument("--trace-only", metavar="NAME")
     a = ap.parse_args()
+    if a.trace_only:
+        return trace_only(a)
+    for k in ("workload", "fetch", "write", "calib_mib", "cmd_fetch", "cmd_write"):
+        if getattr(a, k) is None:
+            ap.error(f"--{k.replace('_', '-')} is required without --trace-only")
 
     import bench
     import workloads
@@ -130,6 +141,20 @@ def main():
                "fetch_scale": kf, "write_scale": kw, "algorithmic_bytes_per_launch": kv,
                "kernel_avg_us": split_stat[0][2] / 1e3 if split_stat else None},
               open(js, "w"), indent=1)
+    print(open(md).read())
+
+
+def trace_only(a):
+    import bench
+    lines = [f"# kernel durations: {a.trace_only}", "",
+             f"kernel sources sha256[:16]: {bench.kernel_source_hash()}", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for n, c, avg, mn, mx in kernel_stats(a.kt):
+        if "gqa::" in n:
+            lines.append(f"| `{n}` | {c} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} |")
+    lines += ["", "## Command (run from the repository root)", "", f"    {a.cmd_kt}", ""]
+    md = os.path.join(ROOT, "profiles", f"{a.trace_only}.md")
+    open(md, "w").write("\n".join(lines) + "\n")
     print(open(md).read())
 
 
