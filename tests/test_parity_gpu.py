@@ -95,6 +95,22 @@ def test_split_counts_agree(ns):
     report(f"70B S=8192 ns={ns}", max_err(got, ref_of(inp)), used, TOL_F32)
 
 
+_RAGGED = {}
+
+
+@pytest.mark.parametrize("hint", [0, 100, 5000, 1 << 20])
+def test_wrong_length_hints_only_change_the_split_count(hint):
+    """s_kv_hint is a performance hint: below the real lengths (100, 5000 for
+    lengths up to 32739), unknown (0) or far above them, the chunking on the
+    device still covers every token with at most n_splits chunks."""
+    if not _RAGGED:
+        _RAGGED["inp"] = inp = workloads.make_inputs("llama70b_gqa_b8_ragged")
+        _RAGGED["ref"] = ref_of(inp)
+    inp, ref = _RAGGED["inp"], _RAGGED["ref"]
+    got, used = run_gpu(inp, hint=hint)
+    report(f"ragged hint={hint}", max_err(got, ref), used, TOL_F32)
+
+
 @pytest.mark.parametrize("ns", [33, 129, 300])
 def test_split_counts_d64(ns):
     """d = 64: two 32-column slices per merged row; several load rounds."""
