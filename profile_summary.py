@@ -76,6 +76,8 @@ def main():
     ap.add_argument("--split-key", default="gqa::split_kv_")
     ap.add_argument("--merge-key", default="gqa::merge_splits")
     ap.add_argument("--trace-only", metavar="NAME")
+    ap.add_argument("--busy", help="a --pmc run of VALUBusy MfmaUtil SQ_INSTS_VALU SQ_INSTS_MFMA")
+    ap.add_argument("--cmd-busy")
     a = ap.parse_args()
     if a.trace_only:
         return trace_only(a)
@@ -124,10 +126,20 @@ def main():
     lines.append(f"split kernel `{sname}`: FETCH_SIZE {f_split:.0f} KiB ({ns_f} dispatches), "
                  f"WRITE_SIZE {w_split:.0f} KiB ({ns_w} dispatches)")
     lines.append(f"scaled HBM traffic per launch: {hbm:.0f} bytes = {hbm / kv:.4f} x the algorithmic KV bytes")
+    if a.busy:
+        busy = {name: pick(counters(a.busy, name), a.split_key)[1]
+                for name in ("VALUBusy", "MfmaUtil", "SQ_INSTS_VALU", "SQ_INSTS_MFMA")}
+        lines.append("")
+        lines.append("## Compute units (rocprofv3 --pmc), split kernel, per dispatch")
+        lines.append("")
+        lines.append(f"VALUBusy {busy['VALUBusy'][1]:.1f}% (vector ALU busy, share of the kernel's GPU time), "
+                     f"MfmaUtil {busy['MfmaUtil'][1]:.1f}% (matrix cores busy); "
+                     f"{busy['SQ_INSTS_VALU'][1]:.0f} VALU and {busy['SQ_INSTS_MFMA'][1]:.0f} MFMA "
+                     f"instructions ({busy['VALUBusy'][0]} dispatches)")
     lines.append("")
     lines.append("## Commands (run from the repository root)")
     lines.append("")
-    for c in (a.cmd_kt, a.cmd_fetch, a.cmd_write):
+    for c in (a.cmd_kt, a.cmd_fetch, a.cmd_write) + ((a.cmd_busy,) if a.busy and a.cmd_busy else ()):
         lines.append(f"    {c}")
     lines.append("")
     lines.append(f"    python profile_summary.py --workload {a.workload} --kt <kt dir> --fetch <fetch dir> "
