@@ -108,6 +108,45 @@ __device__ __forceinline__ void seq_info(const int32_t* seq_lens, const int64_t*
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Butterfly steps of a wave-wide reduction as VALU operations instead of LDS
+// permutes: each returns op(x, x of lane ^ 32 / ^ 16 / ^ 8) in every lane,
+// with the two operands in the same order in both lanes of a pair (so both
+// hold the same bits). gfx950's permlane swaps exchange the two 32-lane
+// halves (or adjacent 16-lane rows) of two registers; given x twice they
+// return the pair's lower and upper values side by side. A DPP rotation by 8
+// within each 16-lane row pairs lane j with lane j ^ 8.
+__device__ __forceinline__ void halves32(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void halves16(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_x32(float x) { float a, b; halves32(x, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float sum_x32(float x) { float a, b; halves32(x, a, b); return a + b; }
+__device__ __forceinline__ float max_x16(float x) { float a, b; halves16(x, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float sum_x16(float x) { float a, b; halves16(x, a, b); return a + b; }
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {   // row_ror:8 = 0x128, quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float sum_x8(float x) {     // lanes j and j ^ 8 of each 16-lane row
+  const float y = dpp<0x128>(x);
+  return (__lane_id() & 8) ? y + x : x + y;            // lower lane's value first in both
+}
+__device__ __forceinline__ float max_x8(float x) { return fmaxf(x, dpp<0x128>(x)); }
+// Maximum over all 64 lanes, in every lane.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));                          // lane ^ 1
+  x = fmaxf(x, dpp<0x4E>(x));                          // lane ^ 2
+  x = fmaxf(x, dpp<0x124>(x));                         // row rotation by 4: with the next, the whole row
+  x = max_x8(x);
+  return max_x32(max_x16(x));
+}
+
 // Streaming loads of the KV cache: every K/V byte is read once per call, so
 // the loads carry the non-temporal hint (measured: 1M-token split kernel
 // 716 us -> 647 us, 6.0 -> 6.6 TB/s).

@@ -78,8 +78,7 @@ __global__ __launch_bounds__(256) void merge_splits(MergeArgs a) {
   for (int u = 0; u < U; ++u)
     if (u * SLOTS + slot < n_active) mx = fmaxf(mx, mv[u].x);
   for (int i = R + tid; i < n_active; i += 256) mx = fmaxf(mx, ml[i * ps].x);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  mx = wave_max(mx);
   if ((tid & 63) == 0) s_max[wave] = mx;
   __syncthreads();
   const float M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
@@ -106,14 +105,11 @@ __global__ __launch_bounds__(256) void merge_splits(MergeArgs a) {
   }
 
   // Sum over the 8 slots of each wave (lane bits 3..5), then over the 4 waves.
-#pragma unroll
-  for (int off = 8; off < 64; off <<= 1) {
-    acc.x += __shfl_xor(acc.x, off);
-    acc.y += __shfl_xor(acc.y, off);
-    acc.z += __shfl_xor(acc.z, off);
-    acc.w += __shfl_xor(acc.w, off);
-    L += __shfl_xor(L, off);
-  }
+  acc.x = sum_x32(sum_x16(sum_x8(acc.x)));
+  acc.y = sum_x32(sum_x16(sum_x8(acc.y)));
+  acc.z = sum_x32(sum_x16(sum_x8(acc.z)));
+  acc.w = sum_x32(sum_x16(sum_x8(acc.w)));
+  L = sum_x32(sum_x16(sum_x8(L)));
   __shared__ float4 s_acc[4][LPS];
   __shared__ float s_l[4];
   if ((tid & 63) < LPS) s_acc[wave][q] = acc;

@@ -173,8 +173,7 @@ __device__ __forceinline__ void softmax_block(const KVRegs<D>& r, const bf16x8 (
   float mb = x[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) mb = fmaxf(mb, x[j]);
-  mb = fmaxf(mb, __shfl_xor(mb, 16));
-  mb = fmaxf(mb, __shfl_xor(mb, 32));
+  mb = max_x32(max_x16(mb));                  // over the 4 lane groups of the column
   const float mn = fmaxf(st.m, mb);
   // mn = -inf only while every position this column has seen is masked (a
   // causal column before its first position); keep alpha and p at 0 then.
@@ -386,9 +385,7 @@ void split_kv_mfma(SplitArgs a) {
 #pragma unroll
   for (int t = 0; t < TILES; ++t) {
     // l: sum the 4 lane groups' partial sums (m is already shared by them).
-    float l = st[t].l;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = sum_x32(sum_x16(st[t].l));
     if (t > 0) __syncthreads();                    // the previous tile's reads are done
     if (grp == 0) {
       sm_m[w][n] = st[t].m;

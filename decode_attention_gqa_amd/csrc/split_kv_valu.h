@@ -65,11 +65,7 @@ struct Elem<__bf16> {
   }
 };
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
+// (wave_max: gqa_common.h.) A sum in butterfly order, so every lane holds the same bits.
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
