@@ -76,36 +76,6 @@ __device__ __forceinline__ void chunking(int S, int n_splits, int min_chunk, int
   n_active = (int)(((unsigned)S + uc - 1u) / uc);
 }
 
-// Length S_b and first token row of sequence b, with one round of loads:
-// explicit offsets are loaded next to seq_lens[b]; for the packed layout the
-// wave reads seq_lens[0..b] (lane j holds S_j of its 64-sequence slice),
-// takes S_b from lane b and sums the lanes below b (every lane gets both).
-__device__ __forceinline__ void seq_info(const int32_t* seq_lens, const int64_t* kv_off, int b,
-                                         int lane, int& S, int64_t& off) {
-  if (kv_off) {
-    S = seq_lens[b];
-    off = kv_off[b];
-    return;
-  }
-  if (b == 0) {
-    S = seq_lens[0];
-    off = 0;
-    return;
-  }
-  int64_t acc = 0;
-  int sb = 0;
-  for (int base = 0; base <= b; base += 64) {     // one pass when b < 64
-    const int j = base + lane;
-    const int v = (j <= b) ? seq_lens[j] : 0;
-    if (j < b) acc += v;
-    if (base + 64 > b) sb = __builtin_amdgcn_readlane(v, b - base);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-  S = sb;
-  off = acc;
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Butterfly steps of a wave-wide reduction as VALU operations instead of LDS
@@ -145,6 +115,65 @@ __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp<0x124>(x));                         // row rotation by 4: with the next, the whole row
   x = max_x8(x);
   return max_x32(max_x16(x));
+}
+
+// Sum of a 64-bit integer over all 64 lanes, in every lane (exact in any
+// order): quad butterflies and row rotations by 4 and 8 (DPP) cover each
+// 16-lane row, the permlane swaps the rows and halves.
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+  auto add = [&](uint32_t plo, uint32_t phi) { v += ((uint64_t)phi << 32) | plo; };
+  auto lo = [&]() { return (uint32_t)v; };
+  auto hi = [&]() { return (uint32_t)(v >> 32); };
+#define GQA_DPP_STEP(CTRL) \
+  add((uint32_t)__builtin_amdgcn_mov_dpp((int)lo(), CTRL, 0xF, 0xF, true), \
+      (uint32_t)__builtin_amdgcn_mov_dpp((int)hi(), CTRL, 0xF, 0xF, true))
+  GQA_DPP_STEP(0xB1);                                  // lane ^ 1
+  GQA_DPP_STEP(0x4E);                                  // lane ^ 2
+  GQA_DPP_STEP(0x124);                                 // row rotation by 4
+  GQA_DPP_STEP(0x128);                                 // row rotation by 8: every lane holds its row's sum
+#undef GQA_DPP_STEP
+  {
+    const auto rl = __builtin_amdgcn_permlane16_swap(lo(), lo(), false, false);
+    const auto rh = __builtin_amdgcn_permlane16_swap(hi(), hi(), false, false);
+    const bool up = __lane_id() & 16;                  // partner = the other row of the pair
+    add(up ? rl[0] : rl[1], up ? rh[0] : rh[1]);
+  }
+  {
+    const auto rl = __builtin_amdgcn_permlane32_swap(lo(), lo(), false, false);
+    const auto rh = __builtin_amdgcn_permlane32_swap(hi(), hi(), false, false);
+    const bool up = __lane_id() & 32;
+    add(up ? rl[0] : rl[1], up ? rh[0] : rh[1]);
+  }
+  return v;
+}
+
+
+// Length S_b and first token row of sequence b, with one round of loads:
+// explicit offsets are loaded next to seq_lens[b]; for the packed layout the
+// wave reads seq_lens[0..b] (lane j holds S_j of its 64-sequence slice),
+// takes S_b from lane b and sums the lanes below b (every lane gets both).
+__device__ __forceinline__ void seq_info(const int32_t* seq_lens, const int64_t* kv_off, int b,
+                                         int lane, int& S, int64_t& off) {
+  if (kv_off) {
+    S = seq_lens[b];
+    off = kv_off[b];
+    return;
+  }
+  if (b == 0) {
+    S = seq_lens[0];
+    off = 0;
+    return;
+  }
+  int64_t acc = 0;
+  int sb = 0;
+  for (int base = 0; base <= b; base += 64) {     // one pass when b < 64
+    const int j = base + lane;
+    const int v = (j <= b) ? seq_lens[j] : 0;
+    if (j < b) acc += v;
+    if (base + 64 > b) sb = __builtin_amdgcn_readlane(v, b - base);
+  }
+  S = sb;
+  off = (int64_t)wave_sum_u64((uint64_t)acc);
 }
 
 // Streaming loads of the KV cache: every K/V byte is read once per call, so
