@@ -2,9 +2,13 @@
 //
 // One workgroup owns one chunk of one (sequence b, kv head g) pair and the
 // n_rep query heads of that group. Each of its 4 waves walks 32-token blocks
-// of the chunk (wave w takes blocks w, w+4, ...) and keeps an online-softmax
-// state (m, l, o) for the group's heads; at the end the 4 states are merged
-// in LDS and the workgroup writes one (m, l, o) triplet per head.
+// of the chunk (wave w takes blocks w, w+4, ...), two register buffers in
+// turn so the next block is in flight while one is computed, and keeps an
+// online-softmax state (m, l, o) for the group's heads; at the end the 4
+// states are merged in LDS and the workgroup writes one (m, l, o) triplet
+// per head. Two template options widen the same kernel: APPEND (a decode
+// step that appends the new token on the way) and TILES = 2 (two 16-column
+// tiles of several query tokens per workgroup); see the kernel.
 //
 // Per 32-token block, with 16x16x32 bf16 MFMAs:
 //   scores  S^T[t, h] = K[t, :] . Q[h, :]      A = K rows, B = Q^T (2 tiles x D/32 steps)
@@ -12,8 +16,9 @@
 // Computing the transposed products makes the MFMA output layout of the
 // scores (lane = head, registers = 4 tokens) exactly the B-operand layout the
 // P.V product needs, and puts the per-head softmax statistics in the same
-// lanes as the output rows they rescale - no cross-lane shuffles besides the
-// max reduction. Query heads n_rep..15 of the 16-wide tile are zero padding.
+// lanes as the output rows they rescale - no cross-lane exchange besides the
+// max over a column's 4 lane groups (two permlane swaps). Query heads
+// n_rep..15 of the 16-wide tile are zero padding.
 //
 // Data movement: K and V go straight from HBM to registers with 16-byte
 // non-temporal loads (nothing is staged in LDS; the group's heads share each K/V register
