@@ -21,6 +21,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import hashlib
+import re
 import json
 import math
 import os
@@ -42,11 +43,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed: what the
+    compiler sees, so an edit of a comment keeps recorded counters valid."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "decode_attention_gqa_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "decode_attention_gqa_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
