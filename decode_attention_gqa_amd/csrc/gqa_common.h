@@ -43,6 +43,8 @@ struct SplitArgs {
   const void* v_new;
   int32_t* lens_out;          // [B] lengths after the append: min(S_b + 1, capacity)
   int capacity;               // token rows per sequence; rows start at kv_off[b] or b * capacity
+  // one chunk per sequence (n_splits = 1): write out = o / l directly, no merge kernel
+  int direct;
 };
 
 struct MergeArgs {

@@ -358,11 +358,16 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
   return GQA_OK;
 }
 
+// direct: the caller merges nothing afterwards; with one chunk per sequence
+// the split kernel then writes out itself (returned in *merged).
 int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* seq_lens, const int64_t* kv_token_offsets, int B, int h_q, int h_kv,
               int d_head, float scale, int in_dtype, hipStream_t stream, int flags,
-              void* out = nullptr, int out_dtype = GQA_DTYPE_F32, int s_q = 1) {
+              void* out = nullptr, int out_dtype = GQA_DTYPE_F32, int s_q = 1, bool* merged = nullptr) {
   const int fused = (flags & GQA_FLAG_FUSED) ? 1 : 0;
+  const bool mfma = in_dtype == GQA_DTYPE_BF16 && !(flags & GQA_FLAG_VALU);   // the kernel with the direct path
+  const int direct = (merged && !fused && mfma && pl.ns == 1) ? 1 : 0;
+  if (merged) *merged = fused || direct;
   int tpt, qtiles, tpw, passes;
   query_tiles(s_q, h_q / h_kv, &tpt, &qtiles, &tpw, &passes);
   gqa::SplitArgs sa{q, k_cache, v_cache, seq_lens, kv_token_offsets, pl.ws_o, pl.ws_ml,
@@ -370,6 +375,7 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
                     fused, out_dtype == GQA_DTYPE_BF16 ? 1 : 0, out, pl.counters,
                     fused ? (g_call_tag.fetch_add(1) & 0xFFFFFFFFFFFFull) : 0ull,
                     s_q, tpt, qtiles, passes};
+  sa.direct = direct;
   const dim3 grid = gqa::split_grid(pl.ns, h_kv, B * passes);
   const bool bf16 = in_dtype == GQA_DTYPE_BF16;
   const bool valu = (flags & GQA_FLAG_VALU) != 0;
@@ -421,10 +427,11 @@ int gqa_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
     return fail(GQA_ERR_INVALID_ARG, "out overlaps workspace");
   Plan pl;
   if ((st = make_plan(B, h_q, h_kv, d_head, n_splits, s_kv_hint, workspace, workspace_bytes, true, &pl))) return st;
+  bool merged = false;
   if ((st = run_split(pl, q, k_cache, v_cache, seq_lens, kv_token_offsets, B, h_q, h_kv, d_head, scale,
-                      in_dtype, stream, flags, out, out_dtype)))
+                      in_dtype, stream, flags, out, out_dtype, 1, &merged)))
     return st;
-  if (flags & GQA_FLAG_FUSED) return GQA_OK;
+  if (merged) return GQA_OK;
   return run_merge(pl, seq_lens, out, B, h_q, d_head, out_dtype, stream);
 }
 
@@ -488,9 +495,11 @@ int gqa_decode_attn_multi(const void* q, const void* k_cache, const void* v_cach
   Plan pl;
   if ((st = make_plan(B, h_q, h_kv, d_head, n_splits, s_kv_hint, workspace, workspace_bytes, true, &pl, S_q)))
     return st;
+  bool merged = false;
   if ((st = run_split(pl, q, k_cache, v_cache, seq_lens, kv_token_offsets, B, h_q, h_kv, d_head, scale,
-                      GQA_DTYPE_BF16, stream, 0, out, out_dtype, S_q)))
+                      GQA_DTYPE_BF16, stream, 0, out, out_dtype, S_q, &merged)))
     return st;
+  if (merged) return GQA_OK;
   return run_merge(pl, seq_lens, out, B, h_q, d_head, out_dtype, stream, S_q);
 }
 
@@ -550,13 +559,14 @@ int gqa_decode_step(const void* q, const void* k_new, const void* v_new, void* k
     return st;
   gqa::SplitArgs sa{q, k_cache, v_cache, seq_lens, kv_token_offsets, pl.ws_o, pl.ws_ml,
                     h_q, h_kv, pl.ns, pl.min_chunk, scale * gqa::kLog2e,
-                    0, 0, nullptr, pl.counters, 0ull, 1, 1, 1, 1,
-                    k_new, v_new, seq_lens_out, (int)capacity};
+                    0, out_dtype == GQA_DTYPE_BF16 ? 1 : 0, out, pl.counters, 0ull, 1, 1, 1, 1,
+                    k_new, v_new, seq_lens_out, (int)capacity, pl.ns == 1 ? 1 : 0};
   const dim3 grid = gqa::split_grid(pl.ns, h_kv, B);
   const int nrep = h_q / h_kv;
   hipError_t e = d_head == 128 ? launch_split_append<128>(nrep, grid, stream, sa)
                                : launch_split_append<64>(nrep, grid, stream, sa);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
+  if (sa.direct) return GQA_OK;                    // one chunk per sequence: out is written
   return run_merge(pl, seq_lens_out, out, B, h_q, d_head, out_dtype, stream);
 }
 

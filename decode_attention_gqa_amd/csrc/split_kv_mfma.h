@@ -280,6 +280,19 @@ void split_kv_mfma(SplitArgs a) {
   chunking(S, a.n_splits, a.min_chunk, c, n_active);
   if (s >= n_active) {                             // the merge reads chunks < n_active only
     if (a.fused && n_active == 0 && s == 0) fused_empty<D, NREP>(a, g, b);
+    if (a.direct && n_active == 0 && s == 0) {     // nothing attended: out = 0
+      constexpr int Q4 = D / 4;
+      for (int t = 0; t < TILES; ++t)
+        for (int idx = tid; idx < NREP * a.tpt * Q4; idx += kThreads) {
+          const int h = idx / Q4, cqi = (pass * TILES + t) * a.tpt + h / NREP;
+          if (cqi >= a.s_q) continue;
+          const int64_t e = (((int64_t)b * a.s_q + cqi) * a.h_q + g * NREP + h % NREP) * D + (idx % Q4) * 4;
+          if (a.out_bf16)
+            store4<__bf16>(static_cast<__bf16*>(a.out) + e, make_float4(0.f, 0.f, 0.f, 0.f));
+          else
+            store4<float>(static_cast<float*>(a.out) + e, make_float4(0.f, 0.f, 0.f, 0.f));
+        }
+    }
     return;
   }
   const int64_t t0 = (int64_t)s * c;
@@ -423,9 +436,19 @@ void split_kv_mfma(SplitArgs a) {
         o.z += f * sm_o[ww][h][d4 + 2];
         o.w += f * sm_o[ww][h][d4 + 3];
       }
-      const int64_t row = (((int64_t)b * a.s_q + cqi) * a.h_q + g * NREP + h % NREP) * a.n_splits + s;
-      *reinterpret_cast<float4*>(a.ws_o + row * D + d4) = o;
-      if (d4 == 0) a.ws_ml[row] = make_float2(M, L);
+      const int64_t orow = ((int64_t)b * a.s_q + cqi) * a.h_q + g * NREP + h % NREP;   // (b, token, head)
+      if (a.direct) {                              // the sequence's only chunk: out = o / l here
+        const float inv = L > 0.f ? 1.f / L : 0.f;   // L = 0: nothing attended (a causal column)
+        const float4 r = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+        if (a.out_bf16)
+          store4<__bf16>(static_cast<__bf16*>(a.out) + orow * D + d4, r);
+        else
+          store4<float>(static_cast<float*>(a.out) + orow * D + d4, r);
+      } else {
+        const int64_t row = orow * a.n_splits + s;
+        *reinterpret_cast<float4*>(a.ws_o + row * D + d4) = o;
+        if (d4 == 0) a.ws_ml[row] = make_float2(M, L);
+      }
     }
   }
   if (a.fused) fused_epilogue<D, NREP>(a, g, b, n_active);

@@ -118,6 +118,9 @@ int gqa_decode_attn(const void* q, const void* k_cache, const void* v_cache,
  *                    s_kv_hint, 0)); 256-byte aligned. NULL: library-owned.
  *  stream            HIP stream (NULL: null stream).
  *  flags             0 or an OR of GQA_FLAG_VALU and GQA_FLAG_FUSED.
+ * With one chunk per sequence (n = 1) and the matrix-core kernel, the split
+ * kernel writes out itself and no merge kernel runs (the same bits as the
+ * merge would give: a single triplet's weight is exactly 1).
  */
 int gqa_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* seq_lens, const int64_t* kv_token_offsets,

@@ -53,7 +53,7 @@ def test_multi_parity(n_rep, S_q, d):
     h_kv = 2
     lens = [700, 37, 1500]
     inp, qm = make(f"multi_r{n_rep}_q{S_q}_d{d}", 3, S_q, n_rep * h_kv, h_kv, d, lens, 90 + n_rep + S_q + d)
-    for ns in (0, 5, 64):
+    for ns in (0, 1, 5, 64):
         check(f"n_rep={n_rep} S_q={S_q} d={d} ns={ns}", inp, qm, n_splits=ns)
 
 

@@ -212,9 +212,10 @@ def test_runs_on_a_side_stream():
     report("side stream", max_err(got, ref_of(inp)), ns, TOL_F32)
 
 
-@pytest.mark.parametrize("ns", [0, 5])
+@pytest.mark.parametrize("ns", [0, 1, 5])
 def test_partial_then_merge_equals_full_call(ns):
-    """The two halves give the same bits as the one-call path."""
+    """The two halves give the same bits as the one-call path (with one chunk
+    per sequence the one-call path writes out in the split kernel)."""
     import torch
 
     import decode_attention_gqa_amd as gqa
@@ -232,6 +233,18 @@ def test_partial_then_merge_equals_full_call(ns):
     torch.cuda.synchronize()
     assert torch.equal(full, out)
     report(f"partial+merge ns={ns}", max_err(out.cpu().numpy().astype(np.float64), ref_of(inp)), n, TOL_F32)
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_one_chunk_per_sequence_writes_out_directly(out_dtype):
+    """n_splits = 1: no merge kernel; empty sequences still give zeros, bf16
+    output is the rounded fp32 output."""
+    lens = [0, 1, 31, 33, 700, 0, 2048]
+    inp = workloads.custom("direct", B=len(lens), h_q=64, h_kv=8, d=128, seq_lens=lens, seed=62)
+    got, used = run_gpu(inp, n_splits=1, out_dtype=out_dtype)
+    assert used == 1
+    report(f"one chunk per sequence out={out_dtype}", max_err(got, ref_of(inp)), used,
+           TOL_BF16 if out_dtype == "bf16" else TOL_F32)
 
 
 @pytest.mark.parametrize("B", [63, 64, 65, 130])
