@@ -1,3 +1,4 @@
+#include <type_traits>
 // Host side of the decode attention library: argument checks, split
 // heuristic, workspace, kernel selection and launches. C ABI in gqa_decode.h.
 #include "gqa_decode.h"
@@ -158,7 +159,21 @@ hipError_t launch_split_append(int nrep, dim3 grid, hipStream_t st, const gqa::S
 
 template <int D, typename TO>
 hipError_t launch_merge_t(int rows, hipStream_t st, const gqa::MergeArgs& a) {
-  // chunks per slot in the first round: one round covers up to 32 * U chunks
+  // Up to 8 chunks per row: several rows per workgroup (32 / SPR of them).
+  auto packed = [&](auto spr) {
+    constexpr int SPR = decltype(spr)::value;
+    const dim3 g((unsigned)((rows + 32 / SPR - 1) / (32 / SPR)), D / 32);
+    hipLaunchKernelGGL((gqa::merge_rows<D, TO, SPR>), g, dim3(256), 0, st, a, rows);
+  };
+  if (a.n_splits <= 8) {
+    if (a.n_splits == 1) packed(std::integral_constant<int, 1>{});
+    else if (a.n_splits == 2) packed(std::integral_constant<int, 2>{});
+    else if (a.n_splits <= 4) packed(std::integral_constant<int, 4>{});
+    else packed(std::integral_constant<int, 8>{});
+    return hipGetLastError();
+  }
+  // One row per workgroup; chunks per slot in the first round: one round
+  // covers up to 32 * U chunks.
   const dim3 grid((unsigned)rows, D / 32);
   if (a.n_splits <= 32)
     hipLaunchKernelGGL((gqa::merge_splits<D, TO, 1>), grid, dim3(256), 0, st, a);
