@@ -117,13 +117,15 @@ def gqa_decode_workspace_bytes(B: int, h_q: int, d_head: int, n_splits: int) -> 
 
 def workspace_layout(B: int, h_q: int, d_head: int, n_splits: int) -> dict:
     """Byte offsets of the workspace parts, as include/gqa_decode.h documents
-    them: arrival counters at 0, partial outputs at `o`, (m, l) pairs at `ml`;
-    `total` equals gqa_decode_workspace_bytes."""
+    them: arrival counters at 0, partial outputs at `o`, (m, l) pairs at `ml`,
+    packed-layout token bases at `tok`; `total` equals
+    gqa_decode_workspace_bytes."""
     r = lambda x: (x + 255) // 256 * 256
     rows = B * h_q * n_splits
     o = r(B * h_q * 8)
     ml = o + r(rows * d_head * 4)
-    return {"counters": 0, "o": o, "ml": ml, "total": ml + r(rows * 8)}
+    tok = ml + r(rows * 8)
+    return {"counters": 0, "o": o, "ml": ml, "tok": tok, "total": tok + r(B * 8)}
 
 
 def _torch():

@@ -17,6 +17,7 @@
 #include "fused_tail.h"
 #include "kv_append.h"
 #include "merge.h"
+#include "packed_offsets.h"
 #include "split_kv_mfma.h"
 #include "split_kv_valu.h"
 
@@ -103,9 +104,10 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 // Workspace layout, 256-byte aligned parts: arrival counters [B * h_kv] (room
 // for B * h_q) uint64 at 0, so their place does not depend on the split
-// count; o [B, h_q, n, d] fp32 at o_off; (m, l) [B, h_q, n] fp32 at ml_off.
+// count; o [B, h_q, n, d] fp32 at o_off; (m, l) [B, h_q, n] fp32 at ml_off;
+// packed-layout token bases [B] int64 at tok_off.
 struct WsLayout {
-  size_t o_off, ml_off, total;
+  size_t o_off, ml_off, tok_off, total;
 };
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 WsLayout ws_layout(int B, int h_q, int d, int n) {
@@ -113,9 +115,14 @@ WsLayout ws_layout(int B, int h_q, int d, int n) {
   WsLayout l;
   l.o_off = round256((size_t)B * h_q * sizeof(unsigned long long));
   l.ml_off = l.o_off + round256(rows * d * sizeof(float));
-  l.total = l.ml_off + round256(rows * sizeof(float2));
+  l.tok_off = l.ml_off + round256(rows * sizeof(float2));
+  l.total = l.tok_off + round256((size_t)B * sizeof(int64_t));
   return l;
 }
+
+// Above this many sequences a packed-layout call computes the token bases
+// with one scan launch instead of inside every split workgroup.
+constexpr int kScanMinBatch = 256;
 size_t ws_bytes(int B, int h_q, int d, int n) { return ws_layout(B, h_q, d, n).total; }
 
 // ---------------------------------------------------------------- launches
@@ -339,6 +346,7 @@ struct Plan {
   float* ws_o;
   float2* ws_ml;
   unsigned long long* counters;
+  int64_t* tok;                 // room for the packed layout's token bases
 };
 
 int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_hint,
@@ -370,6 +378,7 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
   pl->counters = static_cast<unsigned long long*>(workspace);
   pl->ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.o_off);
   pl->ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + lay.ml_off);
+  pl->tok = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + lay.tok_off);
   return GQA_OK;
 }
 
@@ -385,7 +394,14 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
   if (merged) *merged = fused || direct;
   int tpt, qtiles, tpw, passes;
   query_tiles(s_q, h_q / h_kv, &tpt, &qtiles, &tpw, &passes);
-  gqa::SplitArgs sa{q, k_cache, v_cache, seq_lens, kv_token_offsets, pl.ws_o, pl.ws_ml,
+  const int64_t* tok = kv_token_offsets;
+  if (!tok && B > kScanMinBatch) {             // packed layout, many sequences: scan once
+    hipLaunchKernelGGL(gqa::packed_offsets, dim3(1), dim3(1024), 0, stream, seq_lens, B, pl.tok);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(GQA_ERR_HIP, "token offset scan launch: %s", hipGetErrorString(e));
+    tok = pl.tok;
+  }
+  gqa::SplitArgs sa{q, k_cache, v_cache, seq_lens, tok, pl.ws_o, pl.ws_ml,
                     h_q, h_kv, pl.ns, pl.min_chunk, scale * gqa::kLog2e,
                     fused, out_dtype == GQA_DTYPE_BF16 ? 1 : 0, out, pl.counters,
                     fused ? (g_call_tag.fetch_add(1) & 0xFFFFFFFFFFFFull) : 0ull,

@@ -280,6 +280,10 @@ int gqa_decode_multi_splits(int B, int S_q, int h_q, int h_kv, int64_t s_kv_max,
  *             any initial contents are fine, each call tags its counts)
  *   o         [B, h_q, n_splits, d_head] fp32 at C = round_up(B*h_q*8, 256)
  *   (m, l)    [B, h_q, n_splits] fp32 pairs at C + round_up(B*h_q*n_splits*d_head*4, 256)
+ *   tok       [B] int64 after (m, l), at the next 256-byte boundary: with the
+ *             packed layout (no kv_token_offsets) and more than 256 sequences,
+ *             a call first writes each sequence's first token row here (one
+ *             scan launch) instead of summing seq_lens in every split workgroup
  * Calls that share a workspace must not overlap in time.
  * 0 for invalid arguments. */
 size_t gqa_decode_workspace_bytes(int B, int h_q, int d_head, int n_splits);

@@ -95,7 +95,8 @@ int main(void) {
   expect("multi S_q 4", gqa_decode_multi_splits(1, 4, 64, 8, 8192, 256), 32);
   expect("multi bad h_kv", gqa_decode_multi_splits(1, 4, 64, 0, 8192, 256), GQA_ERR_INVALID_ARG);
   expect("workspace bytes", (long)gqa_decode_workspace_bytes(8, 64, 128, 37),
-         (long)(512 * 8 + ((8L * 64 * 37 * 128 * 4 + 255) / 256) * 256 + ((8L * 64 * 37 * 8 + 255) / 256) * 256));
+         (long)(512 * 8 + ((8L * 64 * 37 * 128 * 4 + 255) / 256) * 256 + ((8L * 64 * 37 * 8 + 255) / 256) * 256 +
+                256));
   expect("workspace bytes 0", (long)gqa_decode_workspace_bytes(0, 64, 128, 4), 0);
   for (int s = 0; s >= -5; --s)
     if (!gqa_status_string(s) || !gqa_status_string(s)[0]) {

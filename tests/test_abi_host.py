@@ -112,7 +112,7 @@ def test_no_device_is_reported_not_crashed(gqa):
 def test_workspace_bytes(gqa):
     r = lambda x: (x + 255) // 256 * 256
     for B, h_q, d, n in [(1, 64, 128, 64), (8, 64, 128, 37), (1, 8, 64, 4), (3, 5, 64, 1)]:
-        want = r(B * h_q * 8) + r(B * h_q * n * d * 4) + r(B * h_q * n * 8)
+        want = r(B * h_q * 8) + r(B * h_q * n * d * 4) + r(B * h_q * n * 8) + r(B * 8)
         assert gqa.gqa_decode_workspace_bytes(B, h_q, d, n) == want
         assert gqa.workspace_layout(B, h_q, d, n)["total"] == want
     assert gqa.gqa_decode_workspace_bytes(0, 64, 128, 4) == 0
