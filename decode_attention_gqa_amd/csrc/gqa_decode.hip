@@ -1,3 +1,4 @@
+#include <algorithm>
 #include <type_traits>
 // Host side of the decode attention library: argument checks, split
 // heuristic, workspace, kernel selection and launches. C ABI in gqa_decode.h.
@@ -123,17 +124,25 @@ WsLayout ws_layout(int B, int h_q, int d, int n) {
 // Above this many sequences a packed-layout call computes the token bases
 // with one scan launch instead of inside every split workgroup.
 constexpr int kScanMinBatch = 256;
+// Chunks of at most this many tokens (by the length hint) run in one-wave
+// workgroups: a 4-wave workgroup gives each wave 32-token blocks of the
+// chunk, so shorter chunks leave waves without work, and one-wave
+// workgroups fit four times as many chunks on a CU (measured faster up to
+// 128 tokens).
+constexpr int kOneWaveMaxTokens = 128;
 size_t ws_bytes(int B, int h_q, int d, int n) { return ws_layout(B, h_q, d, n).total; }
 
 // ---------------------------------------------------------------- launches
 template <int D, int NREP>
-hipError_t launch_split(bool bf16, bool valu, dim3 grid, hipStream_t st, const gqa::SplitArgs& a) {
+hipError_t launch_split(bool bf16, bool valu, bool one_wave, dim3 grid, hipStream_t st, const gqa::SplitArgs& a) {
   if (!bf16) {
     hipLaunchKernelGGL((gqa::split_kv_valu<float, D, NREP>), grid, dim3(gqa::kThreads), 0, st, a);
   } else if (valu) {
     hipLaunchKernelGGL((gqa::split_kv_valu<__bf16, D, NREP>), grid, dim3(gqa::kThreads), 0, st, a);
   } else if (a.qtiles > a.passes) {               // two column tiles per workgroup
     hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, false, 2>), grid, dim3(gqa::kThreads), 0, st, a);
+  } else if (one_wave) {
+    hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, false, 1, 1>), grid, dim3(64), 0, st, a);
   } else {
     hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP>), grid, dim3(gqa::kThreads), 0, st, a);
   }
@@ -141,25 +150,33 @@ hipError_t launch_split(bool bf16, bool valu, dim3 grid, hipStream_t st, const g
 }
 
 template <int D>
-hipError_t launch_split_nrep(int nrep, bool bf16, bool valu, dim3 grid, hipStream_t st,
+hipError_t launch_split_nrep(int nrep, bool bf16, bool valu, bool one_wave, dim3 grid, hipStream_t st,
                              const gqa::SplitArgs& a) {
   switch (nrep) {
-    case 1: return launch_split<D, 1>(bf16, valu, grid, st, a);
-    case 2: return launch_split<D, 2>(bf16, valu, grid, st, a);
-    case 4: return launch_split<D, 4>(bf16, valu, grid, st, a);
-    case 8: return launch_split<D, 8>(bf16, valu, grid, st, a);
-    default: return launch_split<D, 16>(bf16, valu, grid, st, a);
+    case 1: return launch_split<D, 1>(bf16, valu, one_wave, grid, st, a);
+    case 2: return launch_split<D, 2>(bf16, valu, one_wave, grid, st, a);
+    case 4: return launch_split<D, 4>(bf16, valu, one_wave, grid, st, a);
+    case 8: return launch_split<D, 8>(bf16, valu, one_wave, grid, st, a);
+    default: return launch_split<D, 16>(bf16, valu, one_wave, grid, st, a);
   }
 }
 
+template <int D, int NREP>
+void launch_append_form(bool one_wave, dim3 grid, hipStream_t st, const gqa::SplitArgs& a) {
+  if (one_wave)
+    hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, true, 1, 1>), grid, dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, true>), grid, dim3(gqa::kThreads), 0, st, a);
+}
+
 template <int D>
-hipError_t launch_split_append(int nrep, dim3 grid, hipStream_t st, const gqa::SplitArgs& a) {
+hipError_t launch_split_append(int nrep, bool one_wave, dim3 grid, hipStream_t st, const gqa::SplitArgs& a) {
   switch (nrep) {
-    case 1: hipLaunchKernelGGL((gqa::split_kv_mfma<D, 1, true>), grid, dim3(gqa::kThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((gqa::split_kv_mfma<D, 2, true>), grid, dim3(gqa::kThreads), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((gqa::split_kv_mfma<D, 4, true>), grid, dim3(gqa::kThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((gqa::split_kv_mfma<D, 8, true>), grid, dim3(gqa::kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((gqa::split_kv_mfma<D, 16, true>), grid, dim3(gqa::kThreads), 0, st, a); break;
+    case 1: launch_append_form<D, 1>(one_wave, grid, st, a); break;
+    case 2: launch_append_form<D, 2>(one_wave, grid, st, a); break;
+    case 4: launch_append_form<D, 4>(one_wave, grid, st, a); break;
+    case 8: launch_append_form<D, 8>(one_wave, grid, st, a); break;
+    default: launch_append_form<D, 16>(one_wave, grid, st, a); break;
   }
   return hipGetLastError();
 }
@@ -347,6 +364,7 @@ struct Plan {
   float2* ws_ml;
   unsigned long long* counters;
   int64_t* tok;                 // room for the packed layout's token bases
+  int64_t hint;                 // the caller's longest length (0: unknown)
 };
 
 int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_hint,
@@ -366,6 +384,7 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
   }
   pl->ns = ns;
   pl->min_chunk = n_splits > 0 ? 1 : kMinChunk;
+  pl->hint = s_kv_hint;
   pl->need = ws_bytes(B * s_q, h_q, d_head, ns);
   if (workspace) {
     if (workspace_bytes < pl->need)
@@ -380,6 +399,20 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
   pl->ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + lay.ml_off);
   pl->tok = reinterpret_cast<int64_t*>(static_cast<char*>(workspace) + lay.tok_off);
   return GQA_OK;
+}
+
+// The matrix-core split kernel's workgroup form for a plan: one wave per
+// workgroup when the length hint puts every chunk at kOneWaveMaxTokens or
+// fewer and the grid is more than one round of 4-wave workgroups (two per
+// CU); with one round or less, four waves per chunk finish it sooner. A
+// wrong hint changes only the speed: both forms take any length.
+bool one_wave_form(const Plan& pl, int B, int h_kv) {
+  if (pl.hint <= 0) return false;
+  const int64_t per_chunk = (pl.hint + pl.ns - 1) / pl.ns;
+  if (std::min<int64_t>(pl.hint, std::max<int64_t>(per_chunk, pl.min_chunk)) > kOneWaveMaxTokens) return false;
+  int cus = 0;
+  if (device_cus(&cus) != GQA_OK) return false;
+  return (int64_t)pl.ns * h_kv * B > 2 * (int64_t)cus;
 }
 
 // direct: the caller merges nothing afterwards; with one chunk per sequence
@@ -414,8 +447,9 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
   hipError_t e;
   if (g_ev_before && (e = hipEventRecord(g_ev_before, stream)) != hipSuccess)
     return fail(GQA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-  e = d_head == 128 ? launch_split_nrep<128>(nrep, bf16, valu, grid, stream, sa)
-                    : launch_split_nrep<64>(nrep, bf16, valu, grid, stream, sa);
+  const bool one_wave = mfma && !fused && s_q == 1 && one_wave_form(pl, B, h_kv);
+  e = d_head == 128 ? launch_split_nrep<128>(nrep, bf16, valu, one_wave, grid, stream, sa)
+                    : launch_split_nrep<64>(nrep, bf16, valu, one_wave, grid, stream, sa);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
   if (g_ev_after && (e = hipEventRecord(g_ev_after, stream)) != hipSuccess)
     return fail(GQA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
@@ -594,8 +628,9 @@ int gqa_decode_step(const void* q, const void* k_new, const void* v_new, void* k
                     k_new, v_new, seq_lens_out, (int)capacity, pl.ns == 1 ? 1 : 0};
   const dim3 grid = gqa::split_grid(pl.ns, h_kv, B);
   const int nrep = h_q / h_kv;
-  hipError_t e = d_head == 128 ? launch_split_append<128>(nrep, grid, stream, sa)
-                               : launch_split_append<64>(nrep, grid, stream, sa);
+  const bool one_wave = one_wave_form(pl, B, h_kv);   // the same form as gqa_decode_attn_ex with this hint
+  hipError_t e = d_head == 128 ? launch_split_append<128>(nrep, one_wave, grid, stream, sa)
+                               : launch_split_append<64>(nrep, one_wave, grid, stream, sa);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
   if (sa.direct) return GQA_OK;                    // one chunk per sequence: out is written
   return run_merge(pl, seq_lens_out, out, B, h_q, d_head, out_dtype, stream);

@@ -8,7 +8,9 @@
 // states are merged in LDS and the workgroup writes one (m, l, o) triplet
 // per head. Two template options widen the same kernel: APPEND (a decode
 // step that appends the new token on the way) and TILES = 2 (two 16-column
-// tiles of several query tokens per workgroup); see the kernel.
+// tiles of several query tokens per workgroup); see the kernel. WAVES = 1
+// gives one-wave workgroups for chunks of a few blocks (many short
+// sequences), where some of four waves would have nothing to read.
 //
 // Per 32-token block, with 16x16x32 bf16 MFMAs:
 //   scores  S^T[t, h] = K[t, :] . Q[h, :]      A = K rows, B = Q^T (2 tiles x D/32 steps)
@@ -236,10 +238,13 @@ __device__ __forceinline__ void pv_block(const KVRegs<D>& r, f32x4 (&acc)[TILES]
 // once for both; each tile has its own softmax state and accumulators, and
 // they share the block's V^T operands. Twice the accumulators leave room for
 // one workgroup per CU only (one wave per SIMD).
-template <int D, int NREP, bool APPEND = false, int TILES = 1>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(TILES == 1 ? 2 : 1)))
+template <int D, int NREP, bool APPEND = false, int TILES = 1, int WAVES = kWaves>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(TILES == 1 ? 2 : 1)))
 void split_kv_mfma(SplitArgs a) {
   constexpr int KS = MfmaTile<D>::KS, NT = MfmaTile<D>::NT;
+  constexpr int THREADS = 64 * WAVES;
+  static_assert(WAVES == kWaves || (WAVES == 1 && TILES == 1), "one-wave form: one column tile");
+  static_assert(!APPEND || 2 * (D * 2 / 16) <= 64 * WAVES, "the new row's copy takes one thread per 16 bytes");
   static_assert(NREP >= 1 && NREP <= 16, "one 16-wide MFMA tile holds the query heads of a group");
   static_assert(TILES == 1 || (TILES == 2 && !APPEND), "two tiles serve multi-token decode only");
   const WgCoord wc = wg_coord();
@@ -279,11 +284,12 @@ void split_kv_mfma(SplitArgs a) {
   int c, n_active;
   chunking(S, a.n_splits, a.min_chunk, c, n_active);
   if (s >= n_active) {                             // the merge reads chunks < n_active only
-    if (a.fused && n_active == 0 && s == 0) fused_empty<D, NREP>(a, g, b);
+    if constexpr (WAVES == kWaves)
+      if (a.fused && n_active == 0 && s == 0) fused_empty<D, NREP>(a, g, b);
     if (a.direct && n_active == 0 && s == 0) {     // nothing attended: out = 0
       constexpr int Q4 = D / 4;
       for (int t = 0; t < TILES; ++t)
-        for (int idx = tid; idx < NREP * a.tpt * Q4; idx += kThreads) {
+        for (int idx = tid; idx < NREP * a.tpt * Q4; idx += THREADS) {
           const int h = idx / Q4, cqi = (pass * TILES + t) * a.tpt + h / NREP;
           if (cqi >= a.s_q) continue;
           const int64_t e = (((int64_t)b * a.s_q + cqi) * a.h_q + g * NREP + h % NREP) * D + (idx % Q4) * 4;
@@ -376,12 +382,12 @@ void split_kv_mfma(SplitArgs a) {
     int blk = w;
     load(ra, blk);
     while (true) {
-      int nb = blk + kWaves;
+      int nb = blk + WAVES;
       if (nb < nblk) load(rb, nb);
       step(ra, blk);
       if (nb >= nblk) break;
       blk = nb;
-      nb = blk + kWaves;
+      nb = blk + WAVES;
       if (nb < nblk) load(ra, nb);
       step(rb, blk);
       if (nb >= nblk) break;
@@ -398,8 +404,8 @@ void split_kv_mfma(SplitArgs a) {
   constexpr int OP = D + 4;                        // padded row (fewer bank conflicts)
   constexpr int Q4 = D / 4;
   const int cols = NREP * a.tpt;                   // columns in use (<= 16)
-  __shared__ float sm_m[kWaves][16], sm_l[kWaves][16];
-  __shared__ float sm_o[kWaves][16][OP];
+  __shared__ float sm_m[WAVES][16], sm_l[WAVES][16];
+  __shared__ float sm_o[WAVES][16][OP];
 #pragma unroll
   for (int t = 0; t < TILES; ++t) {
     // l: sum the 4 lane groups' partial sums (m is already shared by them).
@@ -417,17 +423,17 @@ void split_kv_mfma(SplitArgs a) {
         for (int nt = 0; nt < NT; ++nt) sm_o[w][n][NT * (4 * grp + r) + nt] = acc[t][nt][r];
     }
     __syncthreads();
-    for (int idx = tid; idx < cols * Q4; idx += kThreads) {
+    for (int idx = tid; idx < cols * Q4; idx += THREADS) {
       const int h = idx / Q4, d4 = (idx % Q4) * 4;      // h: column of the tile
       const int cqi = (pass * TILES + t) * a.tpt + h / NREP;
       if (cqi >= a.s_q) continue;
       float M = sm_m[0][h];
 #pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][h]);
+      for (int ww = 1; ww < WAVES; ++ww) M = fmaxf(M, sm_m[ww][h]);
       float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
       float L = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
+      for (int ww = 0; ww < WAVES; ++ww) {
         const float mw = sm_m[ww][h];
         const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);   // a wave with no block
         L += f * sm_l[ww][h];
@@ -451,7 +457,8 @@ void split_kv_mfma(SplitArgs a) {
       }
     }
   }
-  if (a.fused) fused_epilogue<D, NREP>(a, g, b, n_active);
+  if constexpr (WAVES == kWaves)
+    if (a.fused) fused_epilogue<D, NREP>(a, g, b, n_active);
 }
 
 }  // namespace gqa

@@ -110,8 +110,14 @@ int gqa_decode_attn(const void* q, const void* k_cache, const void* v_cache,
  *                    cache); NULL means the packed layout.
  *  in_dtype          GQA_DTYPE_BF16 or GQA_DTYPE_F32 (q, k_cache, v_cache).
  *  out_dtype         GQA_DTYPE_F32, or GQA_DTYPE_BF16 (rounded to nearest even).
- *  s_kv_hint         host-side upper bound of max_b S_b, or 0 if unknown. Only
- *                    the split heuristic uses it; the kernels read seq_lens.
+ *  s_kv_hint         host-side upper bound of max_b S_b, or 0 if unknown. The
+ *                    split heuristic uses it, and so does the choice of the
+ *                    matrix-core kernel's workgroup form (one wave per
+ *                    workgroup when every chunk would hold at most 128
+ *                    tokens and there are more than 2 chunks per compute
+ *                    unit); the kernels read seq_lens, so a wrong hint costs
+ *                    only speed. Different hints can give results that differ
+ *                    in fp32 rounding (another split count or form).
  *  workspace         device buffer of at least gqa_decode_workspace_bytes(B, h_q,
  *                    d_head, n) bytes, n being the split count that will be used
  *                    (n_splits if > 0, else gqa_decode_pick_splits(B, h_kv,

@@ -12,7 +12,8 @@
  * workspace, caller stream).
  *
  * Also checks, and fails with a message otherwise: gqa_decode_attn (default
- * stream, library workspace, same split count) gives the same bytes; an
+ * stream, library workspace, same split count, no length hint) gives the same
+ * bytes as gqa_decode_attn_ex without a hint; an
  * unsupported head size is refused on the host with GQA_ERR_UNSUPPORTED and a
  * message; gqa_decode_workspace_bytes is positive.
  */
@@ -109,15 +110,27 @@ int main(int argc, char** argv) {
     return 3;
   }
   HIP_OK(hipStreamSynchronize(st));
+  HIP_OK(hipMemcpy(out1, dout, nq * 4, hipMemcpyDeviceToHost));
+  /* without the hint, as the base entry point has none (a hint may choose another
+     workgroup form, whose results differ in rounding) */
+  r = gqa_decode_attn_ex(dq, dk, dv, (const int32_t*)dlens, NULL, dout, B, h_q, h_kv, d, scale, ns,
+                         GQA_DTYPE_BF16, GQA_DTYPE_F32, 0, dws, ws_bytes, st, 0);
+  if (r != GQA_OK) {
+    fprintf(stderr, "gqa_decode_attn_ex (no hint): %s (%s)\n", gqa_status_string(r), gqa_last_error());
+    return 3;
+  }
+  HIP_OK(hipStreamSynchronize(st));
   r = gqa_decode_attn(dq, dk, dv, (const int32_t*)dlens, dout2, B, h_q, h_kv, d, scale, ns);
   if (r != GQA_OK) {
     fprintf(stderr, "gqa_decode_attn: %s (%s)\n", gqa_status_string(r), gqa_last_error());
     return 3;
   }
   HIP_OK(hipDeviceSynchronize());
-  HIP_OK(hipMemcpy(out1, dout, nq * 4, hipMemcpyDeviceToHost));
+  float* out3 = malloc(nq * 4);
+  if (!out3) return 1;
+  HIP_OK(hipMemcpy(out3, dout, nq * 4, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(out2, dout2, nq * 4, hipMemcpyDeviceToHost));
-  if (memcmp(out1, out2, nq * 4) != 0) {
+  if (memcmp(out3, out2, nq * 4) != 0) {
     fprintf(stderr, "gqa_decode_attn and gqa_decode_attn_ex differ\n");
     return 4;
   }
@@ -137,6 +150,6 @@ int main(int argc, char** argv) {
   printf("gqa_c_smoke: B=%d h_q=%d h_kv=%d d=%d n_splits=%d ok\n", B, h_q, h_kv, d, ns);
   HIP_OK(hipStreamDestroy(st));
   hipFree(dq); hipFree(dk); hipFree(dv); hipFree(dlens); hipFree(dout); hipFree(dout2); hipFree(dws);
-  free(q); free(k); free(v); free(lens); free(out1); free(out2);
+  free(q); free(k); free(v); free(lens); free(out1); free(out2); free(out3);
   return 0;
 }

@@ -286,3 +286,39 @@ def test_many_sequences_packed_scan(B):
                                      s_kv_hint=int(lens.max()), kv_token_offsets=offs)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(got, exp.float().cpu().numpy().astype(np.float64))
+
+
+# One-wave workgroups need, by the length hint, chunks of at most 128 tokens
+# and more than two chunks (B * h_kv * n_splits) per compute unit: more than
+# 512 on a 256-CU GPU. The cases below have 640 or more.
+ONE_WAVE_UNITS = 512
+
+
+@pytest.mark.parametrize("n_rep,d", [(1, 128), (8, 128), (4, 64), (16, 64)])
+def test_short_sequences_one_wave(n_rep, d):
+    """Chunks of at most 128 tokens, many of them: one-wave workgroups.
+    Lengths 0..128 around the 32-token block edges, one chunk per sequence
+    (written out directly) and forced splits (merged), fp32 and bf16 output."""
+    lens = [0, 1, 2, 15, 16, 17, 31, 32, 33, 47, 63, 64, 65, 96, 127, 128] * 5
+    h_kv = 8
+    inp = workloads.custom(f"short{n_rep}_{d}", B=len(lens), h_q=h_kv * n_rep, h_kv=h_kv, d=d, seq_lens=lens,
+                           seed=100 + n_rep + d)
+    ref = ref_of(inp)
+    for ns in (0, 1, 3):
+        got, used = run_gpu(inp, n_splits=ns)
+        assert len(lens) * h_kv * used > ONE_WAVE_UNITS
+        report(f"short n_rep={n_rep} d={d} ns={ns}", max_err(got, ref), used, TOL_F32)
+    got, used = run_gpu(inp, out_dtype="bf16")
+    report(f"short n_rep={n_rep} d={d} bf16 out", max_err(got, ref), used, TOL_BF16)
+
+
+@pytest.mark.parametrize("ns", [0, 4])
+def test_one_wave_with_a_hint_below_the_lengths(ns):
+    """A hint of 32 tokens picks one-wave workgroups; the real chunks are far
+    longer (up to 3000 tokens), which that form walks block by block: slower,
+    same result."""
+    lens = [3000, 65, 0, 1000, 32] * 14
+    inp = workloads.custom("onewave_hint", B=len(lens), h_q=64, h_kv=8, d=128, seq_lens=lens, seed=111)
+    got, used = run_gpu(inp, n_splits=ns, hint=32)
+    assert len(lens) * 8 * used > ONE_WAVE_UNITS
+    report(f"one-wave hint 32 ns={ns}", max_err(got, ref_of(inp)), used, TOL_F32)

@@ -153,3 +153,11 @@ def test_step_graph_loop():
         assert err <= TOL_F32
     np.testing.assert_array_equal(bits(kc), kc_ref)
     np.testing.assert_array_equal(bits(vc), vc_ref)
+
+
+@pytest.mark.parametrize("explicit,ns", [(False, 0), (True, 0), (False, 2)])
+def test_step_short_capacity_one_wave(explicit, ns):
+    """A capacity of 100 tokens puts every chunk at 128 tokens or fewer, and 70
+    sequences x 8 kv heads give more than two chunks per compute unit: the
+    step and the two-call path both take one-wave workgroups (same bits)."""
+    run_case([0, 1, 31, 32, 63, 99, 100] * 10, 100, 64, 8, 128, explicit, n_splits=ns, seed=6)
