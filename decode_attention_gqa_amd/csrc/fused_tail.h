@@ -11,10 +11,15 @@
 // The compare-and-swap loop ends: every retry means another workgroup's swap
 // succeeded, and at most n_active workgroups arrive.
 //
-// Ordering: every thread fences its own triplet stores at agent scope before
-// the workgroup's arrival is counted (release), and the last workgroup fences
-// again before it reads the other workgroups' triplets (acquire). No
-// workgroup waits for another, so the grid always drains.
+// Ordering: every thread waits until its own triplet stores are complete
+// (accepted by the L2 of its XCD), the workgroup meets at a barrier, and one
+// thread then makes them visible to the whole device with a single
+// agent-scope release - one L2 write-back per workgroup instead of one per
+// thread - before it counts the arrival. The thread that finds its
+// workgroup last acquires at agent scope before a second barrier, and every
+// thread of that workgroup acquires again before it reads the other
+// workgroups' triplets. No workgroup waits for another, so the grid always
+// drains.
 #pragma once
 
 #include "gqa_common.h"
@@ -107,24 +112,31 @@ __device__ __forceinline__ void merge_group(const SplitArgs& a, int b, int g, in
   }
 }
 
+// s_waitcnt immediate that waits for every outstanding vector memory
+// operation of the wave (vmcnt = 0) and leaves the other counters alone.
+constexpr int kWaitVmem = 0x0F70;
+
 // Called by every thread of a split workgroup after its triplets are stored.
 template <int D, int NREP>
 __device__ __forceinline__ void fused_epilogue(const SplitArgs& a, int g, int b, int n_active) {
   __shared__ int s_last;
-  __threadfence();                                   // release this thread's triplet stores
+  __builtin_amdgcn_s_waitcnt(kWaitVmem);             // this thread's triplet stores are in L2
   __syncthreads();
   unsigned long long* cnt = a.counters + (int64_t)b * a.h_kv + g;
   if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // the workgroup's stores, device-wide
     unsigned long long old = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), nw;
     do {
       nw = ((old >> 16) == a.tag) ? old + 1 : ((a.tag << 16) | 1ull);
     } while (!__hip_atomic_compare_exchange_strong(cnt, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT));
-    s_last = (int)(nw & 0xFFFFull) == n_active;
+    const int last = (int)(nw & 0xFFFFull) == n_active;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_last = last;
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();                                   // acquire the other workgroups' triplets
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // before this thread reads other workgroups' triplets
   if (a.out_bf16)
     merge_group<D, NREP, __bf16>(a, b, g, n_active);
   else
