@@ -371,6 +371,30 @@ def main() -> int:
         log(f"[bench] timed {args.steps} calls")
         sec_per_call = (t1 - t0) / args.steps
 
+        # ---- spread (outside the timed region): a graph of G calls replayed
+        # N times, each replay between HIP events on the launch stream.
+        spread = None
+        if not args.eager:
+            G, N = 20, 21
+            gs = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gs, stream=stream):
+                for i in range(G):
+                    call(i)
+            gs.replay()
+            torch.cuda.synchronize()
+            per = []
+            for _ in range(N):
+                a, b = hip.event(), hip.event()
+                hip.lib.hipEventRecord(a, ctypes.c_void_p(stream.cuda_stream))
+                gs.replay()
+                hip.lib.hipEventRecord(b, ctypes.c_void_p(stream.cuda_stream))
+                per.append(hip.elapsed_ms(a, b) * 1e3 / G)
+                hip.lib.hipEventDestroy(a)
+                hip.lib.hipEventDestroy(b)
+            per.sort()
+            spread = {"p10": per[N // 10], "p50": per[N // 2], "p90": per[(9 * N) // 10],
+                      "what": f"us per call over {N} replays of a graph of {G} calls (HIP events)"}
+
         # ---- the split kernel alone: a HIP graph of K split-only launches
         # (gqa_decode_partial) over the same rotating inputs, with HIP events
         # recorded on the launch stream around one replay.
@@ -453,6 +477,11 @@ def main() -> int:
             "kernel_us": split_us,
         },
         "kernel_source_hash": src_hash,
+        "us_per_call_spread": spread,
+        "device": {"name": torch.cuda.get_device_name(dev),
+                   "arch": getattr(torch.cuda.get_device_properties(dev), "gcnArchName", None),
+                   "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
+                   "hip": torch.version.hip},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
