@@ -1,17 +1,17 @@
-#include <algorithm>
-#include <type_traits>
 // Host side of the decode attention library: argument checks, split
 // heuristic, workspace, kernel selection and launches. C ABI in gqa_decode.h.
 #include "gqa_decode.h"
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
-#include <atomic>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "gqa_common.h"
@@ -43,8 +43,7 @@ constexpr int kMinChunk = 128;       // tokens: one 32-token block per wave of a
 // How a split kernel wants its grid: resident workgroups per CU, rounds of
 // those slots the longest sequence's chunks fill (one sequence / a batch, where
 // only the longest length is known and more rounds keep it balanced), and the
-// longest chunk in tokens. Measured per kernel (70B shapes; see the sweeps in
-// the design notes).
+// longest chunk in tokens. Measured per kernel at 70B shapes.
 struct SplitPolicy {
   int wg_per_cu;
   int rounds_one, rounds_many;
@@ -322,6 +321,7 @@ namespace {
 int check_shape(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_hint) {
   if (B < 1 || h_q < 1 || h_kv < 1) return fail(GQA_ERR_INVALID_ARG, "B, h_q, h_kv must be >= 1");
   if (B > 65535 || h_kv > 65535) return fail(GQA_ERR_INVALID_ARG, "B and h_kv must be <= 65535");
+  if ((int64_t)B * h_q > INT32_MAX) return fail(GQA_ERR_INVALID_ARG, "B * h_q must be < 2^31");
   if (h_q % h_kv) return fail(GQA_ERR_INVALID_ARG, "h_q (%d) is not a multiple of h_kv (%d)", h_q, h_kv);
   if (!valid_nrep(h_q / h_kv))
     return fail(GQA_ERR_UNSUPPORTED, "h_q / h_kv = %d not in {1, 2, 4, 8, 16}", h_q / h_kv);
@@ -549,6 +549,7 @@ int gqa_decode_attn_multi(const void* q, const void* k_cache, const void* v_cach
   query_tiles(S_q, h_q / h_kv, &tpt, &qtiles, &tpw, &passes);
   if ((int64_t)B * passes > 65535)
     return fail(GQA_ERR_INVALID_ARG, "B * ceil(query tiles / 2) must be <= 65535");
+  if ((int64_t)B * S_q * h_q > INT32_MAX) return fail(GQA_ERR_INVALID_ARG, "B * S_q * h_q must be < 2^31");
   const size_t qo = (size_t)B * S_q * h_q * d_head;
   if ((st = check_out(out, out_dtype, qo))) return st;
   const size_t out_el = out_dtype == GQA_DTYPE_BF16 ? 2 : 4;

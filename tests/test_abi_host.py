@@ -76,6 +76,7 @@ def call(gqa, **kw):
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(lens=None), -1), (dict(out=None), -1),
     (dict(B=0), -1), (dict(B=-3), -1), (dict(h_q=0), -1), (dict(h_kv=0), -1), (dict(B=70000), -1),
     (dict(h_q=60, h_kv=8), -1),                       # not a multiple
+    (dict(B=65535, h_q=65535 * 16, h_kv=65535), -1),  # B * h_q rows past 2^31
     (dict(h_q=24, h_kv=8), -2),                       # n_rep = 3
     (dict(h_q=256, h_kv=8), -2),                      # n_rep = 32
     (dict(d=96), -2), (dict(d=256), -2),
@@ -199,6 +200,9 @@ def test_multi_token_checks_on_the_host(gqa):
         8, kw.get("d", 128), 0.088, 0, 0, 0, None, 0, None)
     assert f(S_q=0) == -1
     assert f(S_q=65) == -1
+    # B * S_q * h_q rows past 2^31 (each factor and B * passes within its own limit)
+    assert L_.gqa_decode_attn_multi(Q, K, V, L, None, O, 2047, 64, 16 * 2048, 2048, 128, 0.088, 0, 0, 0,
+                                    None, 0, None) == -1
     assert f(q=None) == -1
     assert f(d=80) == -2
     assert f(h_q=48) == -2
