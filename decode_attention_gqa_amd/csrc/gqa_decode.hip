@@ -124,23 +124,26 @@ WsLayout ws_layout(int B, int h_q, int d, int n) {
 // with one scan launch instead of inside every split workgroup.
 constexpr int kScanMinBatch = 256;
 // Chunks of at most this many tokens (by the length hint) run in one-wave
-// workgroups: a 4-wave workgroup gives each wave 32-token blocks of the
-// chunk, so shorter chunks leave waves without work, and one-wave
-// workgroups fit four times as many chunks on a CU (measured faster up to
-// 128 tokens).
+// workgroups when there are enough of them: a 4-wave workgroup gives each
+// wave 32-token blocks of the chunk, so shorter chunks leave waves without
+// work, and one-wave workgroups fit four times as many chunks on a CU
+// (measured faster up to 128 tokens).
 constexpr int kOneWaveMaxTokens = 128;
 size_t ws_bytes(int B, int h_q, int d, int n) { return ws_layout(B, h_q, d, n).total; }
 
 // ---------------------------------------------------------------- launches
+// Workgroup form of the matrix-core split kernel.
+enum class Form { kFourWave, kOneWave };
+
 template <int D, int NREP>
-hipError_t launch_split(bool bf16, bool valu, bool one_wave, dim3 grid, hipStream_t st, const gqa::SplitArgs& a) {
+hipError_t launch_split(bool bf16, bool valu, Form form, dim3 grid, hipStream_t st, const gqa::SplitArgs& a) {
   if (!bf16) {
     hipLaunchKernelGGL((gqa::split_kv_valu<float, D, NREP>), grid, dim3(gqa::kThreads), 0, st, a);
   } else if (valu) {
     hipLaunchKernelGGL((gqa::split_kv_valu<__bf16, D, NREP>), grid, dim3(gqa::kThreads), 0, st, a);
   } else if (a.qtiles > a.passes) {               // two column tiles per workgroup
     hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, false, 2>), grid, dim3(gqa::kThreads), 0, st, a);
-  } else if (one_wave) {
+  } else if (form == Form::kOneWave) {
     hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, false, 1, 1>), grid, dim3(64), 0, st, a);
   } else {
     hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP>), grid, dim3(gqa::kThreads), 0, st, a);
@@ -149,33 +152,33 @@ hipError_t launch_split(bool bf16, bool valu, bool one_wave, dim3 grid, hipStrea
 }
 
 template <int D>
-hipError_t launch_split_nrep(int nrep, bool bf16, bool valu, bool one_wave, dim3 grid, hipStream_t st,
+hipError_t launch_split_nrep(int nrep, bool bf16, bool valu, Form form, dim3 grid, hipStream_t st,
                              const gqa::SplitArgs& a) {
   switch (nrep) {
-    case 1: return launch_split<D, 1>(bf16, valu, one_wave, grid, st, a);
-    case 2: return launch_split<D, 2>(bf16, valu, one_wave, grid, st, a);
-    case 4: return launch_split<D, 4>(bf16, valu, one_wave, grid, st, a);
-    case 8: return launch_split<D, 8>(bf16, valu, one_wave, grid, st, a);
-    default: return launch_split<D, 16>(bf16, valu, one_wave, grid, st, a);
+    case 1: return launch_split<D, 1>(bf16, valu, form, grid, st, a);
+    case 2: return launch_split<D, 2>(bf16, valu, form, grid, st, a);
+    case 4: return launch_split<D, 4>(bf16, valu, form, grid, st, a);
+    case 8: return launch_split<D, 8>(bf16, valu, form, grid, st, a);
+    default: return launch_split<D, 16>(bf16, valu, form, grid, st, a);
   }
 }
 
 template <int D, int NREP>
-void launch_append_form(bool one_wave, dim3 grid, hipStream_t st, const gqa::SplitArgs& a) {
-  if (one_wave)
+void launch_append_form(Form form, dim3 grid, hipStream_t st, const gqa::SplitArgs& a) {
+  if (form == Form::kOneWave)
     hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, true, 1, 1>), grid, dim3(64), 0, st, a);
   else
     hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, true>), grid, dim3(gqa::kThreads), 0, st, a);
 }
 
 template <int D>
-hipError_t launch_split_append(int nrep, bool one_wave, dim3 grid, hipStream_t st, const gqa::SplitArgs& a) {
+hipError_t launch_split_append(int nrep, Form form, dim3 grid, hipStream_t st, const gqa::SplitArgs& a) {
   switch (nrep) {
-    case 1: launch_append_form<D, 1>(one_wave, grid, st, a); break;
-    case 2: launch_append_form<D, 2>(one_wave, grid, st, a); break;
-    case 4: launch_append_form<D, 4>(one_wave, grid, st, a); break;
-    case 8: launch_append_form<D, 8>(one_wave, grid, st, a); break;
-    default: launch_append_form<D, 16>(one_wave, grid, st, a); break;
+    case 1: launch_append_form<D, 1>(form, grid, st, a); break;
+    case 2: launch_append_form<D, 2>(form, grid, st, a); break;
+    case 4: launch_append_form<D, 4>(form, grid, st, a); break;
+    case 8: launch_append_form<D, 8>(form, grid, st, a); break;
+    default: launch_append_form<D, 16>(form, grid, st, a); break;
   }
   return hipGetLastError();
 }
@@ -401,18 +404,21 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
   return GQA_OK;
 }
 
-// The matrix-core split kernel's workgroup form for a plan: one wave per
-// workgroup when the length hint puts every chunk at kOneWaveMaxTokens or
-// fewer and the grid is more than one round of 4-wave workgroups (two per
-// CU); with one round or less, four waves per chunk finish it sooner. A
-// wrong hint changes only the speed: both forms take any length.
-bool one_wave_form(const Plan& pl, int B, int h_kv) {
-  if (pl.hint <= 0) return false;
+// The matrix-core split kernel's workgroup form for a plan (one query tile
+// per workgroup): one wave per workgroup when the length hint puts every
+// chunk at kOneWaveMaxTokens or fewer and the grid is more than one round
+// of 4-wave workgroups (two per CU; with one round or less, four waves per
+// chunk finish it sooner). A wrong hint changes only the speed: both forms
+// take any length. The one-wave form sums a chunk's blocks in another order,
+// so its results differ from the 4-wave form's in rounding.
+Form split_form(const Plan& pl, int B, int h_kv) {
+  if (pl.hint <= 0) return Form::kFourWave;
   const int64_t per_chunk = (pl.hint + pl.ns - 1) / pl.ns;
-  if (std::min<int64_t>(pl.hint, std::max<int64_t>(per_chunk, pl.min_chunk)) > kOneWaveMaxTokens) return false;
+  if (std::min<int64_t>(pl.hint, std::max<int64_t>(per_chunk, pl.min_chunk)) > kOneWaveMaxTokens)
+    return Form::kFourWave;
   int cus = 0;
-  if (device_cus(&cus) != GQA_OK) return false;
-  return (int64_t)pl.ns * h_kv * B > 2 * (int64_t)cus;
+  if (device_cus(&cus) != GQA_OK) return Form::kFourWave;
+  return (int64_t)pl.ns * h_kv * B > 2 * (int64_t)cus ? Form::kOneWave : Form::kFourWave;
 }
 
 // direct: the caller merges nothing afterwards; with one chunk per sequence
@@ -447,9 +453,13 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
   hipError_t e;
   if (g_ev_before && (e = hipEventRecord(g_ev_before, stream)) != hipSuccess)
     return fail(GQA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-  const bool one_wave = mfma && !fused && s_q == 1 && one_wave_form(pl, B, h_kv);
-  e = d_head == 128 ? launch_split_nrep<128>(nrep, bf16, valu, one_wave, grid, stream, sa)
-                    : launch_split_nrep<64>(nrep, bf16, valu, one_wave, grid, stream, sa);
+  Form form = Form::kFourWave;
+  if (mfma && s_q == 1) {
+    form = split_form(pl, B, h_kv);
+    if (fused && form == Form::kOneWave) form = Form::kFourWave;   // the single-launch tail needs 4 waves
+  }
+  e = d_head == 128 ? launch_split_nrep<128>(nrep, bf16, valu, form, grid, stream, sa)
+                    : launch_split_nrep<64>(nrep, bf16, valu, form, grid, stream, sa);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
   if (g_ev_after && (e = hipEventRecord(g_ev_after, stream)) != hipSuccess)
     return fail(GQA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
@@ -629,9 +639,9 @@ int gqa_decode_step(const void* q, const void* k_new, const void* v_new, void* k
                     k_new, v_new, seq_lens_out, (int)capacity, pl.ns == 1 ? 1 : 0};
   const dim3 grid = gqa::split_grid(pl.ns, h_kv, B);
   const int nrep = h_q / h_kv;
-  const bool one_wave = one_wave_form(pl, B, h_kv);   // the same form as gqa_decode_attn_ex with this hint
-  hipError_t e = d_head == 128 ? launch_split_append<128>(nrep, one_wave, grid, stream, sa)
-                               : launch_split_append<64>(nrep, one_wave, grid, stream, sa);
+  const Form form = split_form(pl, B, h_kv);       // the same form as gqa_decode_attn_ex with this hint
+  hipError_t e = d_head == 128 ? launch_split_append<128>(nrep, form, grid, stream, sa)
+                               : launch_split_append<64>(nrep, form, grid, stream, sa);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
   if (sa.direct) return GQA_OK;                    // one chunk per sequence: out is written
   return run_merge(pl, seq_lens_out, out, B, h_q, d_head, out_dtype, stream);
