@@ -198,12 +198,21 @@ hipError_t launch_merge_t(int rows, hipStream_t st, const gqa::MergeArgs& a) {
     else packed(std::integral_constant<int, 8>{});
     return hipGetLastError();
   }
-  // One row per workgroup; chunks per slot in the first round: one round
-  // covers up to 32 * U chunks.
+  // Up to 32 chunks: one wave per 32-column slice, D / 32 waves per row
+  // (measured faster than the workgroup-per-slice merge up to 32 chunks,
+  // slower at 64).
+  if (a.n_splits <= 32) {
+    const dim3 g((unsigned)rows), blk(64 * (D / 32));
+    if (a.n_splits <= 16)
+      hipLaunchKernelGGL((gqa::merge_wave<D, TO, 2>), g, blk, 0, st, a);
+    else
+      hipLaunchKernelGGL((gqa::merge_wave<D, TO, 4>), g, blk, 0, st, a);
+    return hipGetLastError();
+  }
+  // One workgroup per row and 32-column slice; chunks per slot in the first
+  // round: one round covers up to 32 * U chunks.
   const dim3 grid((unsigned)rows, D / 32);
-  if (a.n_splits <= 32)
-    hipLaunchKernelGGL((gqa::merge_splits<D, TO, 1>), grid, dim3(256), 0, st, a);
-  else if (a.n_splits <= 64)
+  if (a.n_splits <= 64)
     hipLaunchKernelGGL((gqa::merge_splits<D, TO, 2>), grid, dim3(256), 0, st, a);
   else if (a.n_splits <= 128)
     hipLaunchKernelGGL((gqa::merge_splits<D, TO, 4>), grid, dim3(256), 0, st, a);

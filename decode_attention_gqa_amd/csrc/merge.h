@@ -8,7 +8,12 @@
 // Every chunk below n_active is non-empty, so M is finite and l > 0 unless
 // the sequence is empty.
 //
-// Grid (row, 32-column slice of d). A workgroup's 256 threads form 32 chunk
+// Three kernels by chunks per row: merge_rows (up to 8; several rows per
+// workgroup), merge_wave (9 to 32; one wave per 32-column slice) and
+// merge_splits (more). Each takes a row's global max first, then sums the
+// weighted chunks (the order of the additions differs between them).
+//
+// merge_splits: grid (row, 32-column slice of d). A workgroup's 256 threads form 32 chunk
 // slots of 8 lanes (a float4 of the slice each); slot j takes chunks j,
 // j + 32, ... U of them per round, with every load of a round issued before
 // any is used, so up to 32 * U chunks cost one memory latency. The global
@@ -135,6 +140,68 @@ __global__ __launch_bounds__(256) void merge_splits(MergeArgs a) {
       TO* out = static_cast<TO*>(a.out) + (int64_t)bh * D + d0;
       store4<TO>(out + 4 * tid, make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv));
     }
+  }
+}
+
+// The same merge for 9 to 32 chunks per row, one wave per 32-column slice
+// of a row: slot j of the wave (8 lanes, a float4 each) holds chunks j,
+// j + 8, ..., U of them, all loaded at once; the max and the sums over the
+// 8 slots are lane butterflies (xor 8, 16, 32), so no LDS step and no
+// barrier. Grid: one workgroup of D / 32 waves per row.
+template <int D, typename TO, int U>
+__global__ __launch_bounds__(64 * (D / 32)) void merge_wave(MergeArgs a) {
+  constexpr int LPS = 8, SLOTS = 64 / LPS;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slot = lane / LPS, q = lane % LPS;
+  const int bh = blockIdx.x;
+  const int b = bh / (a.h_q * a.s_q);
+  const int d0 = wave * 4 * LPS;
+  const int64_t ps = a.part_stride;
+  const float2* ml = a.ws_ml + (int64_t)bh * a.row_stride;
+  const float* o = a.ws_o + (int64_t)bh * a.row_stride * D + d0 + 4 * q;
+  // Clamped indices: every load is in bounds and issued before the wait for
+  // seq_lens; chunks at or past n_active are selected out before any use.
+  float2 mv[U];
+  float4 ov[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) mv[u] = ml[min(u * SLOTS + slot, a.n_splits - 1) * ps];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    ov[u] = *reinterpret_cast<const float4*>(o + min(u * SLOTS + slot, a.n_splits - 1) * ps * D);
+  __builtin_amdgcn_sched_barrier(0);
+  int c, n_active = a.n_splits;
+  if (a.seq_lens) chunking(a.seq_lens[b], a.n_splits, a.min_chunk, c, n_active);
+  float M = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (u * SLOTS + slot < n_active) M = fmaxf(M, mv[u].x);
+  M = max_x32(max_x16(max_x8(M)));
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (u * SLOTS + slot < n_active) {
+      const float w = rescale(mv[u].x, M);   // a causal column can have empty chunks (m = -inf)
+      acc.x += w * ov[u].x;
+      acc.y += w * ov[u].y;
+      acc.z += w * ov[u].z;
+      acc.w += w * ov[u].w;
+      L += w * mv[u].y;
+    }
+  }
+  acc.x = sum_x32(sum_x16(sum_x8(acc.x)));
+  acc.y = sum_x32(sum_x16(sum_x8(acc.y)));
+  acc.z = sum_x32(sum_x16(sum_x8(acc.z)));
+  acc.w = sum_x32(sum_x16(sum_x8(acc.w)));
+  L = sum_x32(sum_x16(sum_x8(L)));
+  if (slot != 0) return;
+  if (a.tri_ml) {                            // merged triplet, relative to M
+    if (q == 0 && wave == 0) a.tri_ml[bh] = make_float2(M, L);
+    *reinterpret_cast<float4*>(a.tri_o + (int64_t)bh * D + d0 + 4 * q) = acc;
+  } else {
+    const float inv = L > 0.f ? 1.f / L : 0.f;   // L = 0 only when nothing was attended
+    store4<TO>(static_cast<TO*>(a.out) + (int64_t)bh * D + d0 + 4 * q,
+               make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv));
   }
 }
 
