@@ -74,7 +74,7 @@ def main():
     ap.add_argument("--cmd-fetch")
     ap.add_argument("--cmd-write")
     ap.add_argument("--split-key", default="gqa::split_kv_")
-    ap.add_argument("--merge-key", default="gqa::merge_splits")
+    ap.add_argument("--merge-key", default="gqa::merge_")
     ap.add_argument("--trace-only", metavar="NAME")
     ap.add_argument("--busy", help="a --pmc run of VALUBusy MfmaUtil SQ_INSTS_VALU SQ_INSTS_MFMA")
     ap.add_argument("--cmd-busy")
