@@ -1,0 +1,87 @@
+"""Randomised GPU parity: seeded draws over the whole argument space of
+gqa_decode_attn_ex (batch, head grouping, head size, lengths with empty
+sequences and block edges, packed or offset layout with unused gaps between
+sequences, split count, length hint below / at / above the lengths or none,
+input and output dtypes, the vector-ALU kernel, the single-launch form),
+each case checked against the fp64 oracle. The gaps of the offset layout
+hold NaN, so a read outside a sequence's rows would show in the output.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import TOL_BF16, TOL_F32, max_err, to_device
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 48
+
+
+def draw(i):
+    r = np.random.default_rng(5000 + i)
+    B = int(r.integers(1, 13))
+    h_kv = int(r.choice([1, 2, 4, 8]))
+    n_rep = int(r.choice([1, 2, 4, 8, 16]))
+    while h_kv * n_rep > 64:
+        h_kv //= 2
+    d = int(r.choice([64, 128]))
+    s_top = int(r.choice([40, 300, 3000, 9000]))
+    lens = r.integers(0, s_top + 1, size=B)
+    edges = [0, 1, 31, 32, 33, 127, 128, 129]
+    for b in range(B):
+        if r.random() < 0.3:
+            lens[b] = min(s_top, int(r.choice(edges)))
+    case = dict(B=B, h_kv=h_kv, h_q=h_kv * n_rep, d=d, lens=lens.astype(np.int32),
+                dtype="f32" if r.random() < 0.15 else "bf16",
+                offsets=bool(r.random() < 0.4),
+                ns=int(r.choice([0, 0, 0, 1, 2, 5, 17, 64, 200])),
+                hint=str(r.choice(["exact", "exact", "none", "below", "above"])),
+                out="bf16" if r.random() < 0.25 else "f32",
+                valu=bool(r.random() < 0.2), fused=bool(r.random() < 0.15), seed=5000 + i)
+    return case
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_case(i):
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    c = draw(i)
+    lens = c["lens"]
+    s_max = int(lens.max())
+    hint = {"exact": s_max, "none": 0, "below": s_max // 3, "above": 4 * s_max + 1}[c["hint"]]
+    print(f"[case {i}] B={c['B']} h_q={c['h_q']} h_kv={c['h_kv']} d={c['d']} lens={lens.tolist()} "
+          f"dtype={c['dtype']} offsets={c['offsets']} ns={c['ns']} hint={hint} out={c['out']} "
+          f"valu={c['valu']} fused={c['fused']}", flush=True)
+    inp = workloads.custom(f"random{i}", B=c["B"], h_q=c["h_q"], h_kv=c["h_kv"], d=c["d"], seq_lens=lens,
+                           dtype=c["dtype"], seed=c["seed"])
+    ref = oracle.attend(inp.q, inp.k, inp.v, inp.seq_lens, inp.scale, c["h_kv"], dtype=c["dtype"])
+    q, k, v, dl = to_device(inp)
+    offs = None
+    if c["offsets"]:
+        # sequences in reverse order, each followed by a gap of NaN rows
+        r = np.random.default_rng(c["seed"] + 1)
+        gaps = r.integers(0, 50, size=c["B"])
+        packed = np.concatenate([[0], np.cumsum(lens[:-1])]).astype(np.int64)
+        order = list(range(c["B"]))[::-1]
+        start, pos = np.zeros(c["B"], dtype=np.int64), 0
+        for b in order:
+            start[b] = pos
+            pos += int(lens[b]) + int(gaps[b])
+        kp = torch.full((max(pos, 1), c["h_kv"], c["d"]), float("nan"), dtype=k.dtype, device="cuda")
+        vp = torch.full_like(kp, float("nan"))
+        for b in range(c["B"]):
+            n = int(lens[b])
+            kp[start[b]:start[b] + n] = k[packed[b]:packed[b] + n]
+            vp[start[b]:start[b] + n] = v[packed[b]:packed[b] + n]
+        k, v = kp, vp
+        offs = torch.from_numpy(start).cuda()
+    odt = torch.bfloat16 if c["out"] == "bf16" else torch.float32
+    out = gqa.gqa_decode_attn_ex(q, k, v, dl, scale=float(inp.scale), n_splits=c["ns"], out_dtype=odt,
+                                 s_kv_hint=hint, kv_token_offsets=offs, valu=c["valu"], fused=c["fused"])
+    torch.cuda.synchronize()
+    err = max_err(out.float().cpu().numpy().astype(np.float64), ref)
+    tol = TOL_BF16 if c["out"] == "bf16" else TOL_F32
+    print(f"[case {i}] max_abs_err={err:.3e} tol={tol:.1e}", flush=True)
+    assert err <= tol
