@@ -85,3 +85,95 @@ def test_random_case(i):
     tol = TOL_BF16 if c["out"] == "bf16" else TOL_F32
     print(f"[case {i}] max_abs_err={err:.3e} tol={tol:.1e}", flush=True)
     assert err <= tol
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_multi_token_case(i):
+    """gqa_decode_attn_multi on seeded draws: S_q in [1, 64] (one or two
+    column tiles per workgroup), lengths shorter than S_q included, split
+    count and hint varied; against oracle.attend_multi."""
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    r = np.random.default_rng(7000 + i)
+    B = int(r.integers(1, 6))
+    h_kv = int(r.choice([1, 2, 8]))
+    n_rep = int(r.choice([1, 4, 8, 16]))
+    while h_kv * n_rep > 64:
+        h_kv //= 2
+    h_q, d = h_kv * n_rep, int(r.choice([64, 128]))
+    S_q = int(r.choice([1, 2, 3, 5, 8, 16, 33, 64]))
+    lens = r.integers(0, int(r.choice([50, 600, 4000])) + 1, size=B).astype(np.int32)
+    ns = int(r.choice([0, 0, 1, 3, 40]))
+    hint = int(lens.max()) if r.random() < 0.7 else 0
+    out_bf16 = bool(r.random() < 0.25)
+    print(f"[multi case {i}] B={B} S_q={S_q} h_q={h_q} h_kv={h_kv} d={d} lens={lens.tolist()} ns={ns} "
+          f"hint={hint} out={'bf16' if out_bf16 else 'f32'}", flush=True)
+    inp = workloads.custom(f"rmulti{i}", B=B, h_q=h_q, h_kv=h_kv, d=d, seq_lens=lens, seed=7000 + i)
+    qm = workloads.normals(7000 + i, 9, B * S_q * h_q * d).reshape(B, S_q, h_q, d)
+    ref = oracle.attend_multi(qm, inp.k, inp.v, inp.seq_lens, inp.scale, h_kv, dtype="bf16")
+    _, k, v, dl = to_device(inp)
+    q = torch.from_numpy(np.ascontiguousarray(qm).view(np.int16)).cuda().view(torch.bfloat16)
+    out = gqa.gqa_decode_attn_multi(q, k, v, dl, scale=float(inp.scale), n_splits=ns, s_kv_hint=hint,
+                                    out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    torch.cuda.synchronize()
+    err = max_err(out.float().cpu().numpy().astype(np.float64), ref)
+    tol = TOL_BF16 if out_bf16 else TOL_F32
+    print(f"[multi case {i}] max_abs_err={err:.3e} tol={tol:.1e}", flush=True)
+    assert err <= tol
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_decode_step_case(i):
+    """gqa_decode_step on seeded draws (lengths from empty to full capacity,
+    padded or explicit offsets, split counts): the cache and new lengths equal
+    oracle.kv_append's bit for bit, the output the oracle's attention over the
+    grown cache within tolerance."""
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    r = np.random.default_rng(8000 + i)
+    B = int(r.integers(1, 9))
+    h_kv = int(r.choice([1, 2, 8]))
+    n_rep = int(r.choice([1, 2, 8, 16]))
+    while h_kv * n_rep > 64:
+        h_kv //= 2
+    h_q, d = h_kv * n_rep, int(r.choice([64, 128]))
+    cap = int(r.choice([40, 200, 2048]))
+    lens = r.integers(0, cap + 1, size=B).astype(np.int32)
+    lens[r.integers(0, B)] = cap if r.random() < 0.3 else lens[0]
+    explicit = bool(r.random() < 0.5)
+    ns = int(r.choice([0, 0, 1, 7]))
+    print(f"[step case {i}] B={B} h_q={h_q} h_kv={h_kv} d={d} cap={cap} lens={lens.tolist()} "
+          f"explicit={explicit} ns={ns}", flush=True)
+    T = B * cap + (5 if explicit else 0)
+    k0 = workloads.normals(8000 + i, 1, T * h_kv * d).reshape(T, h_kv, d)
+    v0 = workloads.normals(8000 + i, 2, T * h_kv * d).reshape(T, h_kv, d)
+    kn = workloads.normals(8000 + i, 3, B * h_kv * d).reshape(B, 1, h_kv, d)
+    vn = workloads.normals(8000 + i, 4, B * h_kv * d).reshape(B, 1, h_kv, d)
+    q = workloads.normals(8000 + i, 5, B * h_q * d).reshape(B, h_q, d)
+    offs = (np.arange(B)[::-1] * cap + 5).astype(np.int64) if explicit else None
+    kc_ref, vc_ref, lens_ref = oracle.kv_append(k0, v0, kn, vn, lens, cap, offs)
+    ref = np.zeros((B, h_q, d))
+    scale = np.float32(d ** -0.5)
+    for b in range(B):
+        o = int(offs[b]) if explicit else b * cap
+        rows = slice(o, o + int(lens_ref[b]))
+        ref[b] = oracle.attend(q[b:b + 1], kc_ref[rows], vc_ref[rows], lens_ref[b:b + 1], scale, h_kv,
+                               dtype="bf16")[0]
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    kc, vc = dev(k0), dev(v0)
+    lens_out = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    out = gqa.gqa_decode_step(dev(q), dev(kn), dev(vn), kc, vc, torch.from_numpy(lens).cuda(), lens_out,
+                              capacity=cap, kv_token_offsets=torch.from_numpy(offs).cuda() if explicit else None,
+                              n_splits=ns, scale=float(scale))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(lens_out.cpu().numpy(), lens_ref)
+    np.testing.assert_array_equal(kc.view(torch.int16).cpu().numpy().view(np.uint16), kc_ref)
+    np.testing.assert_array_equal(vc.view(torch.int16).cpu().numpy().view(np.uint16), vc_ref)
+    err = max_err(out.float().cpu().numpy().astype(np.float64), ref)
+    print(f"[step case {i}] max_abs_err={err:.3e}", flush=True)
+    assert err <= TOL_F32
