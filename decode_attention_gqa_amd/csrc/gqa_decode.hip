@@ -48,13 +48,27 @@ struct SplitPolicy {
   int wg_per_cu;
   int rounds_one, rounds_many;
   int64_t max_chunk;
+  bool eight_wave;              // a single sequence may take one 8-wave workgroup per CU
 };
 // One 16-column tile per workgroup, two workgroups per CU. A second round
 // hides each workgroup's start-up behind another's streaming.
-constexpr SplitPolicy kOneTile{2, 2, 4, 4096};
+constexpr SplitPolicy kOneTile{2, 2, 4, 4096, true};
+// The same for several query tokens in one tile (the 8-wave form serves one
+// query token only).
+constexpr SplitPolicy kOneTileMulti{2, 2, 4, 4096, false};
 // Two tiles per workgroup (multi-token decode), one workgroup per CU: one
 // round for a single sequence; chunks up to 16384 tokens.
-constexpr SplitPolicy kTwoTiles{1, 1, 4, 16384};
+constexpr SplitPolicy kTwoTiles{1, 1, 4, 16384, false};
+
+const SplitPolicy& split_policy(int s_q, int tiles_per_wg) {
+  return tiles_per_wg == 2 ? kTwoTiles : (s_q == 1 ? kOneTile : kOneTileMulti);
+}
+// A single sequence whose chunks, at one 8-wave workgroup per CU, hold this
+// many tokens (each wave one to four 32-token blocks) takes that form:
+// measured faster at 70B shapes from 8k to 32k tokens (and the 7B shape at
+// 8k), slower below (waves without a block) and above (two rounds of 4-wave
+// workgroups balance better).
+constexpr int64_t kEightWaveMinChunk = 256, kEightWaveMaxChunk = 1024;
 
 // Library-owned fallback workspace, one grow-only buffer per device.
 std::mutex g_ws_mu;
@@ -133,7 +147,7 @@ size_t ws_bytes(int B, int h_q, int d, int n) { return ws_layout(B, h_q, d, n).t
 
 // ---------------------------------------------------------------- launches
 // Workgroup form of the matrix-core split kernel.
-enum class Form { kFourWave, kOneWave };
+enum class Form { kFourWave, kOneWave, kEightWave };
 
 template <int D, int NREP>
 hipError_t launch_split(bool bf16, bool valu, Form form, dim3 grid, hipStream_t st, const gqa::SplitArgs& a) {
@@ -145,6 +159,8 @@ hipError_t launch_split(bool bf16, bool valu, Form form, dim3 grid, hipStream_t 
     hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, false, 2>), grid, dim3(gqa::kThreads), 0, st, a);
   } else if (form == Form::kOneWave) {
     hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, false, 1, 1>), grid, dim3(64), 0, st, a);
+  } else if (form == Form::kEightWave) {
+    hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, false, 1, 8>), grid, dim3(512), 0, st, a);
   } else {
     hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP>), grid, dim3(gqa::kThreads), 0, st, a);
   }
@@ -167,6 +183,8 @@ template <int D, int NREP>
 void launch_append_form(Form form, dim3 grid, hipStream_t st, const gqa::SplitArgs& a) {
   if (form == Form::kOneWave)
     hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, true, 1, 1>), grid, dim3(64), 0, st, a);
+  else if (form == Form::kEightWave)
+    hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, true, 1, 8>), grid, dim3(512), 0, st, a);
   else
     hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, true>), grid, dim3(gqa::kThreads), 0, st, a);
 }
@@ -242,6 +260,13 @@ int pick_splits_host(int B, int passes, int h_kv, int64_t s_kv_max, int num_cus,
   const int64_t units = (int64_t)B * passes * h_kv;
   const int64_t slots = (int64_t)p.wg_per_cu * num_cus;
   int64_t n = (slots + units - 1) / units;
+  if (s_kv_max > 0 && B == 1 && p.eight_wave) {
+    // ... one sequence that one round of 8-wave workgroups, one per CU,
+    // covers in chunks of kEightWaveMinChunk to kEightWaveMaxChunk tokens:
+    // that round (the split form picks the 8-wave kernel for it).
+    const int64_t n8 = num_cus / units;
+    if (n8 >= 1 && s_kv_max >= kEightWaveMinChunk * n8 && s_kv_max <= kEightWaveMaxChunk * n8) return (int)n8;
+  }
   if (s_kv_max > 0 && B == 1) {
     // ... one sequence: a whole number of such rounds, up to the policy's,
     // as long as chunks stay at least kMinChunk tokens (a length just past a
@@ -322,7 +347,7 @@ int gqa_decode_multi_splits(int B, int S_q, int h_q, int h_kv, int64_t s_kv_max,
   }
   int tpt, qtiles, tpw, passes;
   query_tiles(S_q, h_q / h_kv, &tpt, &qtiles, &tpw, &passes);
-  return pick_splits_host(B, passes, h_kv, s_kv_max, num_cus, tpw == 2 ? kTwoTiles : kOneTile);
+  return pick_splits_host(B, passes, h_kv, s_kv_max, num_cus, split_policy(S_q, tpw));
 }
 
 }  // extern "C"
@@ -392,7 +417,7 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
     if (st != GQA_OK) return st;
     int tpt, qtiles, tpw, passes;
     query_tiles(s_q, h_q / h_kv, &tpt, &qtiles, &tpw, &passes);
-    ns = pick_splits_host(B, passes, h_kv, s_kv_hint, num_cus, tpw == 2 ? kTwoTiles : kOneTile);
+    ns = pick_splits_host(B, passes, h_kv, s_kv_hint, num_cus, split_policy(s_q, tpw));
   }
   pl->ns = ns;
   pl->min_chunk = n_splits > 0 ? 1 : kMinChunk;
@@ -414,20 +439,28 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
 }
 
 // The matrix-core split kernel's workgroup form for a plan (one query tile
-// per workgroup): one wave per workgroup when the length hint puts every
-// chunk at kOneWaveMaxTokens or fewer and the grid is more than one round
-// of 4-wave workgroups (two per CU; with one round or less, four waves per
-// chunk finish it sooner). A wrong hint changes only the speed: both forms
-// take any length. The one-wave form sums a chunk's blocks in another order,
-// so its results differ from the 4-wave form's in rounding.
+// per workgroup), from the length hint:
+//  - one wave per workgroup when every chunk holds at most
+//    kOneWaveMaxTokens and the grid is more than one round of 4-wave
+//    workgroups (two per CU; with one round or less, four waves per chunk
+//    finish it sooner);
+//  - eight waves per workgroup for a single sequence whose chunks hold
+//    kEightWaveMinChunk to kEightWaveMaxChunk tokens and fit one workgroup
+//    per CU in one round;
+//  - else four waves.
+// A wrong hint changes only the speed: every form takes any length. The
+// forms give a chunk's blocks to their waves differently, so their results
+// differ in rounding.
 Form split_form(const Plan& pl, int B, int h_kv) {
   if (pl.hint <= 0) return Form::kFourWave;
   const int64_t per_chunk = (pl.hint + pl.ns - 1) / pl.ns;
-  if (std::min<int64_t>(pl.hint, std::max<int64_t>(per_chunk, pl.min_chunk)) > kOneWaveMaxTokens)
-    return Form::kFourWave;
+  const int64_t tok = std::min<int64_t>(pl.hint, std::max<int64_t>(per_chunk, pl.min_chunk));
   int cus = 0;
   if (device_cus(&cus) != GQA_OK) return Form::kFourWave;
-  return (int64_t)pl.ns * h_kv * B > 2 * (int64_t)cus ? Form::kOneWave : Form::kFourWave;
+  const int64_t wgs = (int64_t)pl.ns * h_kv * B;
+  if (tok <= kOneWaveMaxTokens) return wgs > 2 * (int64_t)cus ? Form::kOneWave : Form::kFourWave;
+  if (B == 1 && wgs <= cus && tok >= kEightWaveMinChunk && tok <= kEightWaveMaxChunk) return Form::kEightWave;
+  return Form::kFourWave;
 }
 
 // direct: the caller merges nothing afterwards; with one chunk per sequence
@@ -465,7 +498,7 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
   Form form = Form::kFourWave;
   if (mfma && s_q == 1) {
     form = split_form(pl, B, h_kv);
-    if (fused && form == Form::kOneWave) form = Form::kFourWave;   // the single-launch tail needs 4 waves
+    if (fused) form = Form::kFourWave;             // the single-launch tail is built for 4 waves
   }
   e = d_head == 128 ? launch_split_nrep<128>(nrep, bf16, valu, form, grid, stream, sa)
                     : launch_split_nrep<64>(nrep, bf16, valu, form, grid, stream, sa);

@@ -10,7 +10,9 @@
 // step that appends the new token on the way) and TILES = 2 (two 16-column
 // tiles of several query tokens per workgroup); see the kernel. WAVES = 1
 // gives one-wave workgroups for chunks of a few blocks (many short
-// sequences), where some of four waves would have nothing to read.
+// sequences), where some of four waves would have nothing to read; WAVES = 8
+// gives one workgroup per CU for a single sequence cut into one round of
+// chunks (half as many chunks to store and merge as two 4-wave workgroups).
 //
 // Per 32-token block, with 16x16x32 bf16 MFMAs:
 //   scores  S^T[t, h] = K[t, :] . Q[h, :]      A = K rows, B = Q^T (2 tiles x D/32 steps)
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(TILE
 void split_kv_mfma(SplitArgs a) {
   constexpr int KS = MfmaTile<D>::KS, NT = MfmaTile<D>::NT;
   constexpr int THREADS = 64 * WAVES;
-  static_assert(WAVES == kWaves || (WAVES == 1 && TILES == 1), "one-wave form: one column tile");
+  static_assert(WAVES == kWaves || ((WAVES == 1 || WAVES == 8) && TILES == 1), "1 or 8 waves: one column tile");
   static_assert(!APPEND || 2 * (D * 2 / 16) <= 64 * WAVES, "the new row's copy takes one thread per 16 bytes");
   static_assert(NREP >= 1 && NREP <= 16, "one 16-wide MFMA tile holds the query heads of a group");
   static_assert(TILES == 1 || (TILES == 2 && !APPEND), "two tiles serve multi-token decode only");
@@ -457,7 +459,7 @@ void split_kv_mfma(SplitArgs a) {
       }
     }
   }
-  if constexpr (WAVES == kWaves)
+  if constexpr (WAVES == kWaves)                   // the host runs the single-launch form with 4 waves only
     if (a.fused) fused_epilogue<D, NREP>(a, g, b, n_active);
 }
 

@@ -268,7 +268,10 @@ int gqa_decode_merge(const int32_t* seq_lens, const void* workspace, size_t work
  * every compute unit has work at B = 1; when s_kv_max > 0 is known, also
  * enough that the longest sequence's chunks fill about two rounds of the
  * resident workgroup slots (B = 1) or four (B > 1, where lengths may differ),
- * with chunks of 128 to 4096 tokens; at most GQA_MAX_SPLITS.
+ * with chunks of 128 to 4096 tokens; at most GQA_MAX_SPLITS. Exception: a
+ * single sequence that one workgroup per compute unit covers in chunks of
+ * 256 to 1024 tokens gets exactly that many chunks (num_cus / h_kv), which
+ * the library runs with 8-wave workgroups.
  * num_cus <= 0 queries the current device (returns a negative status if that
  * fails). Pure host arithmetic otherwise.
  */

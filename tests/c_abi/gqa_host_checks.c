@@ -87,8 +87,9 @@ int main(void) {
   expect("events off", gqa_decode_set_split_events(NULL, NULL), GQA_OK);
 
   /* split-count rules and workspace sizes: host arithmetic */
-  expect("pick 8k", gqa_decode_pick_splits(1, 8, 8192, 256), 64);
-  expect("pick 8193", gqa_decode_pick_splits(1, 8, 8193, 256), 64);
+  expect("pick 8k", gqa_decode_pick_splits(1, 8, 8192, 256), 32);
+  expect("pick 8191", gqa_decode_pick_splits(1, 8, 8191, 256), 64);
+  expect("pick 40000", gqa_decode_pick_splits(1, 8, 40000, 256), 128);
   expect("pick 1M", gqa_decode_pick_splits(1, 8, 1 << 20, 256), 256);
   expect("pick ragged", gqa_decode_pick_splits(8, 8, 32768, 256), 32);
   expect("pick huge", gqa_decode_pick_splits(1, 1, (int64_t)1 << 40, 256), GQA_MAX_SPLITS);

@@ -132,17 +132,27 @@ def test_split_heuristic_contract(gqa, B, h_kv, S):
     else:
         # never more chunks than the longest sequence fills with 128 tokens each
         assert n <= max(1, math.ceil(S / 128))
-        # every CU gets work whenever the sequence is long enough
+        # every CU gets work whenever the sequence is long enough: two 4-wave
+        # workgroups per CU, or, for one sequence of 256 to 1024 tokens per
+        # chunk, one 8-wave workgroup per CU
+        eight_wave = B == 1 and n * h_kv == cus and 256 * n <= S <= 1024 * n
         if S >= 128 * fill:
-            assert n * B * h_kv >= 2 * cus
+            assert n * B * h_kv >= 2 * cus or eight_wave
 
 
 def test_split_heuristic_values(gqa):
-    # 70B GQA at B = 1: 8 kv heads x 64 chunks = 512 workgroups of 128 tokens at 8k
-    assert gqa.gqa_decode_pick_splits(1, 8, 8192, 256) == 64
-    # one sequence: two rounds of the 512 resident slots (chunks of 256 to 1024 tokens)
-    assert gqa.gqa_decode_pick_splits(1, 8, 32768, 256) == 128
+    # 70B GQA at B = 1, 8k to 32k tokens: one 8-wave workgroup per CU, 8 kv
+    # heads x 32 chunks of 256 to 1024 tokens
+    assert gqa.gqa_decode_pick_splits(1, 8, 8192, 256) == 32
+    assert gqa.gqa_decode_pick_splits(1, 8, 32768, 256) == 32
+    # below: 512 workgroups of 4 waves, chunks of 128 tokens
+    assert gqa.gqa_decode_pick_splits(1, 8, 8191, 256) == 64
+    assert gqa.gqa_decode_pick_splits(1, 8, 4096, 256) == 32
+    # above: two rounds of the 512 resident slots
+    assert gqa.gqa_decode_pick_splits(1, 8, 32769, 256) == 128
     assert gqa.gqa_decode_pick_splits(1, 8, 131072, 256) == 128
+    # the 7B MHA shape (32 kv heads): 8 chunks from 2048 to 8192 tokens
+    assert gqa.gqa_decode_pick_splits(1, 32, 4096, 256) == 8
     # chunks of at most 4096 tokens
     assert gqa.gqa_decode_pick_splits(1, 8, 1 << 20, 256) == 256
     assert gqa.gqa_decode_pick_splits(1, 8, 1 << 22, 256) == 1024
@@ -152,8 +162,9 @@ def test_split_heuristic_values(gqa):
 
 def test_multi_split_heuristic_values(gqa):
     f = lambda B, S_q, S, h_q=64, h_kv=8: gqa.lib.gqa_decode_multi_splits(B, S_q, h_q, h_kv, S, 256)
-    # one query token, or a single 16-column tile: the single-token rule
-    assert f(1, 1, 8192) == gqa.gqa_decode_pick_splits(1, 8, 8192, 256) == 64
+    # one query token: the single-token rule; several in a single 16-column
+    # tile: the same without the 8-wave form (one query token only)
+    assert f(1, 1, 8192) == gqa.gqa_decode_pick_splits(1, 8, 8192, 256) == 32
     assert f(1, 2, 8192) == 64
     # two tiles per workgroup, one workgroup per CU: one round for one sequence
     assert f(1, 4, 8192) == 32

@@ -322,3 +322,17 @@ def test_one_wave_with_a_hint_below_the_lengths(ns):
     got, used = run_gpu(inp, n_splits=ns, hint=32)
     assert len(lens) * 8 * used > ONE_WAVE_UNITS
     report(f"one-wave hint 32 ns={ns}", max_err(got, ref_of(inp)), used, TOL_F32)
+
+
+@pytest.mark.parametrize("S,d,n_rep", [(8192, 128, 8), (8193, 128, 8), (20000, 64, 4), (32768, 128, 16)])
+def test_single_sequence_eight_wave(S, d, n_rep):
+    """One sequence of 8k to 32k tokens over 8 kv heads: 32 chunks of 256 to
+    1024 tokens, one 8-wave workgroup per compute unit (8193: a partial last
+    block in every chunk)."""
+    inp = workloads.custom(f"eight{S}", B=1, h_q=8 * n_rep, h_kv=8, d=d, seq_lens=[S], seed=130 + d + n_rep)
+    ref = ref_of(inp)
+    got, used = run_gpu(inp)
+    assert used == 32
+    report(f"8-wave S={S} d={d} n_rep={n_rep}", max_err(got, ref), used, TOL_F32)
+    got, used = run_gpu(inp, out_dtype="bf16")
+    report(f"8-wave S={S} d={d} n_rep={n_rep} bf16 out", max_err(got, ref), used, TOL_BF16)

@@ -161,3 +161,10 @@ def test_step_short_capacity_one_wave(explicit, ns):
     sequences x 8 kv heads give more than two chunks per compute unit: the
     step and the two-call path both take one-wave workgroups (same bits)."""
     run_case([0, 1, 31, 32, 63, 99, 100] * 10, 100, 64, 8, 128, explicit, n_splits=ns, seed=6)
+
+
+@pytest.mark.parametrize("explicit", [False, True])
+def test_step_single_sequence_eight_wave(explicit):
+    """One sequence in a 16384-token cache: 32 chunks of 512 tokens, 8-wave
+    workgroups in the step and in the two-call path alike (same bits)."""
+    run_case([12000], 16384, 64, 8, 128, explicit, seed=7)
