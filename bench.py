@@ -182,7 +182,7 @@ def bench_append_or_step(args) -> int:
     lens_in = torch.from_numpy(lens0).to(dev)
     lens_out = torch.empty_like(lens_in)
     offs = torch.arange(w.B, dtype=torch.int64, device=dev) * cap
-    ns = gqa.gqa_decode_pick_splits(w.B, w.h_kv, cap)
+    ns = gqa.gqa_decode_pick_splits_d(w.B, w.h_kv, w.d, cap)
     ws = torch.empty(gqa.gqa_decode_workspace_bytes(w.B, w.h_q, w.d, ns), dtype=torch.uint8, device=dev)
     out = torch.empty((w.B, w.h_q, w.d), dtype=torch.float32, device=dev)
 
@@ -317,7 +317,7 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"[bench] counter calibration: neg over {n} bytes")
 
-    ns = args.n_splits if args.n_splits > 0 else gqa.gqa_decode_pick_splits(w.B, w.h_kv, s_max)
+    ns = args.n_splits if args.n_splits > 0 else gqa.gqa_decode_pick_splits_d(w.B, w.h_kv, w.d, s_max)
     ws = torch.empty(gqa.gqa_decode_workspace_bytes(w.B, w.h_q, w.d, ns), dtype=torch.uint8, device=dev)
     out = torch.empty((w.B, w.h_q, w.d), dtype=torch.float32, device=dev)
     scale = float(inp.scale)

@@ -19,7 +19,7 @@ __all__ = [
     "gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_attn_multi", "gqa_decode_partial",
     "gqa_decode_merge", "gqa_kv_append", "gqa_decode_step", "gqa_decode_attn_triplet", "gqa_merge_triplets",
     "GQA_MAX_QUERY_TOKENS",
-    "gqa_decode_pick_splits",
+    "gqa_decode_pick_splits", "gqa_decode_pick_splits_d",
     "gqa_decode_workspace_bytes", "gqa_status_string", "GQAError", "lib", "LIB_PATH",
     "GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_WORKSPACE", "GQA_ERR_HIP",
     "GQA_DTYPE_F32", "GQA_DTYPE_BF16", "GQA_FLAG_VALU", "GQA_FLAG_FUSED", "GQA_MAX_SPLITS",
@@ -80,6 +80,8 @@ lib.gqa_decode_merge.argtypes = [_vp, _vp, _sz, _vp, _i32, _i32, _i32, _i32, _i3
 lib.gqa_decode_merge.restype = _i32
 lib.gqa_decode_pick_splits.argtypes = [_i32, _i32, _i64, _i32]
 lib.gqa_decode_pick_splits.restype = _i32
+lib.gqa_decode_pick_splits_d.argtypes = [_i32, _i32, _i32, _i64, _i32]
+lib.gqa_decode_pick_splits_d.restype = _i32
 lib.gqa_decode_multi_splits.argtypes = [_i32, _i32, _i32, _i32, _i64, _i32]
 lib.gqa_decode_multi_splits.restype = _i32
 lib.gqa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
@@ -104,10 +106,20 @@ def gqa_status_string(status: int) -> str:
 
 
 def gqa_decode_pick_splits(B: int, h_kv: int, s_kv_max: int = 0, num_cus: int = 0) -> int:
-    """Split count the library picks (num_cus <= 0: the current device's)."""
+    """Split count the library picks for d_head = 128 (num_cus <= 0: the
+    current device's)."""
     r = lib.gqa_decode_pick_splits(B, h_kv, s_kv_max, num_cus)
     if r < 0:
         raise GQAError(r, "gqa_decode_pick_splits")
+    return r
+
+
+def gqa_decode_pick_splits_d(B: int, h_kv: int, d_head: int, s_kv_max: int = 0, num_cus: int = 0) -> int:
+    """Split count the library picks for a head size (num_cus <= 0: the
+    current device's)."""
+    r = lib.gqa_decode_pick_splits_d(B, h_kv, d_head, s_kv_max, num_cus)
+    if r < 0:
+        raise GQAError(r, "gqa_decode_pick_splits_d")
     return r
 
 
@@ -164,7 +176,7 @@ def gqa_decode_attn_ex(q, k_cache, v_cache, seq_lens, out=None, *, scale=None, n
     elif out.shape != (B, h_q, d) or out.dtype != out_dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous [B, h_q, d_head] tensor of out_dtype")
     with torch.cuda.device(q.device):
-        ns = n_splits if n_splits > 0 else gqa_decode_pick_splits(B, h_kv, int(s_kv_hint), 0)
+        ns = n_splits if n_splits > 0 else gqa_decode_pick_splits_d(B, h_kv, d, int(s_kv_hint), 0)
         need = gqa_decode_workspace_bytes(B, h_q, d, ns) if ns <= GQA_MAX_SPLITS else 0
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -268,7 +280,7 @@ def gqa_decode_attn_triplet(q, k_cache, v_cache, seq_lens, *, scale=None, n_spli
     ml = torch.empty((B, h_q, 2), dtype=torch.float32, device=q.device)
     o = torch.empty((B, h_q, d), dtype=torch.float32, device=q.device)
     with torch.cuda.device(q.device):
-        ns = n_splits if n_splits > 0 else gqa_decode_pick_splits(B, h_kv, int(s_kv_hint), 0)
+        ns = n_splits if n_splits > 0 else gqa_decode_pick_splits_d(B, h_kv, d, int(s_kv_hint), 0)
         if workspace is None:
             workspace = torch.empty(gqa_decode_workspace_bytes(B, h_q, d, ns), dtype=torch.uint8, device=q.device)
         st = stream if stream is not None else torch.cuda.current_stream(q.device)

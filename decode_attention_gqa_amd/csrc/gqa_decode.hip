@@ -53,21 +53,24 @@ struct SplitPolicy {
 // One 16-column tile per workgroup, two workgroups per CU. A second round
 // hides each workgroup's start-up behind another's streaming.
 constexpr SplitPolicy kOneTile{2, 2, 4, 4096, true};
-// The same for several query tokens in one tile (the 8-wave form serves one
-// query token only).
-constexpr SplitPolicy kOneTileMulti{2, 2, 4, 4096, false};
+// The same without the 8-wave form: head size 64 (where 4-wave workgroups
+// fit three per CU and measured faster) and multi-token calls.
+constexpr SplitPolicy kOneTile4{2, 2, 4, 4096, false};
 // Two tiles per workgroup (multi-token decode), one workgroup per CU: one
 // round for a single sequence; chunks up to 16384 tokens.
 constexpr SplitPolicy kTwoTiles{1, 1, 4, 16384, false};
 
-const SplitPolicy& split_policy(int s_q, int tiles_per_wg) {
-  return tiles_per_wg == 2 ? kTwoTiles : (s_q == 1 ? kOneTile : kOneTileMulti);
+// eight_wave_ok: a single-token entry point (the multi-token one never
+// takes the 8-wave split count, so gqa_decode_multi_splits needs no d_head).
+const SplitPolicy& split_policy(int tiles_per_wg, int d_head, bool eight_wave_ok) {
+  return tiles_per_wg == 2 ? kTwoTiles : (eight_wave_ok && d_head == 128 ? kOneTile : kOneTile4);
 }
-// A single sequence whose chunks, at one 8-wave workgroup per CU, hold this
-// many tokens (each wave one to four 32-token blocks) takes that form:
-// measured faster at 70B shapes from 8k to 32k tokens (and the 7B shape at
-// 8k), slower below (waves without a block) and above (two rounds of 4-wave
-// workgroups balance better).
+// A single sequence with 128-dimension heads whose chunks, at one 8-wave
+// workgroup per CU, hold this many tokens (each wave one to four 32-token
+// blocks) takes that form: measured faster at 70B shapes from 8k to 32k
+// tokens (and at 1 to 16 kv heads in the same chunk range), slower below
+// (waves without a block) and above (two rounds of 4-wave workgroups balance
+// better), and slower with 64-dimension heads.
 constexpr int64_t kEightWaveMinChunk = 256, kEightWaveMaxChunk = 1024;
 
 // Library-owned fallback workspace, one grow-only buffer per device.
@@ -269,10 +272,11 @@ int pick_splits_host(int B, int passes, int h_kv, int64_t s_kv_max, int num_cus,
   }
   if (s_kv_max > 0 && B == 1) {
     // ... one sequence: a whole number of such rounds, up to the policy's,
-    // as long as chunks stay at least kMinChunk tokens (a length just past a
-    // multiple of the chunk must not leave a few workgroups for a last,
-    // nearly empty round), and chunks of at most max_chunk tokens.
-    int64_t k = s_kv_max / (kMinChunk * n);
+    // a second one only while its chunks keep at least two blocks per wave
+    // (2 * kMinChunk tokens; a length just past a multiple of the chunk must
+    // not leave a few workgroups for a last, nearly empty round), and chunks
+    // of at most max_chunk tokens.
+    int64_t k = s_kv_max / (2 * kMinChunk * n);
     if (k > p.rounds_one) k = p.rounds_one;
     if (k < 1) k = 1;
     n *= k;
@@ -328,13 +332,18 @@ size_t gqa_decode_workspace_bytes(int B, int h_q, int d_head, int n_splits) {
   return ws_bytes(B, h_q, d_head, n_splits);
 }
 
-int gqa_decode_pick_splits(int B, int h_kv, int64_t s_kv_max, int num_cus) {
+int gqa_decode_pick_splits_d(int B, int h_kv, int d_head, int64_t s_kv_max, int num_cus) {
   if (B < 1 || h_kv < 1) return fail(GQA_ERR_INVALID_ARG, "B and h_kv must be >= 1");
+  if (d_head != 64 && d_head != 128) return fail(GQA_ERR_UNSUPPORTED, "d_head %d not in {64, 128}", d_head);
   if (num_cus <= 0) {
     int st = device_cus(&num_cus);
     if (st != GQA_OK) return st;
   }
-  return pick_splits_host(B, 1, h_kv, s_kv_max, num_cus, kOneTile);
+  return pick_splits_host(B, 1, h_kv, s_kv_max, num_cus, split_policy(1, d_head, true));
+}
+
+int gqa_decode_pick_splits(int B, int h_kv, int64_t s_kv_max, int num_cus) {
+  return gqa_decode_pick_splits_d(B, h_kv, 128, s_kv_max, num_cus);
 }
 
 int gqa_decode_multi_splits(int B, int S_q, int h_q, int h_kv, int64_t s_kv_max, int num_cus) {
@@ -347,7 +356,7 @@ int gqa_decode_multi_splits(int B, int S_q, int h_q, int h_kv, int64_t s_kv_max,
   }
   int tpt, qtiles, tpw, passes;
   query_tiles(S_q, h_q / h_kv, &tpt, &qtiles, &tpw, &passes);
-  return pick_splits_host(B, passes, h_kv, s_kv_max, num_cus, split_policy(S_q, tpw));
+  return pick_splits_host(B, passes, h_kv, s_kv_max, num_cus, split_policy(tpw, 128, false));
 }
 
 }  // extern "C"
@@ -406,7 +415,7 @@ struct Plan {
 
 int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_hint,
               void* workspace, size_t workspace_bytes, bool allow_library_ws, Plan* pl,
-              int s_q = 1) {
+              int s_q = 1, bool multi_entry = false) {
   if (workspace && reinterpret_cast<uintptr_t>(workspace) % 256)
     return fail(GQA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
   if (!workspace && !allow_library_ws) return fail(GQA_ERR_INVALID_ARG, "this entry point needs a workspace");
@@ -417,7 +426,7 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
     if (st != GQA_OK) return st;
     int tpt, qtiles, tpw, passes;
     query_tiles(s_q, h_q / h_kv, &tpt, &qtiles, &tpw, &passes);
-    ns = pick_splits_host(B, passes, h_kv, s_kv_hint, num_cus, split_policy(s_q, tpw));
+    ns = pick_splits_host(B, passes, h_kv, s_kv_hint, num_cus, split_policy(tpw, d_head, !multi_entry));
   }
   pl->ns = ns;
   pl->min_chunk = n_splits > 0 ? 1 : kMinChunk;
@@ -444,14 +453,14 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
 //    kOneWaveMaxTokens and the grid is more than one round of 4-wave
 //    workgroups (two per CU; with one round or less, four waves per chunk
 //    finish it sooner);
-//  - eight waves per workgroup for a single sequence whose chunks hold
-//    kEightWaveMinChunk to kEightWaveMaxChunk tokens and fit one workgroup
-//    per CU in one round;
+//  - eight waves per workgroup for a single sequence with 128-dimension
+//    heads whose chunks hold kEightWaveMinChunk to kEightWaveMaxChunk tokens
+//    and fit one workgroup per CU in one round;
 //  - else four waves.
 // A wrong hint changes only the speed: every form takes any length. The
 // forms give a chunk's blocks to their waves differently, so their results
 // differ in rounding.
-Form split_form(const Plan& pl, int B, int h_kv) {
+Form split_form(const Plan& pl, int B, int h_kv, int d_head) {
   if (pl.hint <= 0) return Form::kFourWave;
   const int64_t per_chunk = (pl.hint + pl.ns - 1) / pl.ns;
   const int64_t tok = std::min<int64_t>(pl.hint, std::max<int64_t>(per_chunk, pl.min_chunk));
@@ -459,7 +468,8 @@ Form split_form(const Plan& pl, int B, int h_kv) {
   if (device_cus(&cus) != GQA_OK) return Form::kFourWave;
   const int64_t wgs = (int64_t)pl.ns * h_kv * B;
   if (tok <= kOneWaveMaxTokens) return wgs > 2 * (int64_t)cus ? Form::kOneWave : Form::kFourWave;
-  if (B == 1 && wgs <= cus && tok >= kEightWaveMinChunk && tok <= kEightWaveMaxChunk) return Form::kEightWave;
+  if (B == 1 && d_head == 128 && wgs <= cus && tok >= kEightWaveMinChunk && tok <= kEightWaveMaxChunk)
+    return Form::kEightWave;
   return Form::kFourWave;
 }
 
@@ -497,7 +507,7 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
     return fail(GQA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
   Form form = Form::kFourWave;
   if (mfma && s_q == 1) {
-    form = split_form(pl, B, h_kv);
+    form = split_form(pl, B, h_kv, d_head);
     if (fused) form = Form::kFourWave;             // the single-launch tail is built for 4 waves
   }
   e = d_head == 128 ? launch_split_nrep<128>(nrep, bf16, valu, form, grid, stream, sa)
@@ -611,7 +621,8 @@ int gqa_decode_attn_multi(const void* q, const void* k_cache, const void* v_cach
   if (workspace && overlap(out, qo * out_el, workspace, workspace_bytes))
     return fail(GQA_ERR_INVALID_ARG, "out overlaps workspace");
   Plan pl;
-  if ((st = make_plan(B, h_q, h_kv, d_head, n_splits, s_kv_hint, workspace, workspace_bytes, true, &pl, S_q)))
+  if ((st = make_plan(B, h_q, h_kv, d_head, n_splits, s_kv_hint, workspace, workspace_bytes, true, &pl, S_q,
+                      true)))
     return st;
   bool merged = false;
   if ((st = run_split(pl, q, k_cache, v_cache, seq_lens, kv_token_offsets, B, h_q, h_kv, d_head, scale,
@@ -681,7 +692,7 @@ int gqa_decode_step(const void* q, const void* k_new, const void* v_new, void* k
                     k_new, v_new, seq_lens_out, (int)capacity, pl.ns == 1 ? 1 : 0};
   const dim3 grid = gqa::split_grid(pl.ns, h_kv, B);
   const int nrep = h_q / h_kv;
-  const Form form = split_form(pl, B, h_kv);       // the same form as gqa_decode_attn_ex with this hint
+  const Form form = split_form(pl, B, h_kv, d_head);   // the same form as gqa_decode_attn_ex with this hint
   hipError_t e = d_head == 128 ? launch_split_append<128>(nrep, form, grid, stream, sa)
                                : launch_split_append<64>(nrep, form, grid, stream, sa);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));

@@ -96,7 +96,7 @@ enum {
  * own workspace).
  *  scale     multiplies q.k before the softmax (1/sqrt(d_head) for Llama).
  *  n_splits  > 0 forces the number of KV chunks per (sequence, kv head);
- *            <= 0 lets gqa_decode_pick_splits choose.
+ *            <= 0 lets gqa_decode_pick_splits_d choose.
  */
 int gqa_decode_attn(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* seq_lens, void* out,
@@ -120,8 +120,9 @@ int gqa_decode_attn(const void* q, const void* k_cache, const void* v_cache,
  *                    in fp32 rounding (another split count or form).
  *  workspace         device buffer of at least gqa_decode_workspace_bytes(B, h_q,
  *                    d_head, n) bytes, n being the split count that will be used
- *                    (n_splits if > 0, else gqa_decode_pick_splits(B, h_kv,
- *                    s_kv_hint, 0)); 256-byte aligned. NULL: library-owned.
+ *                    (n_splits if > 0, else gqa_decode_pick_splits_d(B, h_kv,
+ *                    d_head, s_kv_hint, 0)); 256-byte aligned. NULL:
+ *                    library-owned.
  *  stream            HIP stream (NULL: null stream).
  *  flags             0 or an OR of GQA_FLAG_VALU and GQA_FLAG_FUSED.
  * With one chunk per sequence (n = 1) and the matrix-core kernel, the split
@@ -192,8 +193,8 @@ int gqa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_c
  *   out           [B, h_q, d_head] fp32 or bf16 (out_dtype).
  * Same result, bit for bit, as gqa_kv_append followed by gqa_decode_attn_ex
  * with explicit offsets (b * capacity when NULL here), s_kv_hint = capacity
- * and the same n_splits. The split count defaults to gqa_decode_pick_splits(B, h_kv,
- * capacity, 0), the workspace to gqa_decode_workspace_bytes for it (NULL:
+ * and the same n_splits. The split count defaults to gqa_decode_pick_splits_d(B, h_kv,
+ * d_head, capacity, 0), the workspace to gqa_decode_workspace_bytes for it (NULL:
  * library-owned). bf16 only (GQA_ERR_UNSUPPORTED otherwise). Asynchronous on
  * `stream`; no host synchronisation, allocation (given a workspace) or memset,
  * so a graph of one step can be replayed while the lengths grow.
@@ -268,13 +269,17 @@ int gqa_decode_merge(const int32_t* seq_lens, const void* workspace, size_t work
  * every compute unit has work at B = 1; when s_kv_max > 0 is known, also
  * enough that the longest sequence's chunks fill about two rounds of the
  * resident workgroup slots (B = 1) or four (B > 1, where lengths may differ),
- * with chunks of 128 to 4096 tokens; at most GQA_MAX_SPLITS. Exception: a
- * single sequence that one workgroup per compute unit covers in chunks of
- * 256 to 1024 tokens gets exactly that many chunks (num_cus / h_kv), which
- * the library runs with 8-wave workgroups.
+ * with chunks of 128 to 4096 tokens; at most GQA_MAX_SPLITS. Exception, for
+ * d_head = 128: a single sequence that one workgroup per compute unit covers
+ * in chunks of 256 to 1024 tokens gets exactly that many chunks
+ * (num_cus / h_kv), which the library runs with 8-wave workgroups.
  * num_cus <= 0 queries the current device (returns a negative status if that
- * fails). Pure host arithmetic otherwise.
+ * fails). Pure host arithmetic otherwise. GQA_ERR_UNSUPPORTED for a d_head
+ * other than 64 or 128.
  */
+int gqa_decode_pick_splits_d(int B, int h_kv, int d_head, int64_t s_kv_max, int num_cus);
+
+/* gqa_decode_pick_splits_d for d_head = 128. */
 int gqa_decode_pick_splits(int B, int h_kv, int64_t s_kv_max, int num_cus);
 
 /* Split count gqa_decode_attn_multi uses when n_splits <= 0 (the same rule,

@@ -89,9 +89,9 @@ int main(int argc, char** argv) {
   HIP_OK(hipMemcpy(dv, v, nkv * 2, hipMemcpyHostToDevice));
   HIP_OK(hipMemcpy(dlens, lens, (size_t)B * 4, hipMemcpyHostToDevice));
 
-  const int ns = n_splits_in > 0 ? n_splits_in : gqa_decode_pick_splits(B, h_kv, s_max, 0);
+  const int ns = n_splits_in > 0 ? n_splits_in : gqa_decode_pick_splits_d(B, h_kv, d, s_max, 0);
   if (ns < 1) {
-    fprintf(stderr, "gqa_decode_pick_splits: %d (%s)\n", ns, gqa_last_error());
+    fprintf(stderr, "gqa_decode_pick_splits_d: %d (%s)\n", ns, gqa_last_error());
     return 3;
   }
   const size_t ws_bytes = gqa_decode_workspace_bytes(B, h_q, d, ns);

@@ -91,6 +91,8 @@ int main(void) {
   expect("pick 8191", gqa_decode_pick_splits(1, 8, 8191, 256), 64);
   expect("pick 40000", gqa_decode_pick_splits(1, 8, 40000, 256), 128);
   expect("pick 1M", gqa_decode_pick_splits(1, 8, 1 << 20, 256), 256);
+  expect("pick d64 8k", gqa_decode_pick_splits_d(1, 8, 64, 8192, 256), 64);
+  expect("pick d96", gqa_decode_pick_splits_d(1, 8, 96, 8192, 256), GQA_ERR_UNSUPPORTED);
   expect("pick ragged", gqa_decode_pick_splits(8, 8, 32768, 256), 32);
   expect("pick huge", gqa_decode_pick_splits(1, 1, (int64_t)1 << 40, 256), GQA_MAX_SPLITS);
   expect("multi S_q 4", gqa_decode_multi_splits(1, 4, 64, 8, 8192, 256), 32);

@@ -34,7 +34,7 @@ def run_gpu(inp: workloads.Inputs, n_splits=0, out_dtype="f32", valu=False, pois
     w = inp.w
     s_max = int(inp.seq_lens.max()) if len(inp.seq_lens) else 0
     hint_v = (s_max if hint else 0) if isinstance(hint, bool) else int(hint)   # an int: that hint
-    ns = n_splits if n_splits > 0 else gqa.gqa_decode_pick_splits(w.B, w.h_kv, hint_v)
+    ns = n_splits if n_splits > 0 else gqa.gqa_decode_pick_splits_d(w.B, w.h_kv, w.d, hint_v)
     ws = torch.empty(gqa.gqa_decode_workspace_bytes(w.B, w.h_q, w.d, ns), dtype=torch.uint8, device=q.device)
     if poison:   # every byte, the arrival counters included
         ws.view(torch.float32).fill_(float("nan"))

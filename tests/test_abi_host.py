@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_attn_multi", "gqa_decode_partial",
                             "gqa_decode_merge", "gqa_kv_append", "gqa_decode_step", "gqa_decode_attn_triplet",
-                            "gqa_merge_triplets", "gqa_decode_pick_splits", "gqa_decode_multi_splits",
+                            "gqa_merge_triplets", "gqa_decode_pick_splits", "gqa_decode_pick_splits_d",
+                            "gqa_decode_multi_splits",
                             "gqa_decode_workspace_bytes", "gqa_status_string", "gqa_last_error",
                             "gqa_decode_set_split_events"])
 
@@ -153,6 +154,13 @@ def test_split_heuristic_values(gqa):
     assert gqa.gqa_decode_pick_splits(1, 8, 131072, 256) == 128
     # the 7B MHA shape (32 kv heads): 8 chunks from 2048 to 8192 tokens
     assert gqa.gqa_decode_pick_splits(1, 32, 4096, 256) == 8
+    # gqa_decode_pick_splits is the 128-dimension case; 64-dimension heads
+    # never take the 8-wave count
+    assert gqa.gqa_decode_pick_splits_d(1, 8, 128, 8192, 256) == 32
+    assert gqa.gqa_decode_pick_splits_d(1, 8, 64, 8192, 256) == 64
+    assert gqa.gqa_decode_pick_splits_d(1, 8, 64, 32768, 256) == 128
+    assert gqa.gqa_decode_pick_splits_d(8, 8, 64, 32768, 256) == gqa.gqa_decode_pick_splits(8, 8, 32768, 256)
+    assert gqa.lib.gqa_decode_pick_splits_d(1, 8, 96, 8192, 256) == gqa.GQA_ERR_UNSUPPORTED
     # chunks of at most 4096 tokens
     assert gqa.gqa_decode_pick_splits(1, 8, 1 << 20, 256) == 256
     assert gqa.gqa_decode_pick_splits(1, 8, 1 << 22, 256) == 1024
@@ -162,9 +170,9 @@ def test_split_heuristic_values(gqa):
 
 def test_multi_split_heuristic_values(gqa):
     f = lambda B, S_q, S, h_q=64, h_kv=8: gqa.lib.gqa_decode_multi_splits(B, S_q, h_q, h_kv, S, 256)
-    # one query token: the single-token rule; several in a single 16-column
-    # tile: the same without the 8-wave form (one query token only)
-    assert f(1, 1, 8192) == gqa.gqa_decode_pick_splits(1, 8, 8192, 256) == 32
+    # one or several query tokens in a single 16-column tile: the
+    # single-token rule without the 8-wave count
+    assert f(1, 1, 8192) == gqa.gqa_decode_pick_splits_d(1, 8, 64, 8192, 256) == 64
     assert f(1, 2, 8192) == 64
     # two tiles per workgroup, one workgroup per CU: one round for one sequence
     assert f(1, 4, 8192) == 32

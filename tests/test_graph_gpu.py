@@ -42,7 +42,7 @@ def test_graph_decode_loop_append_attend():
     vn_d = torch.empty_like(kn_d)
     q_d = torch.empty((B, h_q, d), dtype=torch.bfloat16, device="cuda")
     out_d = torch.empty((B, h_q, d), dtype=torch.float32, device="cuda")
-    ns = gqa.gqa_decode_pick_splits(B, h_kv, cap)
+    ns = gqa.gqa_decode_pick_splits_d(B, h_kv, d, cap)
     ws = torch.empty(gqa.gqa_decode_workspace_bytes(B, h_q, d, ns), dtype=torch.uint8, device="cuda")
 
     st = torch.cuda.Stream()

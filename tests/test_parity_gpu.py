@@ -223,7 +223,7 @@ def test_partial_then_merge_equals_full_call(ns):
     q, k, v, dl = to_device(inp)
     w = inp.w
     hint = int(inp.seq_lens.max())
-    n = ns if ns > 0 else gqa.gqa_decode_pick_splits(w.B, w.h_kv, hint)
+    n = ns if ns > 0 else gqa.gqa_decode_pick_splits_d(w.B, w.h_kv, w.d, hint)
     ws = torch.empty(gqa.gqa_decode_workspace_bytes(w.B, w.h_q, w.d, n), dtype=torch.uint8, device="cuda")
     full = gqa.gqa_decode_attn_ex(q, k, v, dl, scale=float(inp.scale), n_splits=ns, s_kv_hint=hint, workspace=ws)
     out = torch.empty_like(full)
@@ -324,11 +324,11 @@ def test_one_wave_with_a_hint_below_the_lengths(ns):
     report(f"one-wave hint 32 ns={ns}", max_err(got, ref_of(inp)), used, TOL_F32)
 
 
-@pytest.mark.parametrize("S,d,n_rep", [(8192, 128, 8), (8193, 128, 8), (20000, 64, 4), (32768, 128, 16)])
+@pytest.mark.parametrize("S,d,n_rep", [(8192, 128, 8), (8193, 128, 8), (20000, 128, 4), (32768, 128, 16)])
 def test_single_sequence_eight_wave(S, d, n_rep):
-    """One sequence of 8k to 32k tokens over 8 kv heads: 32 chunks of 256 to
-    1024 tokens, one 8-wave workgroup per compute unit (8193: a partial last
-    block in every chunk)."""
+    """One sequence of 8k to 32k tokens over 8 kv heads of 128 dimensions: 32
+    chunks of 256 to 1024 tokens, one 8-wave workgroup per compute unit
+    (8193: a partial last block in every chunk)."""
     inp = workloads.custom(f"eight{S}", B=1, h_q=8 * n_rep, h_kv=8, d=d, seq_lens=[S], seed=130 + d + n_rep)
     ref = ref_of(inp)
     got, used = run_gpu(inp)
