@@ -77,13 +77,25 @@ constexpr int64_t kEightWaveMinChunk = 256, kEightWaveMaxChunk = 1024;
 std::mutex g_ws_mu;
 std::vector<std::pair<void*, size_t>> g_ws;  // index = device ordinal
 
+// Compute units of the current device, queried once per device ordinal.
+std::atomic<int> g_cus[64];
+
 int device_cus(int* cus) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < 64) {
+    const int known = g_cus[dev].load(std::memory_order_relaxed);
+    if (known > 0) {
+      *cus = known;
+      return GQA_OK;
+    }
+  }
   int n = 0;
   e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+  if (n < 1) return fail(GQA_ERR_HIP, "device %d reports %d compute units", dev, n);
+  if (dev >= 0 && dev < 64) g_cus[dev].store(n, std::memory_order_relaxed);
   *cus = n;
   return GQA_OK;
 }
