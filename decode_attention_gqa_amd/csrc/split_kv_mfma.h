@@ -1,12 +1,12 @@
 // Split-KV partial attention on the gfx950 matrix cores (bf16 q, K, V).
 //
 // One workgroup owns one chunk of one (sequence b, kv head g) pair and the
-// n_rep query heads of that group. Each of its 4 waves walks 32-token blocks
-// of the chunk (wave w takes blocks w, w+4, ...), two register buffers in
-// turn so the next block is in flight while one is computed, and keeps an
-// online-softmax state (m, l, o) for the group's heads; at the end the 4
-// states are merged in LDS and the workgroup writes one (m, l, o) triplet
-// per head. Two template options widen the same kernel: APPEND (a decode
+// n_rep query heads of that group. Each of its waves (4 by default) walks
+// 32-token blocks of the chunk (wave w of W takes blocks w, w+W, ...), two
+// register buffers in turn so the next block is in flight while one is
+// computed, and keeps an online-softmax state (m, l, o) for the group's
+// heads; at the end the waves' states are merged in LDS and the workgroup
+// writes one (m, l, o) triplet per head. Two template options widen the same kernel: APPEND (a decode
 // step that appends the new token on the way) and TILES = 2 (two 16-column
 // tiles of several query tokens per workgroup); see the kernel. WAVES = 1
 // gives one-wave workgroups for chunks of a few blocks (many short
@@ -401,7 +401,7 @@ void split_kv_mfma(SplitArgs a) {
     *reinterpret_cast<uint4*>(static_cast<char*>(const_cast<void*>(tid < U16 ? a.k : a.v)) + row_new +
                               16 * (tid % U16)) = piece;
 
-  // Merge the 4 waves' states in LDS and write the workgroup's triplets, one
+  // Merge the waves' states in LDS and write the workgroup's triplets, one
   // tile at a time through the same LDS.
   constexpr int OP = D + 4;                        // padded row (fewer bank conflicts)
   constexpr int Q4 = D / 4;
