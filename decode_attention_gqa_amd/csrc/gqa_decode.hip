@@ -296,10 +296,13 @@ int pick_splits_host(int B, int passes, int h_kv, int64_t s_kv_max, int num_cus,
     if (by_max > n) n = by_max;
   } else if (s_kv_max > 0) {
     // ... several sequences: chunks short enough that the longest one's
-    // workgroups are spread over the policy's rounds of the resident slots
-    // (only the longest length is known, and more rounds keep a ragged batch
-    // balanced); chunks within [kMinChunk, max_chunk] tokens.
-    int64_t chunk = (s_kv_max * units + p.rounds_many * slots - 1) / (p.rounds_many * slots);
+    // workgroups are spread over rounds of the resident slots: only the
+    // longest length is known, and more rounds keep a ragged batch balanced,
+    // but a batch of few sequences can only be so uneven and pays for every
+    // extra round in triplets to store and merge, so B / 2 rounds, from 1 up
+    // to the policy's; chunks within [kMinChunk, max_chunk] tokens.
+    const int64_t rounds = std::max<int64_t>(1, std::min<int64_t>(p.rounds_many, B / 2));
+    int64_t chunk = (s_kv_max * units + rounds * slots - 1) / (rounds * slots);
     if (chunk > p.max_chunk) chunk = p.max_chunk;
     if (chunk < kMinChunk) chunk = kMinChunk;
     const int64_t by_len = (s_kv_max + chunk - 1) / chunk;

@@ -268,7 +268,8 @@ int gqa_decode_merge(const int32_t* seq_lens, const void* workspace, size_t work
  * Split count the library uses when n_splits <= 0: enough workgroups that
  * every compute unit has work at B = 1; when s_kv_max > 0 is known, also
  * enough that the longest sequence's chunks fill about two rounds of the
- * resident workgroup slots (B = 1) or four (B > 1, where lengths may differ),
+ * resident workgroup slots (B = 1) or B / 2 up to four (B > 1, where lengths
+ * may differ),
  * with chunks of 128 to 4096 tokens; at most GQA_MAX_SPLITS. Exception, for
  * d_head = 128: a single sequence that one workgroup per compute unit covers
  * in chunks of 256 to 1024 tokens gets exactly that many chunks
