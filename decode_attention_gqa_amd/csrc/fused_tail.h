@@ -8,8 +8,9 @@
 // its own 48-bit tag, and an arrival that finds a different tag starts the
 // count at 1, so whatever the word held before (a previous call that reset
 // it, or unrelated workspace data) cannot be taken for this call's count.
-// The compare-and-swap loop ends: every retry means another workgroup's swap
-// succeeded, and at most n_active workgroups arrive.
+// The counting loop ends: a failed swap means the word changed, to this
+// call's tag (the next pass adds) or by another arrival's successful swap,
+// and at most n_active workgroups arrive.
 //
 // Ordering: every thread waits until its own triplet stores are complete
 // (accepted by the L2 of its XCD), the workgroup meets at a barrier, and one
@@ -125,11 +126,24 @@ __device__ __forceinline__ void fused_epilogue(const SplitArgs& a, int g, int b,
   unsigned long long* cnt = a.counters + (int64_t)b * a.h_kv + g;
   if (threadIdx.x == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // the workgroup's stores, device-wide
+    // Once a word holds this call's tag it keeps it until every chunk has
+    // arrived (only the last workgroup resets it), so arrivals that see the
+    // tag add 1; the first one installs (tag, 1) with a compare-and-swap
+    // (a loop of compare-and-swaps for every arrival measured several times
+    // slower: they contend for the one word).
     unsigned long long old = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), nw;
-    do {
-      nw = ((old >> 16) == a.tag) ? old + 1 : ((a.tag << 16) | 1ull);
-    } while (!__hip_atomic_compare_exchange_strong(cnt, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT));
+    while (true) {
+      if ((old >> 16) == a.tag) {
+        nw = __hip_atomic_fetch_add(cnt, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1ull;
+        break;
+      }
+      const unsigned long long first = (a.tag << 16) | 1ull;
+      if (__hip_atomic_compare_exchange_strong(cnt, &old, first, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)) {
+        nw = first;
+        break;
+      }
+    }
     const int last = (int)(nw & 0xFFFFull) == n_active;
     if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     s_last = last;
