@@ -109,3 +109,28 @@ def test_empty_shards_give_neutral_triplets():
     ref = oracle.attend(inp.q, inp.k, inp.v, inp.seq_lens, inp.scale, 2, dtype="bf16")
     assert max_err(out.cpu().numpy().astype(np.float64), ref) <= TOL_F32
     assert torch.all(out[0] == 0)
+
+
+@pytest.mark.parametrize("ns", [1, 3, 20, 100])
+def test_shard_triplets_through_every_merge_kernel(ns):
+    """The shard's own merge writes merged triplets instead of o / l; forced
+    split counts take it through each merge kernel (up to 8 chunks: several
+    rows per workgroup; 9 to 32: a wave per slice; more: a workgroup per
+    slice)."""
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    inp = workloads.make_inputs("llama70b_gqa_b8_ragged")
+    q = dev(inp.q)
+    mls, os_ = [], []
+    for k, v, lens in shard(inp, 2):
+        ml, o = gqa.gqa_decode_attn_triplet(q, dev(k), dev(v), torch.from_numpy(lens).cuda(),
+                                            scale=float(inp.scale), n_splits=ns, s_kv_hint=int(lens.max()))
+        mls.append(ml)
+        os_.append(o)
+    out = gqa.gqa_merge_triplets(torch.stack(mls), torch.stack(os_))
+    torch.cuda.synchronize()
+    ref = oracle.attend(inp.q, inp.k, inp.v, inp.seq_lens, inp.scale, 8, dtype="bf16")
+    err = max_err(out.cpu().numpy().astype(np.float64), ref)
+    print(f"[sharded] ns={ns}: max_abs_err={err:.3e}", flush=True)
+    assert err <= TOL_F32
