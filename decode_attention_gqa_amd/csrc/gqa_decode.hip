@@ -40,6 +40,7 @@ int fail(int status, const char* fmt, ...) {
 
 // Heuristic constants (see gqa_decode_pick_splits).
 constexpr int kMinChunk = 128;       // tokens: one 32-token block per wave of a workgroup
+constexpr int kBlockTokens = 32;     // one block: the shortest chunk of a single short sequence
 // How a split kernel wants its grid: resident workgroups per CU, rounds of
 // those slots the longest sequence's chunks fill (one sequence / a batch, where
 // only the longest length is known and more rounds keep it balanced), and the
@@ -49,21 +50,27 @@ struct SplitPolicy {
   int rounds_one, rounds_many;
   int64_t max_chunk;
   bool eight_wave;              // a single sequence may take one 8-wave workgroup per CU
+  bool short_one;               // a single short sequence: chunks down to one block (single token)
 };
-// One 16-column tile per workgroup, two workgroups per CU. A second round
-// hides each workgroup's start-up behind another's streaming.
-constexpr SplitPolicy kOneTile{2, 2, 4, 4096, true};
-// The same without the 8-wave form: head size 64 (where 4-wave workgroups
-// fit three per CU and measured faster) and multi-token calls.
-constexpr SplitPolicy kOneTile4{2, 2, 4, 4096, false};
+// One 16-column tile per workgroup, two workgroups per CU, one query token. A
+// second round hides each workgroup's start-up behind another's streaming.
+constexpr SplitPolicy kOneTile{2, 2, 4, 4096, true, true};
+// The same without the 8-wave form: head size 64, where 4-wave workgroups
+// fit three per CU and measured faster.
+constexpr SplitPolicy kOneTile64{2, 2, 4, 4096, false, true};
+// One tile of several query tokens (multi-token calls).
+constexpr SplitPolicy kOneTileMulti{2, 2, 4, 4096, false, false};
 // Two tiles per workgroup (multi-token decode), one workgroup per CU: one
 // round for a single sequence; chunks up to 16384 tokens.
-constexpr SplitPolicy kTwoTiles{1, 1, 4, 16384, false};
+constexpr SplitPolicy kTwoTiles{1, 1, 4, 16384, false, false};
 
-// eight_wave_ok: a single-token entry point (the multi-token one never
-// takes the 8-wave split count, so gqa_decode_multi_splits needs no d_head).
-const SplitPolicy& split_policy(int tiles_per_wg, int d_head, bool eight_wave_ok) {
-  return tiles_per_wg == 2 ? kTwoTiles : (eight_wave_ok && d_head == 128 ? kOneTile : kOneTile4);
+// single_token: a single-token entry point (the multi-token one takes
+// neither the 8-wave nor the short-sequence count, so gqa_decode_multi_splits
+// needs no d_head).
+const SplitPolicy& split_policy(int tiles_per_wg, int d_head, bool single_token) {
+  if (tiles_per_wg == 2) return kTwoTiles;
+  if (!single_token) return kOneTileMulti;
+  return d_head == 128 ? kOneTile : kOneTile64;
 }
 // A single sequence with 128-dimension heads whose chunks, at one 8-wave
 // workgroup per CU, hold this many tokens (each wave one to four 32-token
@@ -312,6 +319,13 @@ int pick_splits_host(int B, int passes, int h_kv, int64_t s_kv_max, int num_cus,
     const int64_t cap = (s_kv_max + kMinChunk - 1) / kMinChunk;   // no chunk shorter than kMinChunk
     if (n > cap) n = cap;
   }
+  if (s_kv_max > 0 && B == 1 && p.short_one) {
+    // ... except a short single sequence: up to one workgroup per CU while
+    // chunks keep one block (more workgroups engage more CUs' memory paths,
+    // even with waves that have no block; measured faster below 4k tokens).
+    const int64_t n1 = std::min<int64_t>(num_cus / units, (s_kv_max + kBlockTokens - 1) / kBlockTokens);
+    if (n1 > n) n = n1;
+  }
   if (n < 1) n = 1;
   if (n > GQA_MAX_SPLITS) n = GQA_MAX_SPLITS;
   return (int)n;
@@ -444,7 +458,9 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
     ns = pick_splits_host(B, passes, h_kv, s_kv_hint, num_cus, split_policy(tpw, d_head, !multi_entry));
   }
   pl->ns = ns;
-  pl->min_chunk = n_splits > 0 ? 1 : kMinChunk;
+  // a heuristic call keeps chunks of at least kMinChunk tokens, a single
+  // sequence of a single-token call of at least one block
+  pl->min_chunk = n_splits > 0 ? 1 : (B == 1 && !multi_entry ? kBlockTokens : kMinChunk);
   pl->hint = s_kv_hint;
   pl->need = ws_bytes(B * s_q, h_q, d_head, ns);
   if (workspace) {

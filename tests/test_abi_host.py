@@ -131,8 +131,9 @@ def test_split_heuristic_contract(gqa, B, h_kv, S):
     if S == 0:
         assert n == min(fill, gqa.GQA_MAX_SPLITS)
     else:
-        # never more chunks than the longest sequence fills with 128 tokens each
-        assert n <= max(1, math.ceil(S / 128))
+        # never more chunks than the longest sequence fills with 128 tokens
+        # each (32 for a single sequence)
+        assert n <= max(1, math.ceil(S / (32 if B == 1 else 128)))
         # every CU gets work whenever the sequence is long enough: two 4-wave
         # workgroups per CU, or, for one sequence of 256 to 1024 tokens per
         # chunk, one 8-wave workgroup per CU
@@ -149,6 +150,13 @@ def test_split_heuristic_values(gqa):
     # below: 512 workgroups of 4 waves, chunks of 128 tokens
     assert gqa.gqa_decode_pick_splits(1, 8, 8191, 256) == 64
     assert gqa.gqa_decode_pick_splits(1, 8, 4096, 256) == 32
+    # short: up to one workgroup per CU (32 chunks) with chunks down to 32 tokens
+    assert gqa.gqa_decode_pick_splits(1, 8, 2048, 256) == 32
+    assert gqa.gqa_decode_pick_splits(1, 8, 1024, 256) == 32
+    assert gqa.gqa_decode_pick_splits(1, 8, 256, 256) == 8
+    assert gqa.gqa_decode_pick_splits(1, 8, 40, 256) == 2
+    assert gqa.gqa_decode_pick_splits(1, 32, 1024, 256) == 8
+    assert gqa.gqa_decode_pick_splits_d(1, 8, 64, 512, 256) == 16
     # above: two rounds of the 512 resident slots
     assert gqa.gqa_decode_pick_splits(1, 8, 32769, 256) == 128
     assert gqa.gqa_decode_pick_splits(1, 8, 131072, 256) == 128
