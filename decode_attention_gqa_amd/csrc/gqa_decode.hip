@@ -50,7 +50,7 @@ struct SplitPolicy {
   int rounds_one, rounds_many;
   int64_t max_chunk;
   bool eight_wave;              // a single sequence may take one 8-wave workgroup per CU
-  bool short_one;               // a single short sequence: chunks down to one block (single token)
+  bool short_one;               // short sequences, B <= 4: chunks down to one block (single token)
 };
 // One 16-column tile per workgroup, two workgroups per CU, one query token. A
 // second round hides each workgroup's start-up behind another's streaming.
@@ -319,10 +319,11 @@ int pick_splits_host(int B, int passes, int h_kv, int64_t s_kv_max, int num_cus,
     const int64_t cap = (s_kv_max + kMinChunk - 1) / kMinChunk;   // no chunk shorter than kMinChunk
     if (n > cap) n = cap;
   }
-  if (s_kv_max > 0 && B == 1 && p.short_one) {
-    // ... except a short single sequence: up to one workgroup per CU while
-    // chunks keep one block (more workgroups engage more CUs' memory paths,
-    // even with waves that have no block; measured faster below 4k tokens).
+  if (s_kv_max > 0 && B <= 4 && p.short_one) {
+    // ... except short sequences in a batch of at most 4: up to one
+    // workgroup per CU while chunks keep one block (more workgroups engage
+    // more CUs' memory paths, even with waves that have no block; measured
+    // faster below 4k tokens, and not for larger batches).
     const int64_t n1 = std::min<int64_t>(num_cus / units, (s_kv_max + kBlockTokens - 1) / kBlockTokens);
     if (n1 > n) n = n1;
   }
@@ -458,9 +459,9 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
     ns = pick_splits_host(B, passes, h_kv, s_kv_hint, num_cus, split_policy(tpw, d_head, !multi_entry));
   }
   pl->ns = ns;
-  // a heuristic call keeps chunks of at least kMinChunk tokens, a single
-  // sequence of a single-token call of at least one block
-  pl->min_chunk = n_splits > 0 ? 1 : (B == 1 && !multi_entry ? kBlockTokens : kMinChunk);
+  // a heuristic call keeps chunks of at least kMinChunk tokens, a
+  // single-token call of at most 4 sequences of at least one block
+  pl->min_chunk = n_splits > 0 ? 1 : (B <= 4 && !multi_entry ? kBlockTokens : kMinChunk);
   pl->hint = s_kv_hint;
   pl->need = ws_bytes(B * s_q, h_q, d_head, ns);
   if (workspace) {

@@ -245,7 +245,7 @@ int gqa_merge_triplets(const float* ml, const float* o, int parts, int rows, int
  * split count used, and `o` and `ml` sit where gqa_decode_workspace_bytes
  * describes. Chunk s covers tokens
  * [s*c, min(S_b, (s+1)*c)) with c = max(ceil(S_b / n), f), f = 1 when
- * n_splits > 0, else 32 for a single sequence (B = 1) and 128 for a batch;
+ * n_splits > 0, else 32 for B <= 4 and 128 for larger batches;
  * n_active(b) = ceil(S_b / c). Other slots are left untouched. A workspace is
  * required.
  *
@@ -274,8 +274,9 @@ int gqa_decode_merge(const int32_t* seq_lens, const void* workspace, size_t work
  * with chunks of 128 to 4096 tokens; at most GQA_MAX_SPLITS. Exceptions for
  * a single sequence: with d_head = 128, one that one workgroup per compute
  * unit covers in chunks of 256 to 1024 tokens gets exactly that many chunks
- * (num_cus / h_kv), which the library runs with 8-wave workgroups; a short
- * one gets up to num_cus / h_kv chunks of at least 32 tokens.
+ * (num_cus / h_kv), which the library runs with 8-wave workgroups; short
+ * sequences in a batch of at most 4 get up to num_cus / (B * h_kv) chunks of
+ * at least 32 tokens.
  * num_cus <= 0 queries the current device (returns a negative status if that
  * fails). Pure host arithmetic otherwise. GQA_ERR_UNSUPPORTED for a d_head
  * other than 64 or 128.

@@ -133,7 +133,7 @@ def test_split_heuristic_contract(gqa, B, h_kv, S):
     else:
         # never more chunks than the longest sequence fills with 128 tokens
         # each (32 for a single sequence)
-        assert n <= max(1, math.ceil(S / (32 if B == 1 else 128)))
+        assert n <= max(1, math.ceil(S / (32 if B <= 4 else 128)))
         # every CU gets work whenever the sequence is long enough: two 4-wave
         # workgroups per CU, or, for one sequence of 256 to 1024 tokens per
         # chunk, one 8-wave workgroup per CU
@@ -157,6 +157,8 @@ def test_split_heuristic_values(gqa):
     assert gqa.gqa_decode_pick_splits(1, 8, 40, 256) == 2
     assert gqa.gqa_decode_pick_splits(1, 32, 1024, 256) == 8
     assert gqa.gqa_decode_pick_splits_d(1, 8, 64, 512, 256) == 16
+    assert gqa.gqa_decode_pick_splits(2, 8, 256, 256) == 8      # B <= 4: the same
+    assert gqa.gqa_decode_pick_splits(8, 8, 256, 256) == 2      # larger batches: 128-token chunks
     # above: two rounds of the 512 resident slots
     assert gqa.gqa_decode_pick_splits(1, 8, 32769, 256) == 128
     assert gqa.gqa_decode_pick_splits(1, 8, 131072, 256) == 128
