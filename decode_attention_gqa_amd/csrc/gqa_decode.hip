@@ -64,13 +64,14 @@ constexpr SplitPolicy kOneTileMulti{2, 2, 4, 4096, false, false};
 // round for a single sequence; chunks up to 16384 tokens.
 constexpr SplitPolicy kTwoTiles{1, 1, 4, 16384, false, false};
 
-// single_token: a single-token entry point (the multi-token one takes
-// neither the 8-wave nor the short-sequence count, so gqa_decode_multi_splits
-// needs no d_head).
-const SplitPolicy& split_policy(int tiles_per_wg, int d_head, bool single_token) {
+// single_token: a single-token entry point. The multi-token one never takes
+// the 8-wave count (so gqa_decode_multi_splits needs no d_head), and takes the
+// short-sequence count only for one query token, where it then plans like a
+// single-token call outside the 8-wave range.
+const SplitPolicy& split_policy(int tiles_per_wg, int d_head, bool single_token, int s_q) {
   if (tiles_per_wg == 2) return kTwoTiles;
-  if (!single_token) return kOneTileMulti;
-  return d_head == 128 ? kOneTile : kOneTile64;
+  if (single_token && d_head == 128) return kOneTile;
+  return single_token || s_q == 1 ? kOneTile64 : kOneTileMulti;
 }
 // A single sequence with 128-dimension heads whose chunks, at one 8-wave
 // workgroup per CU, hold this many tokens (each wave one to four 32-token
@@ -369,7 +370,7 @@ int gqa_decode_pick_splits_d(int B, int h_kv, int d_head, int64_t s_kv_max, int 
     int st = device_cus(&num_cus);
     if (st != GQA_OK) return st;
   }
-  return pick_splits_host(B, 1, h_kv, s_kv_max, num_cus, split_policy(1, d_head, true));
+  return pick_splits_host(B, 1, h_kv, s_kv_max, num_cus, split_policy(1, d_head, true, 1));
 }
 
 int gqa_decode_pick_splits(int B, int h_kv, int64_t s_kv_max, int num_cus) {
@@ -386,7 +387,7 @@ int gqa_decode_multi_splits(int B, int S_q, int h_q, int h_kv, int64_t s_kv_max,
   }
   int tpt, qtiles, tpw, passes;
   query_tiles(S_q, h_q / h_kv, &tpt, &qtiles, &tpw, &passes);
-  return pick_splits_host(B, passes, h_kv, s_kv_max, num_cus, split_policy(tpw, 128, false));
+  return pick_splits_host(B, passes, h_kv, s_kv_max, num_cus, split_policy(tpw, 128, false, S_q));
 }
 
 }  // extern "C"
@@ -456,12 +457,12 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
     if (st != GQA_OK) return st;
     int tpt, qtiles, tpw, passes;
     query_tiles(s_q, h_q / h_kv, &tpt, &qtiles, &tpw, &passes);
-    ns = pick_splits_host(B, passes, h_kv, s_kv_hint, num_cus, split_policy(tpw, d_head, !multi_entry));
+    ns = pick_splits_host(B, passes, h_kv, s_kv_hint, num_cus, split_policy(tpw, d_head, !multi_entry, s_q));
   }
   pl->ns = ns;
-  // a heuristic call keeps chunks of at least kMinChunk tokens, a
-  // single-token call of at most 4 sequences of at least one block
-  pl->min_chunk = n_splits > 0 ? 1 : (B <= 4 && !multi_entry ? kBlockTokens : kMinChunk);
+  // a heuristic call keeps chunks of at least kMinChunk tokens, a call of
+  // one query token over at most 4 sequences of at least one block
+  pl->min_chunk = n_splits > 0 ? 1 : (B <= 4 && s_q == 1 ? kBlockTokens : kMinChunk);
   pl->hint = s_kv_hint;
   pl->need = ws_bytes(B * s_q, h_q, d_head, ns);
   if (workspace) {
