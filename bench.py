@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E datasheet peak
 DEFAULT_WORKLOAD = "llama70b_gqa_b1_s8192"
 ROTATE_BYTES = 1 << 30
 KERNEL_SOURCES = ["gqa_common.h", "split_kv_mfma.h", "split_kv_valu.h", "merge.h", "fused_tail.h",
-                  "kv_append.h", "packed_offsets.h", "gqa_decode.hip"]
+                  "kv_append.h", "packed_offsets.h", "split_kv_tiles.h", "gqa_decode.hip"]
 
 
 def log(*a):

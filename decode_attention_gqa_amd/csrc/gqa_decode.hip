@@ -20,6 +20,7 @@
 #include "merge.h"
 #include "packed_offsets.h"
 #include "split_kv_mfma.h"
+#include "split_kv_tiles.h"
 #include "split_kv_valu.h"
 
 namespace {
@@ -63,12 +64,17 @@ constexpr SplitPolicy kOneTileMulti{2, 2, 4, 4096, false, false};
 // Two tiles per workgroup (multi-token decode), one workgroup per CU: one
 // round for a single sequence; chunks up to 16384 tokens.
 constexpr SplitPolicy kTwoTiles{1, 1, 4, 16384, false, false};
+// One tile per wave, eight per workgroup (multi-token decode), two workgroups
+// per CU: one round for a single sequence, up to two for a batch (ragged
+// B = 8, S_q = 16: 209.9 µs at two rounds, 227.9 at four).
+constexpr SplitPolicy kTileWavesPolicy{2, 1, 2, 16384, false, false};
 
 // single_token: a single-token entry point. The multi-token one never takes
 // the 8-wave count (so gqa_decode_multi_splits needs no d_head), and takes the
 // short-sequence count only for one query token, where it then plans like a
 // single-token call outside the 8-wave range.
 const SplitPolicy& split_policy(int tiles_per_wg, int d_head, bool single_token, int s_q) {
+  if (tiles_per_wg == gqa::kTileWaves) return kTileWavesPolicy;
   if (tiles_per_wg == 2) return kTwoTiles;
   if (single_token && d_head == 128) return kOneTile;
   return single_token || s_q == 1 ? kOneTile64 : kOneTileMulti;
@@ -170,7 +176,8 @@ size_t ws_bytes(int B, int h_q, int d, int n) { return ws_layout(B, h_q, d, n).t
 
 // ---------------------------------------------------------------- launches
 // Workgroup form of the matrix-core split kernel.
-enum class Form { kFourWave, kOneWave, kEightWave };
+// kTiles: the multi-token kernel with one query tile per wave (split_kv_tiles).
+enum class Form { kFourWave, kOneWave, kEightWave, kTiles };
 
 template <int D, int NREP>
 hipError_t launch_split(bool bf16, bool valu, Form form, dim3 grid, hipStream_t st, const gqa::SplitArgs& a) {
@@ -178,6 +185,8 @@ hipError_t launch_split(bool bf16, bool valu, Form form, dim3 grid, hipStream_t 
     hipLaunchKernelGGL((gqa::split_kv_valu<float, D, NREP>), grid, dim3(gqa::kThreads), 0, st, a);
   } else if (valu) {
     hipLaunchKernelGGL((gqa::split_kv_valu<__bf16, D, NREP>), grid, dim3(gqa::kThreads), 0, st, a);
+  } else if (form == Form::kTiles) {
+    hipLaunchKernelGGL((gqa::split_kv_tiles<D, NREP>), grid, dim3(64 * gqa::kTileWaves), 0, st, a);
   } else if (a.qtiles > a.passes) {               // two column tiles per workgroup
     hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, false, 2>), grid, dim3(gqa::kThreads), 0, st, a);
   } else if (form == Form::kOneWave) {
@@ -268,13 +277,33 @@ hipError_t launch_merge(bool out_bf16, int B, int h_q, hipStream_t st, const gqa
   return out_bf16 ? launch_merge_t<D, __bf16>((int)rows, st, a) : launch_merge_t<D, float>((int)rows, st, a);
 }
 
+// Multi-token calls whose sequences need this many query tiles, over at
+// least this many tokens in all (B times the longest length), take the
+// kernel with one tile per wave (split_kv_tiles: 8 tiles read each K/V block
+// once, through LDS); others take two tiles per workgroup (split_kv_mfma),
+// faster at fewer tiles and at shorter KV, where its repeated passes over the
+// KV hit in the caches. Measured at 70B shapes, µs per call, two-tile vs
+// one-tile-per-wave kernel: S = 8k, S_q = 16: 29.1 vs 31.9; 16k: 46.5 vs
+// 41.6; 32k: 84.4 vs 65.8; 64k, S_q = 8 / 16 / 64: 92.7 / 163 / 579 vs 81.8 /
+// 119.5 / 369; 16k, S_q = 8: 30.8 vs 32.5; ragged B = 8, S_q = 4 / 8 / 16:
+// 108.7 / 179.9 / 294.6 vs 123.1 / 155.2 / 209.9.
+constexpr int kTilesMinTiles = 8;
+constexpr int64_t kTilesMinTokens = 16384;
+constexpr int kTilesMinTilesLong = 4;          // fewer tiles take it only over longer KV
+constexpr int64_t kTilesMinTokensLong = 65536;
+
 // Query tokens per 16-column tile, tiles per sequence, tiles per workgroup
-// (two once a sequence needs two or more: each K/V block is then read once
-// for both) and workgroup passes per sequence over the KV range.
-void query_tiles(int s_q, int nrep, int* tpt, int* qtiles, int* tpw, int* passes) {
+// (two once a sequence needs two or more, each K/V block then read once for
+// both; kTileWaves for the one-tile-per-wave kernel) and workgroup passes per
+// sequence over the KV range. hint: the longest sequence (0: unknown).
+void query_tiles(int s_q, int nrep, int B, int64_t hint, int* tpt, int* qtiles, int* tpw, int* passes) {
   *tpt = s_q < 16 / nrep ? s_q : 16 / nrep;
   *qtiles = (s_q + *tpt - 1) / *tpt;
   *tpw = *qtiles >= 2 ? 2 : 1;
+  const int64_t tokens = hint > 0 ? (int64_t)B * hint : 0;
+  if ((*qtiles >= kTilesMinTiles && tokens >= kTilesMinTokens) ||
+      (*qtiles >= kTilesMinTilesLong && tokens >= kTilesMinTokensLong))
+    *tpw = gqa::kTileWaves;
   *passes = (*qtiles + *tpw - 1) / *tpw;
 }
 
@@ -386,7 +415,7 @@ int gqa_decode_multi_splits(int B, int S_q, int h_q, int h_kv, int64_t s_kv_max,
     if (st != GQA_OK) return st;
   }
   int tpt, qtiles, tpw, passes;
-  query_tiles(S_q, h_q / h_kv, &tpt, &qtiles, &tpw, &passes);
+  query_tiles(S_q, h_q / h_kv, B, s_kv_max, &tpt, &qtiles, &tpw, &passes);
   return pick_splits_host(B, passes, h_kv, s_kv_max, num_cus, split_policy(tpw, 128, false, S_q));
 }
 
@@ -456,7 +485,7 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
     int st = device_cus(&num_cus);
     if (st != GQA_OK) return st;
     int tpt, qtiles, tpw, passes;
-    query_tiles(s_q, h_q / h_kv, &tpt, &qtiles, &tpw, &passes);
+    query_tiles(s_q, h_q / h_kv, B, s_kv_hint, &tpt, &qtiles, &tpw, &passes);
     ns = pick_splits_host(B, passes, h_kv, s_kv_hint, num_cus, split_policy(tpw, d_head, !multi_entry, s_q));
   }
   pl->ns = ns;
@@ -517,7 +546,7 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
   const int direct = (merged && !fused && mfma && pl.ns == 1) ? 1 : 0;
   if (merged) *merged = fused || direct;
   int tpt, qtiles, tpw, passes;
-  query_tiles(s_q, h_q / h_kv, &tpt, &qtiles, &tpw, &passes);
+  query_tiles(s_q, h_q / h_kv, B, pl.hint, &tpt, &qtiles, &tpw, &passes);
   const int64_t* tok = kv_token_offsets;
   if (!tok && B > kScanMinBatch) {             // packed layout, many sequences: scan once
     hipLaunchKernelGGL(gqa::packed_offsets, dim3(1), dim3(1024), 0, stream, seq_lens, B, pl.tok);
@@ -539,6 +568,7 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
   if (g_ev_before && (e = hipEventRecord(g_ev_before, stream)) != hipSuccess)
     return fail(GQA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
   Form form = Form::kFourWave;
+  if (mfma && tpw == gqa::kTileWaves) form = Form::kTiles;
   if (mfma && s_q == 1) {
     form = split_form(pl, B, h_kv, d_head);
     if (fused) form = Form::kFourWave;             // the single-launch tail is built for 4 waves
@@ -641,9 +671,9 @@ int gqa_decode_attn_multi(const void* q, const void* k_cache, const void* v_cach
   if ((st = check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets, scale, GQA_DTYPE_BF16, 0))) return st;
   if ((st = check_shape(B, h_q, h_kv, d_head, n_splits, s_kv_hint))) return st;
   int tpt, qtiles, tpw, passes;
-  query_tiles(S_q, h_q / h_kv, &tpt, &qtiles, &tpw, &passes);
+  query_tiles(S_q, h_q / h_kv, B, s_kv_hint, &tpt, &qtiles, &tpw, &passes);
   if ((int64_t)B * passes > 65535)
-    return fail(GQA_ERR_INVALID_ARG, "B * ceil(query tiles / 2) must be <= 65535");
+    return fail(GQA_ERR_INVALID_ARG, "B * workgroup passes (ceil(query tiles / tiles per workgroup)) must be <= 65535");
   if ((int64_t)B * S_q * h_q > INT32_MAX) return fail(GQA_ERR_INVALID_ARG, "B * S_q * h_q must be < 2^31");
   const size_t qo = (size_t)B * S_q * h_q * d_head;
   if ((st = check_out(out, out_dtype, qo))) return st;

@@ -326,6 +326,9 @@ void split_kv_mfma(SplitArgs a) {
     }
     lim[t] = S - a.s_q + qi[t];                    // causal among the new tokens
   }
+  int lim0[TILES];                                 // the tile's smallest limit (its first token's)
+#pragma unroll
+  for (int t = 0; t < TILES; ++t) lim0[t] = S - a.s_q + (pass * TILES + t) * a.tpt;
 
   f32x4 acc[TILES][NT];
   SoftmaxState st[TILES];
@@ -360,13 +363,16 @@ void split_kv_mfma(SplitArgs a) {
     auto load = [&](KVRegs<D>& r, int bk) {
       const int64_t base = (int64_t)bk * 32 * row_bytes;
       const int nvb = min(32, ntok - bk * 32);
-      if (holds_new(bk, nvb))
+      if (holds_new(bk, nvb)) {
         load_block_new<D>(r, kb0 + base, vb0 + base, row_bytes, grp, n, nvb,
                           static_cast<const char*>(a.k_new) + src_new, static_cast<const char*>(a.v_new) + src_new);
-      else if (nvb == 32)
-        load_block<D>(r, kb0 + base, vb0 + base, full);
-      else
-        load_block<D>(r, kb0 + base, vb0 + base, lane_offsets<D>(row_bytes, grp, n, nvb));
+        return;
+      }
+      // Only the offsets depend on the branch: the loads after it are the
+      // same instructions on both paths.
+      LaneOffsets<D> o = full;
+      if (nvb < 32) o = lane_offsets<D>(row_bytes, grp, n, nvb);
+      load_block<D>(r, kb0 + base, vb0 + base, o);
     };
     auto step = [&](const KVRegs<D>& r, int bk) {
       const int nv = min(32, ntok - bk * 32);
@@ -374,7 +380,9 @@ void split_kv_mfma(SplitArgs a) {
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
         const int nvl = causal ? min(nv, lim[t] - ((int)t0 + bk * 32) + 1) : nv;
-        softmax_block<D>(r, qop[t], acc[t], st[t], a.scale_log2, grp, nv < 32 || causal, nvl, ph[t], pl[t]);
+        // The causal mask matters only in blocks past the tile's first token's limit.
+        const bool mask = nv < 32 || (causal && (int)t0 + bk * 32 + nv - 1 > lim0[t]);
+        softmax_block<D>(r, qop[t], acc[t], st[t], a.scale_log2, grp, mask, nvl, ph[t], pl[t]);
       }
       pv_block<D, TILES>(r, acc, ph, pl);
     };
@@ -383,17 +391,40 @@ void split_kv_mfma(SplitArgs a) {
     KVRegs<D> ra, rb;
     int blk = w;
     load(ra, blk);
-    while (true) {
-      int nb = blk + WAVES;
-      if (nb < nblk) load(rb, nb);
-      step(ra, blk);
-      if (nb >= nblk) break;
-      blk = nb;
-      nb = blk + WAVES;
-      if (nb < nblk) load(ra, nb);
-      step(rb, blk);
-      if (nb >= nblk) break;
-      blk = nb;
+    if constexpr (TILES == 2) {
+      // The loads of the next block are issued on every path that then
+      // computes the current one (the last block is computed outside the
+      // loop), so the wait before computing covers the current block's loads
+      // only: after a load that some path skips, the compiler waits for
+      // every load in flight. (With one tile the extra copies of the block
+      // code this takes would spill registers.)
+      while (blk + WAVES < nblk) {
+        load(rb, blk + WAVES);
+        step(ra, blk);
+        blk += WAVES;
+        if (blk + WAVES >= nblk) {
+          step(rb, blk);
+          blk = -1;                                // done
+          break;
+        }
+        load(ra, blk + WAVES);
+        step(rb, blk);
+        blk += WAVES;
+      }
+      if (blk >= 0) step(ra, blk);
+    } else {
+      while (true) {
+        int nb = blk + WAVES;
+        if (nb < nblk) load(rb, nb);
+        step(ra, blk);
+        if (nb >= nblk) break;
+        blk = nb;
+        nb = blk + WAVES;
+        if (nb < nblk) load(ra, nb);
+        step(rb, blk);
+        if (nb >= nblk) break;
+        blk = nb;
+      }
     }
   }
 

@@ -145,11 +145,15 @@ int gqa_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
  * S_q = 1 this equals gqa_decode_attn_ex. bf16 inputs (matrix-core kernel),
  * fp32 or bf16 out, 1 <= S_q <= GQA_MAX_QUERY_TOKENS. The (token, head)
  * columns fill 16-wide MFMA tiles of t = min(S_q, 16 / n_rep) tokens (the
- * columns single-token decode leaves empty when n_rep < 16), and one pass over
- * the KV range serves two tiles, so 2t tokens read the KV once; more tokens
- * take more passes. Workspace: gqa_decode_workspace_bytes(B * S_q, h_q,
- * d_head, n) with n = n_splits if > 0, else gqa_decode_multi_splits(B, S_q,
- * h_q, h_kv, s_kv_hint, 0). B * ceil(ceil(S_q / t) / 2) <= 65535. Other
+ * columns single-token decode leaves empty when n_rep < 16). A pass over the
+ * KV range serves two tiles (2t tokens read the KV once), or, when a sequence
+ * has at least 8 tiles and B * s_kv_hint >= 16384 tokens, or at least 4
+ * tiles and B * s_kv_hint >= 65536, eight tiles (one per wave, the K/V
+ * blocks shared through LDS); more tokens take more passes. The hint only
+ * picks the kernel and the split count: either kernel takes any length, and
+ * the two round differently. Workspace: gqa_decode_workspace_bytes(B * S_q,
+ * h_q, d_head, n) with n = n_splits if > 0, else gqa_decode_multi_splits(B,
+ * S_q, h_q, h_kv, s_kv_hint, 0). B * passes <= 65535. Other
  * arguments as in gqa_decode_attn_ex.
  */
 int gqa_decode_attn_multi(const void* q, const void* k_cache, const void* v_cache,
@@ -288,8 +292,11 @@ int gqa_decode_pick_splits(int B, int h_kv, int64_t s_kv_max, int num_cus);
 
 /* Split count gqa_decode_attn_multi uses when n_splits <= 0 (the same rule,
  * for its kernels: with two column tiles per workgroup, one workgroup per CU,
- * one round of them for a single sequence, chunks of up to 16384 tokens).
- * Negative status on invalid arguments or a failed device query. */
+ * one round of them for a single sequence; with eight (one per wave), two
+ * workgroups per CU, one round for a single sequence and up to two for a
+ * batch; chunks of up to 16384 tokens). s_kv_max is also the hint that picks
+ * the kernel (see gqa_decode_attn_multi). Negative status on invalid
+ * arguments or a failed device query. */
 int gqa_decode_multi_splits(int B, int S_q, int h_q, int h_kv, int64_t s_kv_max, int num_cus);
 
 /* Workspace bytes for n_splits chunks. Layout, each part starting on a

@@ -96,6 +96,7 @@ int main(void) {
   expect("pick ragged", gqa_decode_pick_splits(8, 8, 32768, 256), 32);
   expect("pick huge", gqa_decode_pick_splits(1, 1, (int64_t)1 << 40, 256), GQA_MAX_SPLITS);
   expect("multi S_q 4", gqa_decode_multi_splits(1, 4, 64, 8, 8192, 256), 32);
+  expect("multi S_q 16, 16k (one tile per wave)", gqa_decode_multi_splits(1, 16, 64, 8, 16384, 256), 64);
   expect("multi bad h_kv", gqa_decode_multi_splits(1, 4, 64, 0, 8192, 256), GQA_ERR_INVALID_ARG);
   expect("workspace bytes", (long)gqa_decode_workspace_bytes(8, 64, 128, 37),
          (long)(512 * 8 + ((8L * 64 * 37 * 128 * 4 + 255) / 256) * 256 + ((8L * 64 * 37 * 8 + 255) / 256) * 256 +

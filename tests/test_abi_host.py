@@ -190,6 +190,15 @@ def test_multi_split_heuristic_values(gqa):
     assert f(1, 4, 1 << 20) == 64                # chunks of up to 16384 tokens
     assert f(8, 4, 32768) == 16                  # a batch: the longest over four rounds
     assert f(1, 32, 4096, 32, 32) == 8           # MHA: 16 tokens per tile
+    # one tile per wave (8 tiles or more over 16384 tokens, 4 or more over
+    # 65536), two workgroups per CU: one round for one sequence, two for a batch
+    assert f(1, 16, 8192) == 8                   # 8 tiles, too short: two tiles per workgroup
+    assert f(1, 16, 16384) == 64
+    assert f(2, 16, 8192) == 32                  # B times the longest length counts
+    assert f(1, 8, 65535) == 16                  # 4 tiles: two per workgroup below 65536 tokens
+    assert f(1, 8, 65536) == 64
+    assert f(1, 64, 65536) == 16                 # 32 tiles: four passes
+    assert f(8, 16, 32768) == 16                 # a batch: the longest over two rounds
     assert f(1, 4, 8192, 64, 0) == -1
     assert f(1, 0, 8192) == -1
 

@@ -24,7 +24,10 @@ def run(inp, qm, n_splits=0, out_dtype="f32", poison=True, hint=True):
     q = torch.from_numpy(qm.view(np.int16)).cuda().view(torch.bfloat16)
     w = inp.w
     B, S_q = qm.shape[0], qm.shape[1]
-    s_max = int(inp.seq_lens.max()) if hint else 0
+    if hint is True:
+        s_max = int(inp.seq_lens.max())
+    else:
+        s_max = int(hint) if hint else 0               # False / 0: no hint; an int: that hint
     ns = gqa.multi_splits(B, S_q, w.h_q, w.h_kv, s_max, n_splits)
     ws = torch.empty(gqa.gqa_decode_workspace_bytes(B * S_q, w.h_q, w.d, ns), dtype=torch.uint8, device="cuda")
     if poison:
@@ -86,3 +89,49 @@ def test_single_query_token_equals_one_token_path():
     one = gqa.gqa_decode_attn_ex(q1, k, v, dl, scale=float(inp.scale), s_kv_hint=4000)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(got[:, 0], one.cpu().numpy().astype(np.float64))
+
+
+# A hint of LONG tokens over the batch sends calls with at least 4 query tiles
+# per sequence to the kernel with one tile per wave (8 per workgroup, K/V
+# blocks shared through LDS); no hint keeps them on the two-tile kernel.
+LONG = 65536
+
+
+@pytest.mark.parametrize("n_rep,S_q,d", [(8, 16, 128), (8, 16, 64), (8, 13, 128), (8, 64, 128), (4, 32, 128),
+                                         (2, 64, 64), (1, 64, 128), (16, 8, 128), (16, 5, 64)])
+def test_tile_waves_parity(n_rep, S_q, d):
+    """One tile per wave: ragged lengths (a partial last block, a sequence
+    shorter than one block), several passes (S_q = 64, n_rep = 8: 32 tiles),
+    a last tile with fewer tokens than it holds (S_q = 13, 5), split counts
+    from one chunk (written out directly) to more chunks than blocks; against
+    the oracle, and against the two-tile kernel (the same sums in another
+    chunking: 1e-3)."""
+    h_kv = 2
+    lens = [700, 37, 1500]
+    inp, qm = make(f"tiles_r{n_rep}_q{S_q}_d{d}", 3, S_q, n_rep * h_kv, h_kv, d, lens, 190 + n_rep + S_q + d)
+    for ns in (0, 1, 5, 64):
+        got, ref = check(f"tiles n_rep={n_rep} S_q={S_q} d={d} ns={ns}", inp, qm, n_splits=ns, hint=LONG)
+        two, _ = run(inp, qm, n_splits=ns, hint=False)
+        assert max_err(got, two) <= 1e-3
+
+
+def test_tile_waves_short_sequences_and_bf16_out():
+    """Sequences shorter than S_q (their early tokens attend nothing: zeros)
+    and chunks past some tokens' causal limit, on the one-tile-per-wave
+    kernel; bf16 output."""
+    lens = [0, 1, 2, 3, 5, 33, 64]
+    S_q = 16
+    inp, qm = make("tiles_short", len(lens), S_q, 16, 2, 128, lens, 197)
+    for ns in (0, 1, 8, 40):
+        got, ref = check(f"tiles short ns={ns}", inp, qm, n_splits=ns, hint=LONG)
+        assert np.all(got[0] == 0)                           # S_b = 0
+        assert np.all(got[1, :15] == 0) and np.all(got[2, :14] == 0)
+    check("tiles short bf16-out", inp, qm, out_dtype="bf16", hint=LONG)
+
+
+def test_tile_waves_70b_shape():
+    """70B heads, 16 query tokens, the kernel taken by the default rule (the
+    true longest length as hint, 2 x 20000 tokens)."""
+    inp, qm = make("tiles70b", 2, 16, 64, 8, 128, [20000, 3000], 198)
+    check("70B S_q=16", inp, qm)
+    check("70B S_q=16 bf16-out", inp, qm, out_dtype="bf16")

@@ -92,25 +92,40 @@ def test_random_multi_token_case(i):
     """gqa_decode_attn_multi on seeded draws: S_q in [1, 64] (one or two
     column tiles per workgroup), lengths shorter than S_q included, split
     count and hint varied; against oracle.attend_multi."""
+    multi_case(i, 7000, long_hint=False)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_multi_token_tile_waves_case(i):
+    """The same draws with S_q >= 8 and a hint of 65536 tokens or more over
+    the batch, which sends every call with at least 4 query tiles per
+    sequence to the kernel with one tile per wave."""
+    multi_case(i, 7500, long_hint=True)
+
+
+def multi_case(i, seed0, long_hint):
     import torch
 
     import decode_attention_gqa_amd as gqa
-    r = np.random.default_rng(7000 + i)
+    r = np.random.default_rng(seed0 + i)
     B = int(r.integers(1, 6))
     h_kv = int(r.choice([1, 2, 8]))
     n_rep = int(r.choice([1, 4, 8, 16]))
     while h_kv * n_rep > 64:
         h_kv //= 2
     h_q, d = h_kv * n_rep, int(r.choice([64, 128]))
-    S_q = int(r.choice([1, 2, 3, 5, 8, 16, 33, 64]))
+    S_q = int(r.choice([8, 13, 16, 33, 64] if long_hint else [1, 2, 3, 5, 8, 16, 33, 64]))
     lens = r.integers(0, int(r.choice([50, 600, 4000])) + 1, size=B).astype(np.int32)
     ns = int(r.choice([0, 0, 1, 3, 40]))
-    hint = int(lens.max()) if r.random() < 0.7 else 0
+    if long_hint:
+        hint = max(int(lens.max()), 65536 // B + 1)
+    else:
+        hint = int(lens.max()) if r.random() < 0.7 else 0
     out_bf16 = bool(r.random() < 0.25)
-    print(f"[multi case {i}] B={B} S_q={S_q} h_q={h_q} h_kv={h_kv} d={d} lens={lens.tolist()} ns={ns} "
+    print(f"[multi case {seed0 + i}] B={B} S_q={S_q} h_q={h_q} h_kv={h_kv} d={d} lens={lens.tolist()} ns={ns} "
           f"hint={hint} out={'bf16' if out_bf16 else 'f32'}", flush=True)
-    inp = workloads.custom(f"rmulti{i}", B=B, h_q=h_q, h_kv=h_kv, d=d, seq_lens=lens, seed=7000 + i)
-    qm = workloads.normals(7000 + i, 9, B * S_q * h_q * d).reshape(B, S_q, h_q, d)
+    inp = workloads.custom(f"rmulti{seed0 + i}", B=B, h_q=h_q, h_kv=h_kv, d=d, seq_lens=lens, seed=seed0 + i)
+    qm = workloads.normals(seed0 + i, 9, B * S_q * h_q * d).reshape(B, S_q, h_q, d)
     ref = oracle.attend_multi(qm, inp.k, inp.v, inp.seq_lens, inp.scale, h_kv, dtype="bf16")
     _, k, v, dl = to_device(inp)
     q = torch.from_numpy(np.ascontiguousarray(qm).view(np.int16)).cuda().view(torch.bfloat16)
@@ -119,7 +134,7 @@ def test_random_multi_token_case(i):
     torch.cuda.synchronize()
     err = max_err(out.float().cpu().numpy().astype(np.float64), ref)
     tol = TOL_BF16 if out_bf16 else TOL_F32
-    print(f"[multi case {i}] max_abs_err={err:.3e} tol={tol:.1e}", flush=True)
+    print(f"[multi case {seed0 + i}] max_abs_err={err:.3e} tol={tol:.1e}", flush=True)
     assert err <= tol
 
 
