@@ -24,12 +24,14 @@
 // max over a column's 4 lane groups (two permlane swaps). Query heads
 // n_rep..15 of the 16-wide tile are zero padding.
 //
-// Data movement: K and V go straight from HBM to registers with 16-byte
-// non-temporal loads (nothing is staged in LDS; the group's heads share each K/V register
-// inside the MFMA). A lane's 8 V loads are 8 tokens x 8 consecutive
-// dimensions; an in-register 8x8 transpose of 16-bit values turns them into
-// the MFMA A operand (8 tokens of one dimension). K is used in its natural
-// row layout. Every K and V byte of the chunk is read exactly once.
+// Data movement: K and V go from HBM to registers with 16-byte non-temporal
+// loads, each instruction reading whole rows (the group's heads share each
+// K/V register inside the MFMA; no workgroup-wide staging). A lane's 8 V
+// loads are 8 tokens x 8 consecutive dimensions; an in-register 8x8
+// transpose of 16-bit values turns them into the MFMA A operand (8 tokens of
+// one dimension). K, loaded a row piece per lane, passes through a small
+// per-wave LDS region on its way to the A-operand layout (a row per lane%16).
+// Every K and V byte of the chunk is read exactly once.
 //
 // The softmax probabilities are split into bf16 hi + lo parts and both are
 // multiplied with V, so P.V keeps about 16 significant bits of P (bf16 alone
@@ -51,8 +53,27 @@ struct MfmaTile {
 // Per-lane registers of one 32-token block.
 template <int D>
 struct KVRegs {
-  uint4 k[2][MfmaTile<D>::KS];        // K rows: tile x (tokens 16x + lane%16), step kk
+  // K: as loaded, piece i is row KRowsPerLoad*i + lane / KPieces, bytes
+  // 16*(lane % KPieces) (whole rows per load instruction); after
+  // k_to_operand, k[x][kk] is the MFMA A operand: row 16x + lane%16, bytes
+  // 16*(lane/16) + 64*kk.
+  uint4 k[2][MfmaTile<D>::KS];
   uint32_t v[8][MfmaTile<D>::VW];     // V: token slot j, VW dwords of consecutive dims
+};
+
+// K rows in the layout they are loaded in: a 16-byte piece per lane, whole
+// rows per instruction (4 rows of 256 bytes at d = 128, 8 of 128 at d = 64).
+// The MFMA wants 16 rows per instruction instead (a row per lane%16), which as
+// loads reach 16 rows x 64 bytes per instruction and measured 0.9 µs slower
+// over 32 MiB than whole rows; the wave turns one layout into the other
+// through LDS (k_to_operand).
+template <int D>
+struct KLoad {
+  static constexpr int KPieces = D * 2 / 16;          // 16-byte pieces per row
+  static constexpr int KRowsPerLoad = 64 / KPieces;   // rows per load instruction
+  static constexpr int ROW = D * 2 + 16;              // padded row in LDS: the 16 lanes of a lane
+                                                      // group read 16 rows at one column
+  static constexpr int BYTES = 32 * ROW;              // one wave's block of K rows
 };
 
 // Token (within the 32-token block) that lane group `grp` holds in slot j of
@@ -63,22 +84,26 @@ __device__ __forceinline__ int slot_token(int grp, int j) {
 }
 
 // Byte offsets, from the first K (or V) row of a block, of the 16-byte
-// pieces a lane loads: K row of token 16x + n at dims 8*grp (+32*kk through
-// the instruction's immediate offset), V row of token slot_token(grp, j) at
-// dims NT*n. Tokens at or past nv (a chunk's last, partial block) are clamped
-// to nv - 1: read again, and masked out of the softmax.
+// pieces a lane loads: K piece i (see KVRegs), V row of token
+// slot_token(grp, j) at dims NT*n. Tokens at or past nv (a chunk's last,
+// partial block) are clamped to nv - 1: read again, and masked out of the
+// softmax.
 template <int D>
 struct LaneOffsets {
-  uint32_t k[2];
+  uint32_t k[2 * MfmaTile<D>::KS];
   uint32_t v[8];
 };
 
 template <int D>
 __device__ __forceinline__ LaneOffsets<D> lane_offsets(uint32_t row_bytes, int grp, int n, int nv) {
-  constexpr int NT = MfmaTile<D>::NT;
+  constexpr int NT = MfmaTile<D>::NT, KS = MfmaTile<D>::KS;
+  using KL = KLoad<D>;
+  const int lane = 16 * grp + n;
   LaneOffsets<D> o;
 #pragma unroll
-  for (int x = 0; x < 2; ++x) o.k[x] = (uint32_t)min(16 * x + n, nv - 1) * row_bytes + 16u * grp;
+  for (int i = 0; i < 2 * KS; ++i)
+    o.k[i] = (uint32_t)min(KL::KRowsPerLoad * i + lane / KL::KPieces, nv - 1) * row_bytes +
+             16u * (lane % KL::KPieces);
 #pragma unroll
   for (int j = 0; j < 8; ++j) o.v[j] = (uint32_t)min(slot_token(grp, j), nv - 1) * row_bytes + 2u * NT * n;
   return o;
@@ -89,9 +114,7 @@ __device__ __forceinline__ void load_block(KVRegs<D>& r, const char* kb, const c
                                            const LaneOffsets<D>& o) {
   constexpr int KS = MfmaTile<D>::KS, VW = MfmaTile<D>::VW;
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) r.k[x][kk] = load_stream16(kb + o.k[x] + 64 * kk);
+  for (int i = 0; i < 2 * KS; ++i) r.k[i / KS][i % KS] = load_stream16(kb + o.k[i]);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if constexpr (VW == 4) {
@@ -112,12 +135,13 @@ __device__ __forceinline__ void load_block_new(KVRegs<D>& r, const char* kb, con
                                                uint32_t row_bytes, int grp, int n, int nv,
                                                const char* k_row, const char* v_row) {
   constexpr int KS = MfmaTile<D>::KS, NT = MfmaTile<D>::NT, VW = MfmaTile<D>::VW;
+  using KL = KLoad<D>;
+  const int lane = 16 * grp + n;
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int t = min(16 * x + n, nv - 1);
+  for (int i = 0; i < 2 * KS; ++i) {
+    const int t = min(KL::KRowsPerLoad * i + lane / KL::KPieces, nv - 1);
     const char* row = (t == nv - 1) ? k_row : kb + (uint32_t)t * row_bytes;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) r.k[x][kk] = load_stream16(row + 16 * grp + 64 * kk);
+    r.k[i / KS][i % KS] = load_stream16(row + 16 * (lane % KL::KPieces));
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -146,6 +170,28 @@ __device__ __forceinline__ bf16x8 v_tile(const KVRegs<D>& r, int nt) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) pa[i] = __builtin_amdgcn_perm(r.v[2 * i + 1][w], r.v[2 * i][w], sel);
   return __builtin_bit_cast(bf16x8, a);
+}
+
+// K from its load layout to the MFMA A-operand layout, through this wave's
+// KLoad<D>::BYTES of LDS (rows padded to KLoad<D>::ROW bytes). Only this wave
+// touches the region, and a wave's LDS accesses complete in order.
+template <int D>
+__device__ __forceinline__ void k_to_operand(KVRegs<D>& r, char* kt, int grp, int n) {
+  constexpr int KS = MfmaTile<D>::KS;
+  using KL = KLoad<D>;
+  const int lane = 16 * grp + n;
+#pragma unroll
+  for (int i = 0; i < 2 * KS; ++i)
+    *reinterpret_cast<uint4*>(kt + (KL::KRowsPerLoad * i + lane / KL::KPieces) * KL::ROW +
+                              16 * (lane % KL::KPieces)) = r.k[i / KS][i % KS];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+      r.k[x][kk] = *reinterpret_cast<const uint4*>(kt + (16 * x + n) * KL::ROW + 16 * grp + 64 * kk);
 }
 
 struct SoftmaxState {
@@ -358,6 +404,7 @@ void split_kv_mfma(SplitArgs a) {
     const char* kb0 = reinterpret_cast<const char*>(kbase);
     const char* vb0 = reinterpret_cast<const char*>(vbase);
     const LaneOffsets<D> full = lane_offsets<D>(row_bytes, grp, n, 32);
+    __shared__ __attribute__((aligned(16))) char kt[WAVES][KLoad<D>::BYTES];   // each wave's K transpose
     // APPEND: the block whose last token ends the sequence holds the new token.
     auto holds_new = [&](int bk, int nvb) { return APPEND && appended && t0 + bk * 32 + nvb == S; };
     auto load = [&](KVRegs<D>& r, int bk) {
@@ -374,7 +421,8 @@ void split_kv_mfma(SplitArgs a) {
       if (nvb < 32) o = lane_offsets<D>(row_bytes, grp, n, nvb);
       load_block<D>(r, kb0 + base, vb0 + base, o);
     };
-    auto step = [&](const KVRegs<D>& r, int bk) {
+    auto step = [&](KVRegs<D>& r, int bk) {
+      k_to_operand<D>(r, kt[w], grp, n);
       const int nv = min(32, ntok - bk * 32);
       bf16x8 ph[TILES], pl[TILES];
 #pragma unroll
