@@ -286,7 +286,9 @@ hipError_t launch_merge(bool out_bf16, int B, int h_q, hipStream_t st, const gqa
 // one-tile-per-wave kernel: S = 8k, S_q = 16: 29.1 vs 31.9; 16k: 46.5 vs
 // 41.6; 32k: 84.4 vs 65.8; 64k, S_q = 8 / 16 / 64: 92.7 / 163 / 579 vs 81.8 /
 // 119.5 / 369; 16k, S_q = 8: 30.8 vs 32.5; ragged B = 8, S_q = 4 / 8 / 16:
-// 108.7 / 179.9 / 294.6 vs 123.1 / 155.2 / 209.9.
+// 108.7 / 179.9 / 294.6 vs 123.1 / 155.2 / 209.9. At the thresholds, after
+// the two-tile kernel's K loads got faster: S_q = 16, 16383 vs 16384 tokens:
+// 43.7 vs 42.1; S_q = 8, 65535 vs 65536: 85.6 vs 74.2.
 constexpr int kTilesMinTiles = 8;
 constexpr int64_t kTilesMinTokens = 16384;
 constexpr int kTilesMinTilesLong = 4;          // fewer tiles take it only over longer KV
