@@ -135,3 +135,41 @@ def test_tile_waves_70b_shape():
     inp, qm = make("tiles70b", 2, 16, 64, 8, 128, [20000, 3000], 198)
     check("70B S_q=16", inp, qm)
     check("70B S_q=16 bf16-out", inp, qm, out_dtype="bf16")
+
+
+@pytest.mark.parametrize("hint", [False, LONG])
+def test_multi_offset_layout_with_nan_gaps(hint):
+    """Explicit token offsets, sequences stored in reverse order with rows of
+    NaN between them: a read outside a sequence's rows would show as NaN in
+    the output. Both multi-token kernels (no hint: two tiles; a long hint:
+    one tile per wave)."""
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    lens = np.array([300, 0, 77, 1025, 33], dtype=np.int32)
+    B, S_q, h_kv, n_rep, d = len(lens), 16, 2, 8, 128
+    inp, qm = make("multi_offsets", B, S_q, n_rep * h_kv, h_kv, d, lens, 199)
+    ref = oracle.attend_multi(qm, inp.k, inp.v, inp.seq_lens, inp.scale, h_kv, dtype="bf16")
+    _, k, v, dl = to_device(inp)
+    packed = np.concatenate([[0], np.cumsum(lens[:-1])]).astype(np.int64)
+    gaps = [5, 40, 0, 17, 3]
+    start, pos = np.zeros(B, dtype=np.int64), 0
+    for b in reversed(range(B)):
+        start[b] = pos
+        pos += int(lens[b]) + gaps[b]
+    kp = torch.full((pos, h_kv, d), float("nan"), dtype=k.dtype, device="cuda")
+    vp = torch.full_like(kp, float("nan"))
+    for b in range(B):
+        n = int(lens[b])
+        kp[start[b]:start[b] + n] = k[packed[b]:packed[b] + n]
+        vp[start[b]:start[b] + n] = v[packed[b]:packed[b] + n]
+    offs = torch.from_numpy(start).cuda()
+    q = torch.from_numpy(np.ascontiguousarray(qm).view(np.int16)).cuda().view(torch.bfloat16)
+    for ns in (0, 1, 7):
+        out = gqa.gqa_decode_attn_multi(q, kp, vp, dl, scale=float(inp.scale), n_splits=ns,
+                                        s_kv_hint=int(hint) if hint else 0, kv_token_offsets=offs)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        err = max_err(got, ref)
+        print(f"[multi] offsets hint={hint} ns={ns}: max_abs_err={err:.3e}", flush=True)
+        assert np.all(np.isfinite(got)) and err <= TOL_F32
