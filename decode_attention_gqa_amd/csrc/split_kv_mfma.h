@@ -249,11 +249,20 @@ __device__ __forceinline__ void softmax_block(const KVRegs<D>& r, const bf16x8 (
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
   }
+  // Two values per conversion (round to nearest even, as the scalar cast);
+  // a bf16 read back as fp32 is its bits in the upper half.
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const __bf16 h = (__bf16)p[j];
-    ph[j] = h;
-    pl[j] = (__bf16)(p[j] - (float)h);
+  for (int j = 0; j < 8; j += 2) {
+    const bf16x2_t h = __builtin_convertvector((f32x2_t){p[j], p[j + 1]}, bf16x2_t);
+    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+    const float h0 = __uint_as_float(hb << 16), h1 = __uint_as_float(hb & 0xFFFF0000u);
+    const bf16x2_t l = __builtin_convertvector((f32x2_t){p[j] - h0, p[j + 1] - h1}, bf16x2_t);
+    ph[j] = h[0];
+    ph[j + 1] = h[1];
+    pl[j] = l[0];
+    pl[j + 1] = l[1];
   }
 }
 
