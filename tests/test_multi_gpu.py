@@ -173,3 +173,22 @@ def test_multi_offset_layout_with_nan_gaps(hint):
         err = max_err(got, ref)
         print(f"[multi] offsets hint={hint} ns={ns}: max_abs_err={err:.3e}", flush=True)
         assert np.all(np.isfinite(got)) and err <= TOL_F32
+
+
+@pytest.mark.parametrize("scale", [-0.088, 0.0])
+@pytest.mark.parametrize("hint", [False, LONG])
+def test_multi_negative_and_zero_scale(scale, hint):
+    """Both multi-token kernels with a negative and a zero scale."""
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    lens = [700, 37, 1500]
+    inp, qm = make("multi_scale", 3, 16, 16, 2, 128, lens, 200)
+    ref = oracle.attend_multi(qm, inp.k, inp.v, inp.seq_lens, np.float32(scale), 2, dtype="bf16")
+    _, k, v, dl = to_device(inp)
+    q = torch.from_numpy(np.ascontiguousarray(qm).view(np.int16)).cuda().view(torch.bfloat16)
+    out = gqa.gqa_decode_attn_multi(q, k, v, dl, scale=scale, s_kv_hint=int(hint) if hint else 0)
+    torch.cuda.synchronize()
+    err = max_err(out.cpu().numpy().astype(np.float64), ref)
+    print(f"[multi] scale={scale} hint={hint}: max_abs_err={err:.3e}", flush=True)
+    assert err <= TOL_F32

@@ -336,3 +336,25 @@ def test_single_sequence_eight_wave(S, d, n_rep):
     report(f"8-wave S={S} d={d} n_rep={n_rep}", max_err(got, ref), used, TOL_F32)
     got, used = run_gpu(inp, out_dtype="bf16")
     report(f"8-wave S={S} d={d} n_rep={n_rep} bf16 out", max_err(got, ref), used, TOL_BF16)
+
+
+@pytest.mark.parametrize("scale", [-0.088, 0.0, 0.6])
+def test_negative_zero_and_large_scale(scale):
+    """The matrix-core kernels take the scale's sign with Q and its size
+    inside the exponent; a zero scale (every attended position weighs the
+    same) and a large one (a peaky softmax) too. The 8-wave, 4-wave and
+    one-wave forms and the vector-ALU kernel, against the oracle."""
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    cases = [("8-wave", dict(B=1, h_q=64, h_kv=8, d=128, seq_lens=[8192])),
+             ("4-wave", dict(B=3, h_q=16, h_kv=2, d=128, seq_lens=[700, 37, 1500])),
+             ("one-wave", dict(B=200, h_q=8, h_kv=2, d=64, seq_lens=[40 + (i * 7) % 90 for i in range(200)]))]
+    for name, kw in cases:
+        inp = workloads.custom(f"scale_{name}", seed=61, **kw)
+        ref = oracle.attend(inp.q, inp.k, inp.v, inp.seq_lens, np.float32(scale), kw["h_kv"], dtype="bf16")
+        q, k, v, dl = to_device(inp)
+        for valu in (False, True):
+            out = gqa.gqa_decode_attn_ex(q, k, v, dl, scale=scale, s_kv_hint=int(max(kw["seq_lens"])), valu=valu)
+            torch.cuda.synchronize()
+            report(f"scale={scale} {name} valu={valu}", max_err(out.cpu().numpy().astype(np.float64), ref), 0, TOL_F32)
