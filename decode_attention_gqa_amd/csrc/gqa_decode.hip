@@ -188,7 +188,10 @@ hipError_t launch_split(bool bf16, bool valu, Form form, dim3 grid, hipStream_t 
   } else if (form == Form::kTiles) {
     hipLaunchKernelGGL((gqa::split_kv_tiles<D, NREP>), grid, dim3(64 * gqa::kTileWaves), 0, st, a);
   } else if (a.qtiles > a.passes) {               // two column tiles per workgroup
-    hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, false, 2>), grid, dim3(gqa::kThreads), 0, st, a);
+    if (form == Form::kEightWave)
+      hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, false, 2, 8>), grid, dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, false, 2>), grid, dim3(gqa::kThreads), 0, st, a);
   } else if (form == Form::kOneWave) {
     hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, false, 1, 1>), grid, dim3(64), 0, st, a);
   } else if (form == Form::kEightWave) {
@@ -537,6 +540,18 @@ Form split_form(const Plan& pl, int B, int h_kv, int d_head) {
   return Form::kFourWave;
 }
 
+// Two query tiles per workgroup: eight waves (one block each, one register
+// buffer) instead of four when every chunk holds 5 to 8 blocks and the grid
+// is one workgroup per CU or less.
+bool two_tile_eight_waves(const Plan& pl, int64_t units, int h_kv) {
+  if (pl.hint <= 0) return false;
+  const int64_t per_chunk = (pl.hint + pl.ns - 1) / pl.ns;
+  const int64_t tok = std::min<int64_t>(pl.hint, std::max<int64_t>(per_chunk, pl.min_chunk));
+  int cus = 0;
+  if (device_cus(&cus) != GQA_OK) return false;
+  return tok > 4 * kBlockTokens && tok <= 8 * kBlockTokens && (int64_t)pl.ns * h_kv * units <= cus;
+}
+
 // direct: the caller merges nothing afterwards; with one chunk per sequence
 // the split kernel then writes out itself (returned in *merged).
 int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_cache,
@@ -571,6 +586,7 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
     return fail(GQA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
   Form form = Form::kFourWave;
   if (mfma && tpw == gqa::kTileWaves) form = Form::kTiles;
+  if (mfma && tpw == 2 && !fused && two_tile_eight_waves(pl, B * passes, h_kv)) form = Form::kEightWave;
   if (mfma && s_q == 1) {
     form = split_form(pl, B, h_kv, d_head);
     if (fused) form = Form::kFourWave;             // the single-launch tail is built for 4 waves

@@ -295,11 +295,11 @@ __device__ __forceinline__ void pv_block(const KVRegs<D>& r, f32x4 (&acc)[TILES]
 // they share the block's V^T operands. Twice the accumulators leave room for
 // one workgroup per CU only (one wave per SIMD).
 template <int D, int NREP, bool APPEND = false, int TILES = 1, int WAVES = kWaves>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(TILES == 1 ? 2 : 1)))
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(TILES == 1 || WAVES == 8 ? 2 : 1)))
 void split_kv_mfma(SplitArgs a) {
   constexpr int KS = MfmaTile<D>::KS, NT = MfmaTile<D>::NT;
   constexpr int THREADS = 64 * WAVES;
-  static_assert(WAVES == kWaves || ((WAVES == 1 || WAVES == 8) && TILES == 1), "1 or 8 waves: one column tile");
+  static_assert(WAVES == kWaves || (WAVES == 1 && TILES == 1) || WAVES == 8, "1 wave: one column tile");
   static_assert(!APPEND || 2 * (D * 2 / 16) <= 64 * WAVES, "the new row's copy takes one thread per 16 bytes");
   static_assert(NREP >= 1 && NREP <= 16, "one 16-wide MFMA tile holds the query heads of a group");
   static_assert(TILES == 1 || (TILES == 2 && !APPEND), "two tiles serve multi-token decode only");
@@ -449,7 +449,18 @@ void split_kv_mfma(SplitArgs a) {
     KVRegs<D> ra, rb;
     int blk = w;
     load(ra, blk);
-    if constexpr (TILES == 2) {
+    if constexpr (TILES == 2 && WAVES == 8) {
+      // Two tiles with eight waves: one register buffer (two would not fit
+      // next to two tiles' state at two waves per SIMD); the host takes this
+      // form only where every wave has one block, so nothing waits on a load
+      // that a second buffer could have hidden.
+      while (true) {
+        step(ra, blk);
+        blk += WAVES;
+        if (blk >= nblk) break;
+        load(ra, blk);
+      }
+    } else if constexpr (TILES == 2) {
       // The loads of the next block are issued on every path that then
       // computes the current one (the last block is computed outside the
       // loop), so the wait before computing covers the current block's loads

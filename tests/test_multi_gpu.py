@@ -192,3 +192,19 @@ def test_multi_negative_and_zero_scale(scale, hint):
     err = max_err(out.cpu().numpy().astype(np.float64), ref)
     print(f"[multi] scale={scale} hint={hint}: max_abs_err={err:.3e}", flush=True)
     assert err <= TOL_F32
+
+
+@pytest.mark.parametrize("n_rep,S_q,d", [(8, 4, 128), (8, 3, 64), (4, 8, 128), (1, 32, 128), (2, 16, 64)])
+def test_two_tiles_eight_waves(n_rep, S_q, d):
+    """Two tiles per workgroup on eight waves (one block each): taken with a
+    length hint when chunks hold 5 to 8 blocks and the grid fits one round;
+    a partial last block, a sequence shorter than S_q's causal span. Against
+    the oracle, and against the four-wave form (no hint) within 1e-3."""
+    h_kv = 2
+    for lens, ns in (([700, 37, 1500], 8), ([4000], 16)):
+        inp, qm = make(f"t2w8_r{n_rep}_q{S_q}_d{d}", len(lens), S_q, n_rep * h_kv, h_kv, d, lens,
+                       210 + n_rep + S_q + d + len(lens))
+        got, ref = check(f"two tiles, 8 waves n_rep={n_rep} S_q={S_q} d={d} lens={lens} ns={ns}", inp, qm,
+                         n_splits=ns, hint=True)
+        four, _ = run(inp, qm, n_splits=ns, hint=False)
+        assert max_err(got, four) <= 1e-3
