@@ -208,3 +208,16 @@ def test_two_tiles_eight_waves(n_rep, S_q, d):
                          n_splits=ns, hint=True)
         four, _ = run(inp, qm, n_splits=ns, hint=False)
         assert max_err(got, four) <= 1e-3
+
+
+def test_two_tiles_eight_waves_with_a_hint_below_the_lengths():
+    """A hint below the true lengths picks the eight-wave two-tile form for
+    chunks that turn out longer than 8 blocks: its waves then take two blocks
+    each, one after the other (no second register buffer)."""
+    inp, qm = make("t2w8_lowhint", 2, 4, 16, 2, 128, [4000, 3100], 230)
+    ref = oracle.attend_multi(qm, inp.k, inp.v, inp.seq_lens, inp.scale, 2, dtype="bf16")
+    for ns in (10, 12):
+        got, _ = run(inp, qm, n_splits=ns, hint=2000)   # 2000 / ns tokens per chunk by the hint
+        err = max_err(got, ref)
+        print(f"[multi] eight-wave two tiles, hint 2000 < 4000, ns={ns}: max_abs_err={err:.3e}", flush=True)
+        assert err <= TOL_F32
