@@ -12,6 +12,7 @@ import types
 import pytest
 
 import oracle
+import test_oracle_append as A
 import test_oracle_merge as M
 import test_oracle_multi as MM
 import test_oracle_pins as P
@@ -47,6 +48,12 @@ MUTANTS = {
     "multi_position_from_start": ("p = S - S_q + i", "p = min(S - 1, i + S // 2)"),
     "multi_values_not_causal": ("out[b, i, hs, :] = (e / e.sum(axis=1, keepdims=True)) @ Vg[:p + 1]",
                                 "out[b, i, hs, :] = (e / e.sum(axis=1, keepdims=True)) @ Vg[S - p - 1:]"),
+    "scores_scale_dropped": ("return float(np.float32(scale)) * (k_rows @ q_row)", "return k_rows @ q_row"),
+    "scores_sign_flipped": ("return float(np.float32(scale)) * (k_rows @ q_row)",
+                            "return -float(np.float32(scale)) * (k_rows @ q_row)"),
+    "append_one_row_late": ("pos = int(lens[b]) + i", "pos = int(lens[b]) + i + 1"),
+    "append_lengths_not_clamped": ("np.minimum(lens + n_new, capacity)", "(lens + n_new)"),
+    "append_k_into_v": ("vc[off + pos] = v_new[b, i]", "vc[off + pos] = k_new[b, i]"),
     "fanout_east_first": ("            if inbox_w[i] is not None:\n                state[i] = merge(state[i], inbox_w[i])\n                order[i].append(inbox_w_org[i])\n            if inbox_e[i] is not None:\n                state[i] = merge(state[i], inbox_e[i])\n                order[i].append(inbox_e_org[i])",
                           "            if inbox_e[i] is not None:\n                state[i] = merge(state[i], inbox_e[i])\n                order[i].append(inbox_e_org[i])\n            if inbox_w[i] is not None:\n                state[i] = merge(state[i], inbox_w[i])\n                order[i].append(inbox_w_org[i])"),
 }
@@ -72,7 +79,8 @@ def pin_checks():
           P.test_identical_value_rows_give_that_row, P.test_one_hot_dominant_score_selects_its_row,
           P.test_large_scores_stay_finite_and_exact, P.test_head_mapping_is_contiguous_groups,
           P.test_token_offsets_follow_packed_layout, P.test_ragged_batch_equals_independent_sequences,
-          P.test_shift_of_all_scores_changes_nothing, P.test_output_inside_value_hull]
+          P.test_shift_of_all_scores_changes_nothing, P.test_output_inside_value_hull,
+          P.test_scores_on_hand_values, P.test_scores_triplet_finalize_is_brute_force]
     c += [lambda: M.test_whole_triplet_equals_unsplit(17),
           lambda: M.test_random_chunkings_with_empty_chunks(257, 8, 1),
           M.test_size_one_chunks_every_order, M.test_tree_merge_equals_sequential,
@@ -84,11 +92,19 @@ def pin_checks():
     c += [MM.test_single_query_token_is_attend, lambda: MM.test_each_token_is_brute_force_on_its_prefix(3),
           MM.test_future_positions_do_not_matter, MM.test_last_token_sees_everything,
           MM.test_more_query_tokens_than_cached_positions]
+    c += [A.test_rows_land_where_expected, A.test_explicit_offsets,
+          A.test_append_then_attend_equals_attend_on_full_cache]
     return c
 
 
-NAMES = ["NEG_INF", "attend", "attend_multi", "fanout", "finalize", "merge", "scores", "token_offsets",
-         "triplet", "widen"]
+NAMES = ["NEG_INF", "attend", "attend_multi", "fanout", "finalize", "kv_append", "merge", "scores",
+         "token_offsets", "triplet", "widen"]
+
+
+def test_every_exported_function_is_swapped():
+    """Every name the oracle package exports is replaced by the mutant's, so a
+    mistake planted in any exported function reaches the pins."""
+    assert sorted(NAMES) == sorted(oracle.__all__)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

@@ -218,3 +218,28 @@ def test_workload_shapes_match_printed_llama2_configs():
     w7 = workloads.WORKLOADS["llama2_7b_mha_s4096"]
     assert w7.h_q == heads["heads"]["7B"] and w7.h_kv == w7.h_q   # MHA: n_rep = 1
     assert "7B" in heads["multi_head_attention"]
+
+
+def test_scores_on_hand_values():
+    """s_t = scale * <q, K_t>, worked by hand: q = (1, 2, -1), scale 0.5,
+    K rows (1, 0, 0), (0, 1, 1), (2, -1, 3) -> 0.5 * (1, 1, -3)."""
+    q = np.array([1.0, 2.0, -1.0])
+    k = np.array([[1.0, 0.0, 0.0], [0.0, 1.0, 1.0], [2.0, -1.0, 3.0]])
+    np.testing.assert_array_equal(oracle.scores(q, k, np.float32(0.5)), [0.5, 0.5, -1.5])
+    # the scale is the float32 value the GPU receives, widened
+    np.testing.assert_array_equal(oracle.scores(np.array([1.0]), np.array([[1.0]]), 0.1),
+                                  [float(np.float32(0.1))])
+
+
+def test_scores_triplet_finalize_is_brute_force():
+    """The chunk pieces composed by hand (scores of one head, its triplet,
+    o / l) give the brute-force attention of that head, with a scale that is
+    neither 1 nor 1/sqrt(d) and a negative one."""
+    rng = np.random.default_rng(14)
+    q, k, v, sl = rand_case(rng, 1, 2, 1, 5, [23], sigma=2.0)
+    for scale in (np.float32(0.37), np.float32(-1.3)):
+        ref = np.array(attend_brute(q.tolist(), k.tolist(), v.tolist(), sl, float(scale), 1))
+        for h in range(2):
+            s = oracle.scores(q[0, h], k[:, 0, :], scale)
+            got = oracle.finalize(oracle.triplet(s, v[:, 0, :]))
+            np.testing.assert_allclose(got, ref[0, h], rtol=0, atol=1e-13)
