@@ -16,14 +16,14 @@ import math
 import os
 
 __all__ = [
-    "gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_attn_multi", "gqa_decode_partial",
+    "gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_attn_noalloc", "gqa_decode_attn_multi", "gqa_decode_partial",
     "gqa_decode_merge", "gqa_kv_append", "gqa_decode_step", "gqa_decode_attn_triplet", "gqa_merge_triplets",
     "GQA_MAX_QUERY_TOKENS",
     "gqa_decode_pick_splits", "gqa_decode_pick_splits_d",
     "gqa_decode_workspace_bytes", "gqa_status_string", "GQAError", "lib", "LIB_PATH",
     "GQA_OK", "GQA_ERR_INVALID_ARG", "GQA_ERR_UNSUPPORTED", "GQA_ERR_WORKSPACE", "GQA_ERR_HIP",
     "GQA_DTYPE_F32", "GQA_DTYPE_BF16", "GQA_FLAG_VALU", "GQA_FLAG_FUSED", "GQA_MAX_SPLITS",
-    "workspace_layout", "multi_splits",
+    "workspace_layout", "multi_splits", "GQA_SCRATCH_BYTES",
 ]
 
 GQA_OK = 0
@@ -37,6 +37,7 @@ GQA_FLAG_VALU = 1
 GQA_FLAG_FUSED = 2
 GQA_MAX_SPLITS = 4096
 GQA_MAX_QUERY_TOKENS = 64
+GQA_SCRATCH_BYTES = 16 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_decode.so")
 
@@ -60,6 +61,9 @@ lib.gqa_decode_attn.restype = _i32
 lib.gqa_decode_attn_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32,
                                    _i32, _i32, _i64, _vp, _sz, _vp, _i32]
 lib.gqa_decode_attn_ex.restype = _i32
+lib.gqa_decode_attn_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32,
+                                        _i32, _i32, _i64, _vp, _i32]
+lib.gqa_decode_attn_noalloc.restype = _i32
 lib.gqa_decode_attn_multi.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                       _i32, _i64, _vp, _sz, _vp]
 lib.gqa_decode_attn_multi.restype = _i32
@@ -192,6 +196,33 @@ def gqa_decode_attn_ex(q, k_cache, v_cache, seq_lens, out=None, *, scale=None, n
             (GQA_FLAG_VALU if valu else 0) | (GQA_FLAG_FUSED if fused else 0))
     if r != GQA_OK:
         raise GQAError(r, "gqa_decode_attn_ex")
+    return out
+
+
+def gqa_decode_attn_noalloc(q, k_cache, v_cache, seq_lens, out, *, scale=None, n_splits=0, s_kv_hint=0,
+                            kv_token_offsets=None, stream=None, valu=False, fused=False):
+    """gqa_decode_attn_ex with the library's static scratch as its workspace:
+    neither this function nor the library allocates (the caller gives `out`,
+    [B, h_q, d] fp32 or bf16). Calls that overlap in time on one GPU race on
+    the scratch."""
+    torch = _torch()
+    B, h_q, d = q.shape
+    h_kv = k_cache.shape[1]
+    _check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets)
+    if out.shape != (B, h_q, d) or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous [B, h_q, d_head] GPU tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    with torch.cuda.device(q.device):
+        st = stream if stream is not None else torch.cuda.current_stream(q.device)
+        r = lib.gqa_decode_attn_noalloc(
+            q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+            kv_token_offsets.data_ptr() if kv_token_offsets is not None else None,
+            out.data_ptr(), B, h_q, h_kv, d, float(scale), int(n_splits),
+            _dtype_code(q.dtype), _dtype_code(out.dtype), int(s_kv_hint), ctypes.c_void_p(st.cuda_stream),
+            (GQA_FLAG_VALU if valu else 0) | (GQA_FLAG_FUSED if fused else 0))
+    if r != GQA_OK:
+        raise GQAError(r, "gqa_decode_attn_noalloc")
     return out
 
 

@@ -478,21 +478,30 @@ struct Plan {
   int64_t hint;                 // the caller's longest length (0: unknown)
 };
 
+// The split count of a call: n_splits if > 0, else the heuristic's (which
+// queries the device's compute units once per device).
+int plan_splits(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_hint, int s_q,
+                bool multi_entry, int* ns) {
+  *ns = n_splits;
+  if (n_splits > 0) return GQA_OK;
+  int num_cus = 0;
+  int st = device_cus(&num_cus);
+  if (st != GQA_OK) return st;
+  int tpt, qtiles, tpw, passes;
+  query_tiles(s_q, h_q / h_kv, B, s_kv_hint, &tpt, &qtiles, &tpw, &passes);
+  *ns = pick_splits_host(B, passes, h_kv, s_kv_hint, num_cus, split_policy(tpw, d_head, !multi_entry, s_q));
+  return GQA_OK;
+}
+
 int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_hint,
               void* workspace, size_t workspace_bytes, bool allow_library_ws, Plan* pl,
               int s_q = 1, bool multi_entry = false) {
   if (workspace && reinterpret_cast<uintptr_t>(workspace) % 256)
     return fail(GQA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
   if (!workspace && !allow_library_ws) return fail(GQA_ERR_INVALID_ARG, "this entry point needs a workspace");
-  int ns = n_splits;
-  if (ns <= 0) {
-    int num_cus = 0;
-    int st = device_cus(&num_cus);
-    if (st != GQA_OK) return st;
-    int tpt, qtiles, tpw, passes;
-    query_tiles(s_q, h_q / h_kv, B, s_kv_hint, &tpt, &qtiles, &tpw, &passes);
-    ns = pick_splits_host(B, passes, h_kv, s_kv_hint, num_cus, split_policy(tpw, d_head, !multi_entry, s_q));
-  }
+  int ns = 0;
+  int st0 = plan_splits(B, h_q, h_kv, d_head, n_splits, s_kv_hint, s_q, multi_entry, &ns);
+  if (st0 != GQA_OK) return st0;
   pl->ns = ns;
   // a heuristic call keeps chunks of at least kMinChunk tokens, a call of
   // one query token over at most 4 sequences of at least one block
@@ -611,6 +620,68 @@ int run_merge(const Plan& pl, const int32_t* seq_lens, void* out, int B, int h_q
   return GQA_OK;
 }
 
+// Argument checks of the single-token attention entry points (host only).
+int check_attn_args(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                    const int64_t* kv_token_offsets, const void* out, int B, int h_q, int h_kv, int d_head,
+                    float scale, int n_splits, int in_dtype, int out_dtype, int64_t s_kv_hint, int flags) {
+  int st;
+  if (!out) return fail(GQA_ERR_INVALID_ARG, "null tensor pointer");
+  if ((st = check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets, scale, in_dtype, flags))) return st;
+  if ((st = check_shape(B, h_q, h_kv, d_head, n_splits, s_kv_hint))) return st;
+  const size_t qo = (size_t)B * h_q * d_head;
+  if ((st = check_out(out, out_dtype, qo))) return st;
+  const size_t in_el = in_dtype == GQA_DTYPE_BF16 ? 2 : 4, out_el = out_dtype == GQA_DTYPE_BF16 ? 2 : 4;
+  if (overlap(out, qo * out_el, q, qo * in_el) || overlap(out, qo * out_el, seq_lens, (size_t)B * 4) ||
+      out == k_cache || out == v_cache)
+    return fail(GQA_ERR_INVALID_ARG, "out overlaps an input");
+  return GQA_OK;
+}
+
+// Split kernel, then the merge unless the split kernel wrote out itself.
+int run_attn(const Plan& pl, const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+             const int64_t* kv_token_offsets, void* out, int B, int h_q, int h_kv, int d_head, float scale,
+             int in_dtype, int out_dtype, hipStream_t stream, int flags) {
+  bool merged = false;
+  int st = run_split(pl, q, k_cache, v_cache, seq_lens, kv_token_offsets, B, h_q, h_kv, d_head, scale, in_dtype,
+                     stream, flags, out, out_dtype, 1, &merged);
+  if (st != GQA_OK) return st;
+  if (merged) return GQA_OK;
+  return run_merge(pl, seq_lens, out, B, h_q, d_head, out_dtype, stream);
+}
+
+}  // namespace
+
+// Workspace of gqa_decode_attn_noalloc: a static device array, one copy per
+// GPU, kept until the process ends. In host code this name stands for a
+// host-side shadow, not for device memory: kernels and copies get the
+// device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[GQA_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch[64];                           // device address of `scratch`, per device ordinal
+
+// The current device's copy of `scratch`, looked up once per device with
+// that device current (the first gqa_decode_attn_noalloc call on it).
+int scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(GQA_ERR_HIP, "device ordinal %d not supported", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    if (!p || reinterpret_cast<uintptr_t>(p) % 256)
+      return fail(GQA_ERR_HIP, "static scratch at %p: null or not 256-byte aligned", p);
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return GQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -622,25 +693,44 @@ int gqa_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
                        int64_t s_kv_hint, void* workspace, size_t workspace_bytes,
                        hipStream_t stream, int flags) {
   int st;
-  if (!out) return fail(GQA_ERR_INVALID_ARG, "null tensor pointer");
-  if ((st = check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets, scale, in_dtype, flags))) return st;
-  if ((st = check_shape(B, h_q, h_kv, d_head, n_splits, s_kv_hint))) return st;
-  const size_t qo = (size_t)B * h_q * d_head;
-  if ((st = check_out(out, out_dtype, qo))) return st;
-  const size_t in_el = in_dtype == GQA_DTYPE_BF16 ? 2 : 4, out_el = out_dtype == GQA_DTYPE_BF16 ? 2 : 4;
-  if (overlap(out, qo * out_el, q, qo * in_el) || overlap(out, qo * out_el, seq_lens, (size_t)B * 4) ||
-      out == k_cache || out == v_cache)
-    return fail(GQA_ERR_INVALID_ARG, "out overlaps an input");
+  if ((st = check_attn_args(q, k_cache, v_cache, seq_lens, kv_token_offsets, out, B, h_q, h_kv, d_head, scale,
+                            n_splits, in_dtype, out_dtype, s_kv_hint, flags)))
+    return st;
+  const size_t qo = (size_t)B * h_q * d_head, out_el = out_dtype == GQA_DTYPE_BF16 ? 2 : 4;
   if (workspace && overlap(out, qo * out_el, workspace, workspace_bytes))
     return fail(GQA_ERR_INVALID_ARG, "out overlaps workspace");
   Plan pl;
   if ((st = make_plan(B, h_q, h_kv, d_head, n_splits, s_kv_hint, workspace, workspace_bytes, true, &pl))) return st;
-  bool merged = false;
-  if ((st = run_split(pl, q, k_cache, v_cache, seq_lens, kv_token_offsets, B, h_q, h_kv, d_head, scale,
-                      in_dtype, stream, flags, out, out_dtype, 1, &merged)))
+  return run_attn(pl, q, k_cache, v_cache, seq_lens, kv_token_offsets, out, B, h_q, h_kv, d_head, scale,
+                  in_dtype, out_dtype, stream, flags);
+}
+
+int gqa_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, const int64_t* kv_token_offsets,
+                            void* out, int B, int h_q, int h_kv, int d_head,
+                            float scale, int n_splits, int in_dtype, int out_dtype,
+                            int64_t s_kv_hint, hipStream_t stream, int flags) {
+  int st;
+  if ((st = check_attn_args(q, k_cache, v_cache, seq_lens, kv_token_offsets, out, B, h_q, h_kv, d_head, scale,
+                            n_splits, in_dtype, out_dtype, s_kv_hint, flags)))
     return st;
-  if (merged) return GQA_OK;
-  return run_merge(pl, seq_lens, out, B, h_q, d_head, out_dtype, stream);
+  int ns = 0;
+  if ((st = plan_splits(B, h_q, h_kv, d_head, n_splits, s_kv_hint, 1, false, &ns))) return st;
+  const size_t need = ws_bytes(B, h_q, d_head, ns);
+  if (need > (size_t)GQA_SCRATCH_BYTES)
+    return fail(GQA_ERR_WORKSPACE,
+                "gqa_decode_attn_noalloc: %d splits of %d x %d rows of %d need %zu bytes of workspace, more than "
+                "the static scratch's %zu (GQA_SCRATCH_BYTES); pass fewer splits or use gqa_decode_attn_ex",
+                ns, B, h_q, d_head, need, (size_t)GQA_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  const size_t qo = (size_t)B * h_q * d_head, out_el = out_dtype == GQA_DTYPE_BF16 ? 2 : 4;
+  if (overlap(out, qo * out_el, ws, GQA_SCRATCH_BYTES))
+    return fail(GQA_ERR_INVALID_ARG, "out overlaps the static scratch");
+  Plan pl;
+  if ((st = make_plan(B, h_q, h_kv, d_head, n_splits, s_kv_hint, ws, GQA_SCRATCH_BYTES, false, &pl))) return st;
+  return run_attn(pl, q, k_cache, v_cache, seq_lens, kv_token_offsets, out, B, h_q, h_kv, d_head, scale,
+                  in_dtype, out_dtype, stream, flags);
 }
 
 int gqa_decode_partial(const void* q, const void* k_cache, const void* v_cache,

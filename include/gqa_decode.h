@@ -137,6 +137,31 @@ int gqa_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
                        hipStream_t stream, int flags);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * gqa_decode_attn_ex without a workspace argument and without allocating.
+ * Its split and merge kernels use a library-owned static device array of
+ * GQA_SCRATCH_BYTES bytes (one per GPU, held until the process ends) as
+ * their workspace. The call returns GQA_ERR_WORKSPACE, with nothing
+ * launched, when gqa_decode_workspace_bytes(B, h_q, d_head, n) exceeds
+ * GQA_SCRATCH_BYTES for the split count n it would use; pass a smaller
+ * n_splits, or call gqa_decode_attn_ex with a workspace. It calls no
+ * hipMalloc or hipFree; its first call on a device looks up that device's
+ * copy of the array (hipGetSymbolAddress). Every call on one GPU shares the
+ * array, and no kernel needs it cleared, but calls that overlap in time on
+ * one GPU (different streams, or host threads) race on it: serialise them.
+ * Same arguments, kernels and results (bit for bit) as gqa_decode_attn_ex
+ * given a workspace.
+ */
+#define GQA_SCRATCH_BYTES (16u << 20)
+
+int gqa_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, const int64_t* kv_token_offsets,
+                            void* out, int B, int h_q, int h_kv, int d_head,
+                            float scale, int n_splits, int in_dtype, int out_dtype,
+                            int64_t s_kv_hint, hipStream_t stream, int flags);
+
+/*
  * Several new query tokens per sequence (e.g. verifying speculated tokens):
  * q and out are [B, S_q, h_q, d_head]; the S_q tokens are the last S_q
  * positions of sequence b, their K/V rows already in the cache, and token i

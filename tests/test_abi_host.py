@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert names == sorted(["gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_attn_multi", "gqa_decode_partial",
+    assert names == sorted(["gqa_decode_attn", "gqa_decode_attn_ex", "gqa_decode_attn_noalloc",
+                            "gqa_decode_attn_multi", "gqa_decode_partial",
                             "gqa_decode_merge", "gqa_kv_append", "gqa_decode_step", "gqa_decode_attn_triplet",
                             "gqa_merge_triplets", "gqa_decode_pick_splits", "gqa_decode_pick_splits_d",
                             "gqa_decode_multi_splits",
@@ -49,6 +50,8 @@ def test_status_constants_match_header(gqa):
         assert m and int(m.group(1)) == getattr(gqa, name), name
     assert int(re.search(r"#define GQA_MAX_SPLITS (\d+)", src).group(1)) == gqa.GQA_MAX_SPLITS
     assert int(re.search(r"#define GQA_MAX_QUERY_TOKENS (\d+)", src).group(1)) == gqa.GQA_MAX_QUERY_TOKENS
+    assert int(re.search(r"#define GQA_SCRATCH_BYTES \((\d+)u << (\d+)\)", src).group(1)) << \
+        int(re.search(r"#define GQA_SCRATCH_BYTES \((\d+)u << (\d+)\)", src).group(2)) == gqa.GQA_SCRATCH_BYTES
 
 
 def test_status_strings(gqa):
@@ -293,3 +296,22 @@ def test_sharded_entry_points_check_on_the_host(gqa):
     assert m(d=80) == -2
     assert m(dt=3) == -2
     assert m(out=W + (1 << 16)) == -1        # out overlaps o
+
+
+def test_noalloc_checks_on_the_host(gqa):
+    """The no-allocation entry point runs the same argument checks as
+    gqa_decode_attn_ex, and rejects a split count whose workspace would not
+    fit its static scratch before any HIP call (the split count is given, so
+    no device is queried)."""
+    f = lambda **kw: gqa.lib.gqa_decode_attn_noalloc(
+        kw.get("q", Q), K, V, L, None, kw.get("out", O), kw.get("B", 1), 64, 8, kw.get("d", 128), 0.088,
+        kw.get("n", 4), 1, 0, 0, None, kw.get("fl", 0))
+    assert f(q=None) == -1
+    assert f(d=96) == -2
+    assert f(out=Q) == -1
+    assert f(fl=4) == -1
+    need = lambda B, n: gqa.gqa_decode_workspace_bytes(B, 64, 128, n)
+    assert need(1, 512) > gqa.GQA_SCRATCH_BYTES >= need(1, 256)
+    assert f(n=512) == gqa.GQA_ERR_WORKSPACE
+    assert "GQA_SCRATCH_BYTES" in gqa.lib.gqa_last_error().decode()
+    assert f(n=gqa.GQA_MAX_SPLITS) == gqa.GQA_ERR_WORKSPACE
