@@ -14,7 +14,11 @@ divided by the time per call, and its fraction of the 8 TB/s HBM peak.
 `roofline.achieved` uses the split kernel's own duration: HIP events recorded
 on the launch stream around a replay of a graph of K split-only launches
 (gqa_decode_partial), divided by K.
-`cpu_baseline` times the fp64 oracle on one host thread in a subprocess.
+`cpu_baseline` times the fp64 oracle on the host's cores in a subprocess
+(and on one thread, as an extra key). `extra_workloads` holds the same
+measurement on the other Llama-70B workloads (the ragged batch of 8, one
+sequence of 32k and of 1M tokens) and on the plan made without a length
+hint (8k, 1M), with inputs drawn on the GPU from a seeded generator.
 """
 from __future__ import annotations
 
@@ -92,8 +96,17 @@ class Hip:
         return ms.value
 
 
-def cpu_baseline(name: str, budget_s: float) -> dict:
-    """Time oracle.attend on the host, one thread, in a child process."""
+def host_cores() -> int:
+    """Host cores this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _time_oracle(name: str, budget_s: float, threads: int) -> dict:
+    """Time oracle.attend on the host in a child process with `threads` BLAS
+    and OpenMP threads."""
     code = f"""
 import json, os, sys, time
 sys.path.insert(0, {ROOT!r})
@@ -121,17 +134,28 @@ else:
     sample = f"kv group 0 of sequence 0 ({{w.n_rep}} query heads, {{int(inp.seq_lens[0])}} tokens) per call, {{n}} call(s)"
 print(json.dumps(dict(seconds_per_call=dt, sample_bytes=sample_bytes, calls=n, sample=sample)))
 """
-    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
+    t = str(threads)
+    env = dict(os.environ, OMP_NUM_THREADS=t, OPENBLAS_NUM_THREADS=t, MKL_NUM_THREADS=t,
                HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
                        timeout=600)
     if r.returncode != 0:
         raise RuntimeError("cpu baseline failed: " + r.stderr[-2000:])
-    d = json.loads(r.stdout.strip().splitlines()[-1])
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def cpu_baseline(name: str, budget_s: float) -> dict:
+    """The fp64 oracle on the host's cores (BLAS and OpenMP threads = the
+    cores this process may use), and on one thread for comparison."""
+    cores = host_cores()
+    d = _time_oracle(name, budget_s, cores)
+    d1 = _time_oracle(name, budget_s / 2, 1)
     gbs = d["sample_bytes"] / d["seconds_per_call"] / 1e9
-    return {"value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": gbs, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"fp64 numpy oracle on {name}: {d['sample']}; "
-                      f"{d['seconds_per_call'] * 1e3:.1f} ms per sample (BLAS and OpenMP threads = 1)"}
+                      f"{d['seconds_per_call'] * 1e3:.1f} ms per sample (BLAS and OpenMP threads = {cores})",
+            "value_one_thread": d1["sample_bytes"] / d1["seconds_per_call"] / 1e9,
+            "ms_per_sample_one_thread": d1["seconds_per_call"] * 1e3}
 
 
 def traffic_from_profile(name: str, src_hash: str):
@@ -144,6 +168,102 @@ def traffic_from_profile(name: str, src_hash: str):
     if d.get("kernel_source_hash") != src_hash:
         return None, d
     return d.get("hbm_bytes_per_launch"), d
+
+
+EXTRA_WORKLOADS = [
+    # (key, workload whose shapes and lengths are used, hint given to the library, steps)
+    ("llama70b_gqa_b8_ragged", "llama70b_gqa_b8_ragged", True, 60),
+    ("llama70b_gqa_b1_s32768", None, True, 100),
+    ("llama70b_gqa_b1_s1m", "llama70b_gqa_b1_s1m", True, 12),
+    ("llama70b_gqa_b1_s8192_no_hint", "llama70b_gqa_b1_s8192", False, 100),
+    ("llama70b_gqa_b1_s1m_no_hint", "llama70b_gqa_b1_s1m", False, 12),
+]
+
+
+def measure_extra(gqa, hip, key: str, base: str | None, with_hint: bool, steps: int) -> dict:
+    """One call (split + merge) of another Llama-70B workload, timed like the
+    headline (a HIP graph of `steps` calls over rotating inputs, split-only
+    graph for the split kernel), with inputs drawn on the GPU from a seeded
+    generator (same shapes, lengths and distributions as the named workload;
+    not the oracle's bits: these are timing runs). Without a hint the call
+    plans as the base entry point does (gqa_decode_attn: no length known)."""
+    import numpy as np
+    import torch
+
+    import workloads
+    if base is None:
+        w = workloads.WORKLOADS["llama70b_gqa_b1_s8192"]
+        lens_np = np.array([32768], dtype=np.int32)
+    else:
+        w = workloads.WORKLOADS[base]
+        lens_np = workloads.seq_lens_for(w)
+    dev = torch.device("cuda:0")
+    B, T = len(lens_np), int(lens_np.sum())
+    kv_bytes = 2 * T * w.h_kv * w.d * 2
+    free, _ = torch.cuda.mem_get_info()
+    R = max(1, min(math.ceil(ROTATE_BYTES / kv_bytes), int(0.4 * free // kv_bytes)))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 + w.seed)
+    sets = []
+    for _ in range(R):
+        q = torch.randn((B, w.h_q, w.d), generator=gen, device=dev).to(torch.bfloat16)
+        k = torch.empty((T, w.h_kv, w.d), dtype=torch.bfloat16, device=dev)
+        v = torch.empty_like(k)
+        for t0 in range(0, T, 1 << 18):             # in slices: bounded fp32 temporaries
+            t1 = min(T, t0 + (1 << 18))
+            k[t0:t1] = (w.k_sigma * torch.randn((t1 - t0, w.h_kv, w.d), generator=gen, device=dev)).to(torch.bfloat16)
+            v[t0:t1] = torch.randn((t1 - t0, w.h_kv, w.d), generator=gen, device=dev).to(torch.bfloat16)
+        sets.append((q, k, v))
+    lens = torch.from_numpy(lens_np).to(dev)
+    hint = int(lens_np.max()) if with_hint else 0
+    ns = gqa.gqa_decode_pick_splits_d(B, w.h_kv, w.d, hint)
+    ws = torch.empty(gqa.gqa_decode_workspace_bytes(B, w.h_q, w.d, ns), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, w.h_q, w.d), dtype=torch.float32, device=dev)
+    scale = float(np.float32(1.0 / math.sqrt(w.d)))
+    stream = torch.cuda.Stream()
+
+    def call(i):
+        q, k, v = sets[i % R]
+        gqa.gqa_decode_attn_ex(q, k, v, lens, out, scale=scale, s_kv_hint=hint, workspace=ws)
+
+    def partial(i):
+        q, k, v = sets[i % R]
+        gqa.gqa_decode_partial(q, k, v, lens, ws, scale=scale, s_kv_hint=hint)
+
+    def graph_us(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(steps):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = hip.event(), hip.event()
+        hip.lib.hipEventRecord(e0, ctypes.c_void_p(stream.cuda_stream))
+        g.replay()
+        hip.lib.hipEventRecord(e1, ctypes.c_void_p(stream.cuda_stream))
+        us = hip.elapsed_ms(e0, e1) * 1e3 / steps
+        hip.lib.hipEventDestroy(e0)
+        hip.lib.hipEventDestroy(e1)
+        return us
+
+    with torch.cuda.stream(stream):
+        for i in range(3):
+            call(i)
+        torch.cuda.synchronize()
+        us = graph_us(call)
+        split_us = graph_us(partial)
+    if not torch.isfinite(out).all():
+        raise RuntimeError(f"{key}: non-finite output")
+    res = {"us_per_call": round(us, 3), "effective_gbs": round(kv_bytes / us / 1e3, 1),
+           "pct_hbm_peak": round(100.0 * kv_bytes / us / 1e3 / HBM_PEAK_GBS, 2),
+           "split_kernel_us": round(split_us, 3), "kv_bytes_per_call": kv_bytes,
+           "frac": round(kv_bytes / split_us / 1e3 / HBM_PEAK_GBS, 4),
+           "n_splits": ns, "s_kv_hint": hint, "B": B, "rotating_input_sets": R, "steps": steps,
+           "seq_lens": lens_np.tolist() if B <= 16 else f"{B} sequences"}
+    del sets, ws
+    torch.cuda.empty_cache()
+    log(f"[bench] {key}: {us:.2f} us per call, split kernel {split_us:.2f} us (frac {res['frac']:.3f})")
+    return res
 
 
 def bench_append_or_step(args) -> int:
@@ -258,7 +378,10 @@ def main() -> int:
     ap.add_argument("--fused", action="store_true",
                     help="single-launch form (GQA_FLAG_FUSED) instead of split + merge kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the extra workloads (ragged batch, 32k, 1M, no-hint plans)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work on all cores (half as long on one thread)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one elementwise copy-like kernel over this many MiB first "
                          "(calibrates HBM byte counters)")
@@ -483,6 +606,12 @@ def main() -> int:
                    "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
                    "hip": torch.version.hip},
     }
+    if not args.no_extra and args.workload == DEFAULT_WORKLOAD and not args.seq_lens and args.s_q == 1 \
+            and not (args.valu or args.fused or args.eager or args.n_splits):
+        del sets
+        torch.cuda.empty_cache()
+        res["extra_workloads"] = {key: measure_extra(gqa, hip, key, base, hint, st)
+                                  for key, base, hint, st in EXTRA_WORKLOADS}
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
         res["cpu_baseline"] = cpu_baseline(w.name, args.cpu_budget)

@@ -42,6 +42,7 @@ int fail(int status, const char* fmt, ...) {
 // Heuristic constants (see gqa_decode_pick_splits).
 constexpr int kMinChunk = 128;       // tokens: one 32-token block per wave of a workgroup
 constexpr int kBlockTokens = 32;     // one block: the shortest chunk of a single short sequence
+constexpr int kNoHintRounds = 4;     // rounds of resident workgroups a call without a length hint plans for
 // How a split kernel wants its grid: resident workgroups per CU, rounds of
 // those slots the longest sequence's chunks fill (one sequence / a batch, where
 // only the longest length is known and more rounds keep it balanced), and the
@@ -354,6 +355,14 @@ int pick_splits_host(int B, int passes, int h_kv, int64_t s_kv_max, int num_cus,
     const int64_t cap = (s_kv_max + kMinChunk - 1) / kMinChunk;   // no chunk shorter than kMinChunk
     if (n > cap) n = cap;
   }
+  if (s_kv_max <= 0 && p.short_one) {
+    // ... no length known (one query token): enough chunks for a long
+    // sequence, kNoHintRounds rounds of the resident slots, with a chunk
+    // floor that grows with each sequence's length on the device (see
+    // make_plan), so short sequences leave most chunks empty: 70B B = 1 gets
+    // 256 chunks, 4096 tokens each at 1M, 128 at 8k (64 of them non-empty).
+    n *= kNoHintRounds;
+  }
   if (s_kv_max > 0 && B <= 4 && p.short_one) {
     // ... except short sequences in a batch of at most 4: up to one
     // workgroup per CU while chunks keep one block (more workgroups engage
@@ -505,7 +514,10 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
   pl->ns = ns;
   // a heuristic call keeps chunks of at least kMinChunk tokens, a call of
   // one query token over at most 4 sequences of at least one block
-  pl->min_chunk = n_splits > 0 ? 1 : (B <= 4 && s_q == 1 ? kBlockTokens : kMinChunk);
+  // (no length hint, one query token: the floor grows with each sequence's
+  // length on the device, see chunk_floor, over the wider grid the split
+  // count gives such a call)
+  pl->min_chunk = n_splits > 0 ? 1 : (s_kv_hint <= 0 && s_q == 1) ? 0 : (B <= 4 && s_q == 1 ? kBlockTokens : kMinChunk);
   pl->hint = s_kv_hint;
   pl->need = ws_bytes(B * s_q, h_q, d_head, ns);
   if (workspace) {
@@ -586,7 +598,7 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
                     fused ? (g_call_tag.fetch_add(1) & 0xFFFFFFFFFFFFull) : 0ull,
                     s_q, tpt, qtiles, passes};
   sa.direct = direct;
-  const dim3 grid = gqa::split_grid(pl.ns, h_kv, B * passes);
+  dim3 grid = gqa::split_grid(pl.ns, h_kv, B * passes);
   const bool bf16 = in_dtype == GQA_DTYPE_BF16;
   const bool valu = (flags & GQA_FLAG_VALU) != 0;
   const int nrep = h_q / h_kv;
@@ -600,6 +612,7 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
     form = split_form(pl, B, h_kv, d_head);
     if (fused) form = Form::kFourWave;             // the single-launch tail is built for 4 waves
   }
+  if (form == Form::kEightWave) grid = gqa::split_grid_heads_fastest(pl.ns, h_kv, B * passes);
   e = d_head == 128 ? launch_split_nrep<128>(nrep, bf16, valu, form, grid, stream, sa)
                     : launch_split_nrep<64>(nrep, bf16, valu, form, grid, stream, sa);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
@@ -861,9 +874,10 @@ int gqa_decode_step(const void* q, const void* k_new, const void* v_new, void* k
                     h_q, h_kv, pl.ns, pl.min_chunk, scale * gqa::kLog2e,
                     0, out_dtype == GQA_DTYPE_BF16 ? 1 : 0, out, pl.counters, 0ull, 1, 1, 1, 1,
                     k_new, v_new, seq_lens_out, (int)capacity, pl.ns == 1 ? 1 : 0};
-  const dim3 grid = gqa::split_grid(pl.ns, h_kv, B);
   const int nrep = h_q / h_kv;
   const Form form = split_form(pl, B, h_kv, d_head);   // the same form as gqa_decode_attn_ex with this hint
+  const dim3 grid = form == Form::kEightWave ? gqa::split_grid_heads_fastest(pl.ns, h_kv, B)
+                                             : gqa::split_grid(pl.ns, h_kv, B);
   hipError_t e = d_head == 128 ? launch_split_append<128>(nrep, form, grid, stream, sa)
                                : launch_split_append<64>(nrep, form, grid, stream, sa);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));

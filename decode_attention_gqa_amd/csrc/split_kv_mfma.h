@@ -303,9 +303,10 @@ void split_kv_mfma(SplitArgs a) {
   static_assert(!APPEND || 2 * (D * 2 / 16) <= 64 * WAVES, "the new row's copy takes one thread per 16 bytes");
   static_assert(NREP >= 1 && NREP <= 16, "one 16-wide MFMA tile holds the query heads of a group");
   static_assert(TILES == 1 || (TILES == 2 && !APPEND), "two tiles serve multi-token decode only");
-  const WgCoord wc = wg_coord();
+  // 8 waves: the grid has kv heads fastest (split_grid_heads_fastest).
+  const WgCoord wc = WAVES == 8 ? WgCoord{(int)blockIdx.y, (int)blockIdx.x, (int)blockIdx.z} : wg_coord();
   const int s = wc.s, g = wc.g;
-  const int b = wc.b / a.passes, pass = wc.b - b * a.passes;
+  const int b = a.passes == 1 ? wc.b : wc.b / a.passes, pass = wc.b - b * a.passes;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int grp = lane >> 4, n = lane & 15;
@@ -336,17 +337,16 @@ void split_kv_mfma(SplitArgs a) {
   S = __builtin_amdgcn_readfirstlane(S);
   off = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(off >> 32)) << 32) |
                   (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)off));
-  int c, n_active;
-  chunking(S, a.n_splits, a.min_chunk, c, n_active);
+  const int c = split_chunk(S, a);                 // chunk s: tokens [s*c, min(S, (s+1)*c))
   // APPEND: the new length is stored last (a store early in the kernel would
   // sit in the wave's memory counter ahead of its K/V loads and every wait for
   // them would wait for its acknowledgement too: 0.25 µs per decode step).
   const bool lens_writer = APPEND && a.lens_out && s == 0 && g == 0 && tid == 0;
-  if (s >= n_active) {                             // the merge reads chunks < n_active only
+  if ((int64_t)s * c >= S) {                       // an empty chunk: the merge reads non-empty ones only
     if (lens_writer) a.lens_out[b] = S;
     if constexpr (WAVES == kWaves)
-      if (a.fused && n_active == 0 && s == 0) fused_empty<D, NREP>(a, g, b);
-    if (a.direct && n_active == 0 && s == 0) {     // nothing attended: out = 0
+      if (a.fused && S == 0 && s == 0) fused_empty<D, NREP>(a, g, b);
+    if (a.direct && S == 0 && s == 0) {            // nothing attended: out = 0
       constexpr int Q4 = D / 4;
       for (int t = 0; t < TILES; ++t)
         for (int idx = tid; idx < NREP * a.tpt * Q4; idx += THREADS) {
@@ -404,7 +404,7 @@ void split_kv_mfma(SplitArgs a) {
   const int64_t src_new = ((int64_t)b * a.h_kv + g) * D * 2;            // row in k_new / v_new (bytes)
   const int64_t row_new = ((off + S - 1) * a.h_kv + g) * D * 2;         // its cache row (bytes)
   constexpr int U16 = D * 2 / 16;                                       // 16-byte pieces per row
-  const bool copier = APPEND && appended && s == n_active - 1 && tid < 2 * U16;
+  const bool copier = APPEND && appended && (int64_t)(s + 1) * c >= S && tid < 2 * U16;   // the last chunk
   uint4 piece = make_uint4(0u, 0u, 0u, 0u);
   if (copier)
     piece = *reinterpret_cast<const uint4*>(static_cast<const char*>(tid < U16 ? a.k_new : a.v_new) + src_new +
@@ -561,7 +561,7 @@ void split_kv_mfma(SplitArgs a) {
   }
   if (lens_writer) a.lens_out[b] = S;
   if constexpr (WAVES == kWaves)                   // the host runs the single-launch form with 4 waves only
-    if (a.fused) fused_epilogue<D, NREP>(a, g, b, n_active);
+    if (a.fused) fused_epilogue<D, NREP>(a, g, b, (S + c - 1) / c);
 }
 
 }  // namespace gqa

@@ -96,7 +96,11 @@ enum {
  * own workspace).
  *  scale     multiplies q.k before the softmax (1/sqrt(d_head) for Llama).
  *  n_splits  > 0 forces the number of KV chunks per (sequence, kv head);
- *            <= 0 lets gqa_decode_pick_splits_d choose.
+ *            <= 0 lets gqa_decode_pick_splits_d choose with no length hint:
+ *            a grid of four rounds of workgroups whose chunks, sized on the
+ *            device from each sequence's length, hold at least 32 to 128
+ *            tokens (at most 4096 tokens each for one 8-kv-head sequence of
+ *            up to 1M tokens).
  */
 int gqa_decode_attn(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* seq_lens, void* out,
@@ -274,9 +278,10 @@ int gqa_merge_triplets(const float* ml, const float* o, int parts, int rows, int
  * split count used, and `o` and `ml` sit where gqa_decode_workspace_bytes
  * describes. Chunk s covers tokens
  * [s*c, min(S_b, (s+1)*c)) with c = max(ceil(S_b / n), f), f = 1 when
- * n_splits > 0, else 32 for B <= 4 and 128 for larger batches;
- * n_active(b) = ceil(S_b / c). Other slots are left untouched. A workspace is
- * required.
+ * n_splits > 0; with a length hint 32 for B <= 4 and 128 for larger
+ * batches; without one (a single query token), ceil(S_b / 32) rounded up to
+ * a multiple of 32, clamped to [32, 128]; n_active(b) = ceil(S_b / c). Other
+ * slots are left untouched. A workspace is required.
  *
  * gqa_decode_merge reads those triplets and writes out = o / l per (b, h),
  * merged exactly over the chunks. It must be given the seq_lens, shape,
@@ -296,7 +301,11 @@ int gqa_decode_merge(const int32_t* seq_lens, const void* workspace, size_t work
 
 /*
  * Split count the library uses when n_splits <= 0: enough workgroups that
- * every compute unit has work at B = 1; when s_kv_max > 0 is known, also
+ * every compute unit has work at B = 1 (s_kv_max = 0, no length known: four
+ * rounds of two workgroups per compute unit, e.g. 256 chunks for one
+ * sequence with 8 kv heads on 256 CUs, with the chunk floor of a hint-less
+ * call, see gqa_decode_partial, so short sequences leave most chunks empty);
+ * when s_kv_max > 0 is known, also
  * enough that the longest sequence's chunks fill about two rounds of the
  * resident workgroup slots (B = 1) or B / 2 up to four (B > 1, where lengths
  * may differ),

@@ -1,6 +1,8 @@
 """Helpers shared by the GPU tests: upload seeded inputs and run the library."""
 from __future__ import annotations
 
+import functools
+
 import numpy as np
 
 import workloads
@@ -51,3 +53,22 @@ def max_err(got, ref) -> float:
     if not np.all(np.isfinite(got[ok])):
         return float("inf")
     return float(np.max(np.abs(got[ok] - ref[ok]))) if ok.any() else 0.0
+
+
+@functools.lru_cache(maxsize=2)
+def oracle_all_heads(name: str) -> np.ndarray:
+    """The fp64 oracle on every head of a named workload, one kv group at a
+    time (for the 1M-token workload a group's K and V in fp64 are 2 GiB, so
+    host memory stays bounded). Cached per process: the parity and the
+    single-launch tests share it."""
+    import oracle
+    inp = workloads.make_inputs(name)
+    w = inp.w
+    out = np.full((w.B, w.h_q, w.d), np.nan)
+    for g in range(w.h_kv):
+        heads = [(b, h) for b in range(w.B) for h in range(g * w.n_rep, (g + 1) * w.n_rep)]
+        part = oracle.attend(inp.q, inp.k, inp.v, inp.seq_lens, inp.scale, w.h_kv, dtype=w.dtype, heads=heads)
+        for b, h in heads:
+            out[b, h] = part[b, h]
+        print(f"[oracle] {name}: kv group {g} done", flush=True)
+    return out

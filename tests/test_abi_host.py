@@ -132,7 +132,9 @@ def test_split_heuristic_contract(gqa, B, h_kv, S):
     assert 1 <= n <= gqa.GQA_MAX_SPLITS
     fill = math.ceil(2 * cus / (B * h_kv))
     if S == 0:
-        assert n == min(fill, gqa.GQA_MAX_SPLITS)
+        # no length known: four rounds of the resident slots (the chunk floor
+        # then grows with each length on the device)
+        assert n == min(4 * fill, gqa.GQA_MAX_SPLITS)
     else:
         # never more chunks than the longest sequence fills with 128 tokens
         # each (32 for a single sequence)
@@ -179,6 +181,11 @@ def test_split_heuristic_values(gqa):
     assert gqa.gqa_decode_pick_splits(1, 8, 1 << 22, 256) == 1024
     # several sequences: the longest over four rounds
     assert gqa.gqa_decode_pick_splits(8, 8, 32768, 256) == 32
+    # no length hint: four rounds of the resident slots
+    assert gqa.gqa_decode_pick_splits(1, 8, 0, 256) == 256
+    assert gqa.gqa_decode_pick_splits(8, 8, 0, 256) == 32
+    assert gqa.gqa_decode_pick_splits(1, 32, 0, 256) == 64
+    assert gqa.gqa_decode_pick_splits_d(1, 8, 64, 0, 256) == 256
 
 
 def test_multi_split_heuristic_values(gqa):

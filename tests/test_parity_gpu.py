@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import TOL_BF16, TOL_F32, max_err, run_gpu, to_device
+from gpu_util import TOL_BF16, TOL_F32, max_err, oracle_all_heads, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -49,19 +49,35 @@ def test_bf16_output_is_rounded_fp32_output():
     np.testing.assert_array_equal(b16, rounded.astype(np.float64))
 
 
-def test_long_context_1m_sampled_heads():
-    """Full-size 1M-token case (4 GiB KV, K ~ N(0, 4)); the oracle computes a
-    sample of heads from 3 of the 8 kv groups, plus the value-hull property on
-    all heads."""
+def test_long_context_1m_every_head():
+    """Full-size 1M-token case (4 GiB KV, K ~ N(0, 4), so the running max
+    grows many times along the sequence): every one of the 64 heads, in all 8
+    kv groups, against the fp64 oracle (computed one kv group at a time), with
+    the split count the length hint gives (256 chunks of 4096 tokens)."""
     inp = workloads.make_inputs("llama70b_gqa_b1_s1m")
     print(f"[case] 1M B=1 S={int(inp.seq_lens[0])}", flush=True)
     got, ns = run_gpu(inp)
-    heads = [(0, 0), (0, 5), (0, 13), (0, 63)]
-    report("llama70b_gqa_b1_s1m/sampled", max_err(got, ref_of(inp, heads=heads)), ns, TOL_F32)
+    ref = oracle_all_heads("llama70b_gqa_b1_s1m")
+    assert not np.isnan(ref).any()
+    report("llama70b_gqa_b1_s1m/all heads", max_err(got, ref), ns, TOL_F32)
     vmin = workloads.bf16_bits_to_f32(inp.v).min(axis=0)  # [h_kv, d]
     vmax = workloads.bf16_bits_to_f32(inp.v).max(axis=0)
     g = np.arange(64) // 8
     assert np.all(got[0] <= vmax[g] + 1e-6) and np.all(got[0] >= vmin[g] - 1e-6)
+
+
+def test_long_context_1m_base_entry_point():
+    """The base entry point (no length hint: it plans without knowing S) at
+    1M tokens, every head against the oracle."""
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    inp = workloads.make_inputs("llama70b_gqa_b1_s1m")
+    q, k, v, lens = to_device(inp)
+    out = gqa.gqa_decode_attn(q, k, v, lens, scale=float(inp.scale))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    report("llama70b_gqa_b1_s1m/base entry", max_err(got, oracle_all_heads("llama70b_gqa_b1_s1m")), 0, TOL_F32)
 
 
 @pytest.mark.parametrize("valu", [False, True], ids=["mfma", "valu"])
@@ -201,6 +217,29 @@ def test_base_entry_point_and_library_workspace():
         out = gqa.gqa_decode_attn(q, k, v, dl, scale=float(inp.scale), n_splits=ns)
         torch.cuda.synchronize()
         report(f"base entry ns={ns}", max_err(out.cpu().numpy().astype(np.float64), ref), ns, TOL_F32)
+
+
+@pytest.mark.parametrize("lens", [[1], [31], [32], [256], [1000], [1024], [3000], [4096], [4097], [8192],
+                                  [20000], [70000], [5, 0, 2049, 8191], [11032, 4287, 10486, 11180, 21209, 32739,
+                                                                     5895, 7145]])
+def test_base_entry_point_without_hint_at_many_lengths(lens):
+    """The base entry point plans without the lengths: a grid of several
+    rounds of chunks, whose floor grows with each sequence's length on the
+    device. Every length class against the oracle; the merge must agree with
+    the split kernel on which chunks exist (the workspace is NaN-poisoned)."""
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    inp = workloads.custom(f"nohint_{len(lens)}_{lens[0]}", B=len(lens), h_q=64, h_kv=8, d=128, seq_lens=lens,
+                           seed=90 + len(lens) + lens[0] % 97)
+    got, ns = run_gpu(inp, hint=False)
+    assert ns == gqa.gqa_decode_pick_splits(len(lens), 8, 0)
+    report(f"no hint lens={lens[:4]}", max_err(got, ref_of(inp)), ns, TOL_F32)
+    if len(lens) == 1:                                 # the base entry: the same plan and bits
+        q, k, v, dl = to_device(inp)
+        out = gqa.gqa_decode_attn(q, k, v, dl, scale=float(inp.scale))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out.cpu().numpy().astype(np.float64), got)
 
 
 def test_runs_on_a_side_stream():
