@@ -1,4 +1,5 @@
-// Single-launch form of the split-KV attention: the split workgroups of a
+// Single-launch form of the split-KV attention (4- and 8-wave workgroups,
+// THREADS = 256 or 512): the split workgroups of a
 // (sequence b, kv head g) group count their arrivals on a per-group counter;
 // the workgroup that arrives last merges the group's (m, l, o) triplets with
 // the same rule as merge_splits and writes out = o / l for the group's n_rep
@@ -28,21 +29,21 @@
 
 namespace gqa {
 
-template <int D, int NREP, typename TO>
+template <int D, int NREP, typename TO, int THREADS = kThreads>
 __device__ __forceinline__ void merge_group(const SplitArgs& a, int b, int g, int n_active) {
   constexpr int Q4 = D / 4;                          // float4 per row
   constexpr int PAIRS = NREP * Q4;                   // (head, float4) items of the group
-  constexpr int SL = PAIRS >= kThreads ? 1 : kThreads / PAIRS;   // chunk slots per item
+  constexpr int SL = PAIRS >= THREADS ? 1 : THREADS / PAIRS;   // chunk slots per item
   constexpr int U = 16;                              // chunks per slot per round
   const int tid = threadIdx.x;
-  const int slot = tid / (PAIRS >= kThreads ? kThreads : PAIRS);
+  const int slot = tid / (PAIRS >= THREADS ? THREADS : PAIRS);
   const int64_t row0 = ((int64_t)b * a.h_q + (int64_t)g * NREP) * a.n_splits;   // (head 0, chunk 0)
   TO* out = static_cast<TO*>(a.out) + ((int64_t)b * a.h_q + (int64_t)g * NREP) * D;
 
   __shared__ float sm[SL][NREP], sl[SL][NREP];
   __shared__ float4 sacc[SL > 1 ? SL : 1][SL > 1 ? PAIRS : 1];
 
-  for (int p = tid % (PAIRS >= kThreads ? kThreads : PAIRS); p < PAIRS; p += kThreads) {
+  for (int p = tid % (PAIRS >= THREADS ? THREADS : PAIRS); p < PAIRS; p += THREADS) {
     const int h = p / Q4, q4 = p % Q4;
     const float2* ml = a.ws_ml + row0 + (int64_t)h * a.n_splits;
     const float* o = a.ws_o + (row0 + (int64_t)h * a.n_splits) * D + 4 * q4;
@@ -118,7 +119,7 @@ __device__ __forceinline__ void merge_group(const SplitArgs& a, int b, int g, in
 constexpr int kWaitVmem = 0x0F70;
 
 // Called by every thread of a split workgroup after its triplets are stored.
-template <int D, int NREP>
+template <int D, int NREP, int THREADS = kThreads>
 __device__ __forceinline__ void fused_epilogue(const SplitArgs& a, int g, int b, int n_active) {
   __shared__ int s_last;
   __builtin_amdgcn_s_waitcnt(kWaitVmem);             // this thread's triplet stores are in L2
@@ -152,18 +153,18 @@ __device__ __forceinline__ void fused_epilogue(const SplitArgs& a, int g, int b,
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // before this thread reads other workgroups' triplets
   if (a.out_bf16)
-    merge_group<D, NREP, __bf16>(a, b, g, n_active);
+    merge_group<D, NREP, __bf16, THREADS>(a, b, g, n_active);
   else
-    merge_group<D, NREP, float>(a, b, g, n_active);
+    merge_group<D, NREP, float, THREADS>(a, b, g, n_active);
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // A sequence with S_b = 0 has no split workgroup to merge: workgroup s = 0
 // of each group writes zeros for the group's heads instead.
-template <int D, int NREP>
+template <int D, int NREP, int THREADS = kThreads>
 __device__ __forceinline__ void fused_empty(const SplitArgs& a, int g, int b) {
   constexpr int Q4 = D / 4;
-  for (int p = threadIdx.x; p < NREP * Q4; p += kThreads) {
+  for (int p = threadIdx.x; p < NREP * Q4; p += THREADS) {
     const int64_t off = ((int64_t)b * a.h_q + (int64_t)g * NREP + p / Q4) * D + 4 * (p % Q4);
     if (a.out_bf16)
       store4<__bf16>(static_cast<__bf16*>(a.out) + off, make_float4(0.f, 0.f, 0.f, 0.f));

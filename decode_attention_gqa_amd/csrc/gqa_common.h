@@ -59,6 +59,12 @@ struct MergeArgs {
   int64_t row_stride, part_stride;
   float2* tri_ml;             // if set: write the merged (m, l) per row here ...
   float* tri_o;               // ... and the merged unnormalised o [rows, D], instead of out
+  // merge_wave only. 0: workgroup L merges row L. R > 0 (8 kv heads, R query
+  // heads per group, split kernel launched kv heads fastest so that kv head g
+  // ran on XCD g): within each block of 8R rows, workgroup L merges row
+  // (L mod 8) * R + (L / 8) mod R, a head of group L mod 8, on the XCD that
+  // wrote its triplets.
+  int xcd_rep;
 };
 
 // Chunk length and number of non-empty chunks of a sequence of S tokens.

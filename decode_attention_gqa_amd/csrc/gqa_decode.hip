@@ -573,6 +573,21 @@ bool two_tile_eight_waves(const Plan& pl, int64_t units, int h_kv) {
   return tok > 4 * kBlockTokens && tok <= 8 * kBlockTokens && (int64_t)pl.ns * h_kv * units <= cus;
 }
 
+// The matrix-core split kernel's form for a call (four waves for anything
+// else: the vector-ALU kernel, fp32 inputs).
+Form choose_form(const Plan& pl, int B, int h_q, int h_kv, int d_head, int s_q, bool mfma, bool fused) {
+  if (!mfma) return Form::kFourWave;
+  int tpt, qtiles, tpw, passes;
+  query_tiles(s_q, h_q / h_kv, B, pl.hint, &tpt, &qtiles, &tpw, &passes);
+  if (s_q == 1) {                                  // the single-launch tail: 4 or 8 waves
+    const Form f = split_form(pl, B, h_kv, d_head);
+    return fused && f == Form::kOneWave ? Form::kFourWave : f;
+  }
+  if (tpw == gqa::kTileWaves) return Form::kTiles;
+  if (tpw == 2 && !fused && two_tile_eight_waves(pl, B * passes, h_kv)) return Form::kEightWave;
+  return Form::kFourWave;
+}
+
 // direct: the caller merges nothing afterwards; with one chunk per sequence
 // the split kernel then writes out itself (returned in *merged).
 int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_cache,
@@ -605,13 +620,7 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
   hipError_t e;
   if (g_ev_before && (e = hipEventRecord(g_ev_before, stream)) != hipSuccess)
     return fail(GQA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-  Form form = Form::kFourWave;
-  if (mfma && tpw == gqa::kTileWaves) form = Form::kTiles;
-  if (mfma && tpw == 2 && !fused && two_tile_eight_waves(pl, B * passes, h_kv)) form = Form::kEightWave;
-  if (mfma && s_q == 1) {
-    form = split_form(pl, B, h_kv, d_head);
-    if (fused) form = Form::kFourWave;             // the single-launch tail is built for 4 waves
-  }
+  const Form form = choose_form(pl, B, h_q, h_kv, d_head, s_q, mfma, fused);
   if (form == Form::kEightWave) grid = gqa::split_grid_heads_fastest(pl.ns, h_kv, B * passes);
   e = d_head == 128 ? launch_split_nrep<128>(nrep, bf16, valu, form, grid, stream, sa)
                     : launch_split_nrep<64>(nrep, bf16, valu, form, grid, stream, sa);
@@ -621,11 +630,16 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
   return GQA_OK;
 }
 
-int run_merge(const Plan& pl, const int32_t* seq_lens, void* out, int B, int h_q, int d_head,
-              int out_dtype, hipStream_t stream, int s_q = 1, float2* tri_ml = nullptr,
+// eight_wave: the split kernel ran in an 8-wave form (kv heads fastest).
+int run_merge(const Plan& pl, const int32_t* seq_lens, void* out, int B, int h_q, int h_kv, int d_head,
+              int out_dtype, hipStream_t stream, bool eight_wave, int s_q = 1, float2* tri_ml = nullptr,
               float* tri_o = nullptr) {
+  // With 8 kv heads launched heads fastest, kv head g's chunks ran on XCD g;
+  // merging its heads there measured faster for several query tokens (8k
+  // tokens, 4 query tokens: 14.86 -> 14.02 us per call; one token: no change).
+  const int xcd_rep = eight_wave && h_kv == 8 ? h_q / 8 : 0;
   gqa::MergeArgs ma{s_q, seq_lens, pl.ws_o, pl.ws_ml, out, h_q, pl.ns, pl.min_chunk,
-                    pl.ns, 1, tri_ml, tri_o};
+                    pl.ns, 1, tri_ml, tri_o, xcd_rep};
   const bool obf16 = out_dtype == GQA_DTYPE_BF16;
   hipError_t e = d_head == 128 ? launch_merge<128>(obf16, B * s_q, h_q, stream, ma)
                                : launch_merge<64>(obf16, B * s_q, h_q, stream, ma);
@@ -659,7 +673,9 @@ int run_attn(const Plan& pl, const void* q, const void* k_cache, const void* v_c
                      stream, flags, out, out_dtype, 1, &merged);
   if (st != GQA_OK) return st;
   if (merged) return GQA_OK;
-  return run_merge(pl, seq_lens, out, B, h_q, d_head, out_dtype, stream);
+  const bool mfma = in_dtype == GQA_DTYPE_BF16 && !(flags & GQA_FLAG_VALU);
+  const bool eight = choose_form(pl, B, h_q, h_kv, d_head, 1, mfma, flags & GQA_FLAG_FUSED) == Form::kEightWave;
+  return run_merge(pl, seq_lens, out, B, h_q, h_kv, d_head, out_dtype, stream, eight);
 }
 
 }  // namespace
@@ -777,7 +793,9 @@ int gqa_decode_merge(const int32_t* seq_lens, const void* workspace, size_t work
   if ((st = make_plan(B, h_q, h_kv, d_head, n_splits, s_kv_hint, const_cast<void*>(workspace), workspace_bytes,
                       false, &pl)))
     return st;
-  return run_merge(pl, seq_lens, out, B, h_q, d_head, out_dtype, stream);
+  // (the split kernel's form only moves rows between workgroups: taken for bf16 inputs)
+  const bool eight = choose_form(pl, B, h_q, h_kv, d_head, 1, true, false) == Form::kEightWave;
+  return run_merge(pl, seq_lens, out, B, h_q, h_kv, d_head, out_dtype, stream, eight);
 }
 
 int gqa_decode_attn_multi(const void* q, const void* k_cache, const void* v_cache,
@@ -813,7 +831,8 @@ int gqa_decode_attn_multi(const void* q, const void* k_cache, const void* v_cach
                       GQA_DTYPE_BF16, stream, 0, out, out_dtype, S_q, &merged)))
     return st;
   if (merged) return GQA_OK;
-  return run_merge(pl, seq_lens, out, B, h_q, d_head, out_dtype, stream, S_q);
+  const bool eight = choose_form(pl, B, h_q, h_kv, d_head, S_q, true, false) == Form::kEightWave;
+  return run_merge(pl, seq_lens, out, B, h_q, h_kv, d_head, out_dtype, stream, eight, S_q);
 }
 
 int gqa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
@@ -882,7 +901,7 @@ int gqa_decode_step(const void* q, const void* k_new, const void* v_new, void* k
                                : launch_split_append<64>(nrep, form, grid, stream, sa);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
   if (sa.direct) return GQA_OK;                    // one chunk per sequence: out is written
-  return run_merge(pl, seq_lens_out, out, B, h_q, d_head, out_dtype, stream);
+  return run_merge(pl, seq_lens_out, out, B, h_q, h_kv, d_head, out_dtype, stream, form == Form::kEightWave);
 }
 
 int gqa_decode_attn_triplet(const void* q, const void* k_cache, const void* v_cache,
@@ -907,7 +926,9 @@ int gqa_decode_attn_triplet(const void* q, const void* k_cache, const void* v_ca
   if ((st = run_split(pl, q, k_cache, v_cache, seq_lens, kv_token_offsets, B, h_q, h_kv, d_head, scale,
                       in_dtype, stream, flags)))
     return st;
-  return run_merge(pl, seq_lens, nullptr, B, h_q, d_head, GQA_DTYPE_F32, stream, 1,
+  const bool mfma = in_dtype == GQA_DTYPE_BF16 && !(flags & GQA_FLAG_VALU);
+  const bool eight = choose_form(pl, B, h_q, h_kv, d_head, 1, mfma, false) == Form::kEightWave;
+  return run_merge(pl, seq_lens, nullptr, B, h_q, h_kv, d_head, GQA_DTYPE_F32, stream, eight, 1,
                    reinterpret_cast<float2*>(ml_out), o_out);
 }
 
@@ -925,7 +946,7 @@ int gqa_merge_triplets(const float* ml, const float* o, int parts, int rows, int
       overlap(out, (size_t)rows * d_head * out_el, o, n * d_head * 4))
     return fail(GQA_ERR_INVALID_ARG, "out overlaps an input");
   gqa::MergeArgs ma{1, nullptr, o, reinterpret_cast<const float2*>(ml), out, 1, parts, 1,
-                    1, rows, nullptr, nullptr};
+                    1, rows, nullptr, nullptr, 0};
   const bool obf16 = out_dtype == GQA_DTYPE_BF16;
   hipError_t e = d_head == 128 ? launch_merge<128>(obf16, rows, 1, stream, ma)
                                : launch_merge<64>(obf16, rows, 1, stream, ma);

@@ -153,7 +153,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void merge_wave(MergeArgs a) {
   constexpr int LPS = 8, SLOTS = 64 / LPS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slot = lane / LPS, q = lane % LPS;
-  const int bh = blockIdx.x;
+  const int wg = blockIdx.x, R = a.xcd_rep;
+  const int bh = R > 0 ? wg - wg % (8 * R) + (wg % 8) * R + (wg / 8) % R : wg;   // see MergeArgs::xcd_rep
   const int b = bh / (a.h_q * a.s_q);
   const int d0 = wave * 4 * LPS;
   const int64_t ps = a.part_stride;

@@ -344,8 +344,8 @@ void split_kv_mfma(SplitArgs a) {
   const bool lens_writer = APPEND && a.lens_out && s == 0 && g == 0 && tid == 0;
   if ((int64_t)s * c >= S) {                       // an empty chunk: the merge reads non-empty ones only
     if (lens_writer) a.lens_out[b] = S;
-    if constexpr (WAVES == kWaves)
-      if (a.fused && S == 0 && s == 0) fused_empty<D, NREP>(a, g, b);
+    if constexpr ((WAVES == kWaves || WAVES == 8) && TILES == 1 && !APPEND)
+      if (a.fused && S == 0 && s == 0) fused_empty<D, NREP, THREADS>(a, g, b);
     if (a.direct && S == 0 && s == 0) {            // nothing attended: out = 0
       constexpr int Q4 = D / 4;
       for (int t = 0; t < TILES; ++t)
@@ -560,8 +560,8 @@ void split_kv_mfma(SplitArgs a) {
     }
   }
   if (lens_writer) a.lens_out[b] = S;
-  if constexpr (WAVES == kWaves)                   // the host runs the single-launch form with 4 waves only
-    if (a.fused) fused_epilogue<D, NREP>(a, g, b, (S + c - 1) / c);
+  if constexpr ((WAVES == kWaves || WAVES == 8) && TILES == 1 && !APPEND)   // the single-launch forms
+    if (a.fused) fused_epilogue<D, NREP, THREADS>(a, g, b, (S + c - 1) / c);
 }
 
 }  // namespace gqa

@@ -75,11 +75,12 @@ enum {
     GQA_FLAG_FUSED = 2  /* one kernel launch: the last split workgroup of each (sequence,
                            kv head) merges that group's triplets and writes out (uses the
                            workspace's arrival counters, see gqa_decode_workspace_bytes).
-                           Correct, but slower on MI355X than the default two launches:
-                           making a workgroup's triplets visible to a workgroup on another
-                           XCD takes device-scope fences that write back and invalidate
-                           the XCD's L2 (measured 206 us vs 12.6 us per call for 64 query /
-                           8 kv heads, 8k tokens). */
+                           Correct, but slower on MI355X than the default two launches
+                           (70B shapes, 8k tokens: 27.4 us vs 11.5 us per call): the
+                           device-scope counter load and add a workgroup makes to learn
+                           whether it is the last take 3 and 7 us (median) when the 32
+                           workgroups of a group arrive together, and the last one then
+                           reads the group's triplets after an L2 invalidation (3.4 us). */
 };
 
 /* Largest split count. */
