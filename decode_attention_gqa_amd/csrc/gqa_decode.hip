@@ -297,6 +297,12 @@ constexpr int kTilesMinTiles = 8;
 constexpr int64_t kTilesMinTokens = 16384;
 constexpr int kTilesMinTilesLong = 4;          // fewer tiles take it only over longer KV
 constexpr int64_t kTilesMinTokensLong = 65536;
+// Many tiles (chunked-prefill sizes) take it from 8192 tokens: 70B B = 1,
+// 8k tokens, µs per call (one tile per wave vs two tiles): S_q = 64 59.4 vs
+// 64.8, 128 97.4 vs 110.9, 512 325.8 vs 396.0; at 2k tokens S_q = 128 41.4
+// vs 35.3 and at 2.5k S_q = 512 160.3 vs 154.4 (two tiles ahead).
+constexpr int kTilesMinTilesMany = 32;
+constexpr int64_t kTilesMinTokensMany = 8192;
 
 // Query tokens per 16-column tile, tiles per sequence, tiles per workgroup
 // (two once a sequence needs two or more, each K/V block then read once for
@@ -308,7 +314,8 @@ void query_tiles(int s_q, int nrep, int B, int64_t hint, int* tpt, int* qtiles, 
   *tpw = *qtiles >= 2 ? 2 : 1;
   const int64_t tokens = hint > 0 ? (int64_t)B * hint : 0;
   if ((*qtiles >= kTilesMinTiles && tokens >= kTilesMinTokens) ||
-      (*qtiles >= kTilesMinTilesLong && tokens >= kTilesMinTokensLong))
+      (*qtiles >= kTilesMinTilesLong && tokens >= kTilesMinTokensLong) ||
+      (*qtiles >= kTilesMinTilesMany && tokens >= kTilesMinTokensMany))
     *tpw = gqa::kTileWaves;
   *passes = (*qtiles + *tpw - 1) / *tpw;
 }

@@ -86,8 +86,9 @@ enum {
 /* Largest split count. */
 #define GQA_MAX_SPLITS 4096
 
-/* Largest number of query tokens per sequence of gqa_decode_attn_multi. */
-#define GQA_MAX_QUERY_TOKENS 64
+/* Largest number of query tokens per sequence of gqa_decode_attn_multi
+ * (speculative decoding verifies a few; chunked prefill sends hundreds). */
+#define GQA_MAX_QUERY_TOKENS 1024
 
 /*
  * Attention for bf16 q/k_cache/v_cache in the packed layout, fp32 `out`, on
@@ -177,8 +178,9 @@ int gqa_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_ca
  * columns fill 16-wide MFMA tiles of t = min(S_q, 16 / n_rep) tokens (the
  * columns single-token decode leaves empty when n_rep < 16). A pass over the
  * KV range serves two tiles (2t tokens read the KV once), or, when a sequence
- * has at least 8 tiles and B * s_kv_hint >= 16384 tokens, or at least 4
- * tiles and B * s_kv_hint >= 65536, eight tiles (one per wave, the K/V
+ * has at least 8 tiles and B * s_kv_hint >= 16384 tokens, at least 4
+ * tiles and B * s_kv_hint >= 65536, or at least 32 tiles and B * s_kv_hint
+ * >= 8192, eight tiles (one per wave, the K/V
  * blocks shared through LDS); more tokens take more passes. The hint only
  * picks the kernel and the split count: either kernel takes any length, and
  * the two round differently. Workspace: gqa_decode_workspace_bytes(B * S_q,

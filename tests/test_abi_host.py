@@ -208,6 +208,9 @@ def test_multi_split_heuristic_values(gqa):
     assert f(1, 8, 65535) == 16                  # 4 tiles: two per workgroup below 65536 tokens
     assert f(1, 8, 65536) == 64
     assert f(1, 64, 65536) == 16                 # 32 tiles: four passes
+    assert f(1, 64, 8192) == 16                  # 32 tiles from 8192 tokens: one tile per wave, four passes
+    assert f(1, 64, 8191) == 2                   # below: two tiles per workgroup, 16 passes
+    assert f(1, 1024, 8192) == 1                 # chunked prefill: 128 passes of 8 tiles fill the GPU
     assert f(8, 16, 32768) == 16                 # a batch: the longest over two rounds
     assert f(1, 4, 8192, 64, 0) == -1
     assert f(1, 0, 8192) == -1
@@ -247,7 +250,7 @@ def test_multi_token_checks_on_the_host(gqa):
         kw.get("q", Q), K, V, L, None, kw.get("out", O), kw.get("B", 2), kw.get("S_q", 4), kw.get("h_q", 64),
         8, kw.get("d", 128), 0.088, 0, 0, 0, None, 0, None)
     assert f(S_q=0) == -1
-    assert f(S_q=65) == -1
+    assert f(S_q=1025) == -1
     # B * S_q * h_q rows past 2^31 (each factor and B * passes within its own limit)
     assert L_.gqa_decode_attn_multi(Q, K, V, L, None, O, 2047, 64, 16 * 2048, 2048, 128, 0.088, 0, 0, 0,
                                     None, 0, None) == -1

@@ -221,3 +221,24 @@ def test_two_tiles_eight_waves_with_a_hint_below_the_lengths():
         err = max_err(got, ref)
         print(f"[multi] eight-wave two tiles, hint 2000 < 4000, ns={ns}: max_abs_err={err:.3e}", flush=True)
         assert err <= TOL_F32
+
+
+@pytest.mark.parametrize("n_rep,S_q,d", [(8, 96, 128), (8, 256, 128), (1, 128, 128), (4, 200, 64), (16, 130, 128)])
+def test_many_query_tokens(n_rep, S_q, d):
+    """Chunked-prefill sizes (past 64 query tokens): many passes of tiles over
+    the KV, causal among the new tokens; sequences longer than S_q, one
+    exactly S_q long and one shorter (its first tokens attend nothing), on
+    both kernels (the length hint picks one)."""
+    h_kv = 2
+    lens = [S_q + 600, S_q, max(1, S_q // 3)]
+    inp, qm = make(f"manyq_r{n_rep}_q{S_q}_d{d}", 3, S_q, n_rep * h_kv, h_kv, d, lens, 300 + n_rep + S_q + d)
+    for ns, hint in ((0, True), (3, True), (0, LONG), (1, LONG)):
+        got, ref = check(f"S_q={S_q} n_rep={n_rep} d={d} ns={ns} hint={hint}", inp, qm, n_splits=ns, hint=hint)
+        assert np.all(got[2, :S_q - lens[2]] == 0)          # positions before the cache's start
+
+
+def test_many_query_tokens_70b_bf16_out():
+    """70B heads, 512 new tokens over 2048 cached ones (a prefill chunk), bf16 out."""
+    inp, qm = make("manyq70b", 1, 512, 64, 8, 128, [2560], 310)
+    check("70B S_q=512", inp, qm)
+    check("70B S_q=512 bf16-out", inp, qm, out_dtype="bf16")
