@@ -69,6 +69,8 @@ constexpr SplitPolicy kTwoTiles{1, 1, 4, 16384, false, false};
 // per CU: one round for a single sequence, up to two for a batch (ragged
 // B = 8, S_q = 16: 209.9 µs at two rounds, 227.9 at four).
 constexpr SplitPolicy kTileWavesPolicy{2, 1, 2, 16384, false, false};
+// Two tiles per wave, sixteen per workgroup, one workgroup per CU.
+constexpr SplitPolicy kTilePairsPolicy{1, 1, 2, 16384, false, false};
 
 // single_token: a single-token entry point. The multi-token one never takes
 // the 8-wave count (so gqa_decode_multi_splits needs no d_head), and takes the
@@ -76,6 +78,7 @@ constexpr SplitPolicy kTileWavesPolicy{2, 1, 2, 16384, false, false};
 // single-token call outside the 8-wave range.
 const SplitPolicy& split_policy(int tiles_per_wg, int d_head, bool single_token, int s_q) {
   if (tiles_per_wg == gqa::kTileWaves) return kTileWavesPolicy;
+  if (tiles_per_wg == gqa::kTilePairs) return kTilePairsPolicy;
   if (tiles_per_wg == 2) return kTwoTiles;
   if (single_token && d_head == 128) return kOneTile;
   return single_token || s_q == 1 ? kOneTile64 : kOneTileMulti;
@@ -177,8 +180,9 @@ size_t ws_bytes(int B, int h_q, int d, int n) { return ws_layout(B, h_q, d, n).t
 
 // ---------------------------------------------------------------- launches
 // Workgroup form of the matrix-core split kernel.
-// kTiles: the multi-token kernel with one query tile per wave (split_kv_tiles).
-enum class Form { kFourWave, kOneWave, kEightWave, kTiles };
+// kTiles / kTilePairs: the multi-token kernel with one / two query tiles per
+// wave (split_kv_tiles).
+enum class Form { kFourWave, kOneWave, kEightWave, kTiles, kTilePairs };
 
 template <int D, int NREP>
 hipError_t launch_split(bool bf16, bool valu, Form form, dim3 grid, hipStream_t st, const gqa::SplitArgs& a) {
@@ -188,6 +192,8 @@ hipError_t launch_split(bool bf16, bool valu, Form form, dim3 grid, hipStream_t 
     hipLaunchKernelGGL((gqa::split_kv_valu<__bf16, D, NREP>), grid, dim3(gqa::kThreads), 0, st, a);
   } else if (form == Form::kTiles) {
     hipLaunchKernelGGL((gqa::split_kv_tiles<D, NREP>), grid, dim3(64 * gqa::kTileWaves), 0, st, a);
+  } else if (form == Form::kTilePairs) {
+    hipLaunchKernelGGL((gqa::split_kv_tiles<D, NREP, 2>), grid, dim3(64 * gqa::kTileWaves), 0, st, a);
   } else if (a.qtiles > a.passes) {               // two column tiles per workgroup
     if (form == Form::kEightWave)
       hipLaunchKernelGGL((gqa::split_kv_mfma<D, NREP, false, 2, 8>), grid, dim3(512), 0, st, a);
@@ -303,6 +309,13 @@ constexpr int64_t kTilesMinTokensLong = 65536;
 // vs 35.3 and at 2.5k S_q = 512 160.3 vs 154.4 (two tiles ahead).
 constexpr int kTilesMinTilesMany = 32;
 constexpr int64_t kTilesMinTokensMany = 8192;
+// Calls that take the tile-per-wave kernel with at least this many tiles per
+// sequence carry two tiles per wave (half the LDS reads per tile, one pass of
+// 16 tiles instead of two of 8). 70B B = 1, µs per call, two tiles per wave
+// vs one: 8k tokens S_q = 64 47.8 vs 50.1, S_q = 128 73.8 vs 81.3; 16k S_q =
+// 32 52.0 vs 53.2, S_q = 48 70.7 vs 98.6; 32k S_q = 32 80.8 vs 86.3, S_q =
+// 64 127.0 vs 144.7; 64k S_q = 32 134.7 vs 151.4.
+constexpr int kTilePairsMinTiles = 16;
 
 // Query tokens per 16-column tile, tiles per sequence, tiles per workgroup
 // (two once a sequence needs two or more, each K/V block then read once for
@@ -316,7 +329,7 @@ void query_tiles(int s_q, int nrep, int B, int64_t hint, int* tpt, int* qtiles, 
   if ((*qtiles >= kTilesMinTiles && tokens >= kTilesMinTokens) ||
       (*qtiles >= kTilesMinTilesLong && tokens >= kTilesMinTokensLong) ||
       (*qtiles >= kTilesMinTilesMany && tokens >= kTilesMinTokensMany))
-    *tpw = gqa::kTileWaves;
+    *tpw = *qtiles >= kTilePairsMinTiles ? gqa::kTilePairs : gqa::kTileWaves;
   *passes = (*qtiles + *tpw - 1) / *tpw;
 }
 
@@ -597,6 +610,7 @@ Form choose_form(const Plan& pl, int B, int h_q, int h_kv, int d_head, int s_q, 
     return fused && f == Form::kOneWave ? Form::kFourWave : f;
   }
   if (tpw == gqa::kTileWaves) return Form::kTiles;
+  if (tpw == gqa::kTilePairs) return Form::kTilePairs;
   if (tpw == 2 && !fused && two_tile_eight_waves(pl, B * passes, h_kv)) return Form::kEightWave;
   return Form::kFourWave;
 }

@@ -198,37 +198,83 @@ struct SoftmaxState {
   float l;   // partial sum of exponentials over this lane's tokens
 };
 
-// Scores of one 16-column tile for a block and the online-softmax update of
-// its state (running max, sum, and the rescale of its accumulators); gives
-// P^T as bf16 hi + lo parts in the B-operand layout.
+// P^T as bf16 hi + lo parts in the B-operand layout: two values per
+// conversion (round to nearest even, as the scalar cast); a bf16 read back as
+// fp32 is its bits in the upper half, and the part it misses is rounded again.
+__device__ __forceinline__ void split_p(const float (&p)[8], bf16x8& ph, bf16x8& pl) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const bf16x2_t h = __builtin_convertvector((f32x2_t){p[j], p[j + 1]}, bf16x2_t);
+    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+    const float h0 = __uint_as_float(hb << 16), h1 = __uint_as_float(hb & 0xFFFF0000u);
+    const bf16x2_t l = __builtin_convertvector((f32x2_t){p[j] - h0, p[j + 1] - h1}, bf16x2_t);
+    ph[j] = h[0];
+    ph[j + 1] = h[1];
+    pl[j] = l[0];
+    pl[j + 1] = l[1];
+  }
+}
+
+// Scores of one 16-column tile for a block in log2 units: x[j] is the score of
+// token slot_token(grp, j) for this lane's column.
 template <int D>
-__device__ __forceinline__ void softmax_block(const KVRegs<D>& r, const bf16x8 (&qop)[MfmaTile<D>::KS],
-                                              f32x4 (&acc)[MfmaTile<D>::NT], SoftmaxState& st,
-                                              float scale_log2, int grp, bool mask, int nvl,
-                                              bf16x8& ph, bf16x8& pl) {
-  constexpr int KS = MfmaTile<D>::KS, NT = MfmaTile<D>::NT;
+__device__ __forceinline__ void tile_scores(const KVRegs<D>& r, const bf16x8 (&qop)[MfmaTile<D>::KS],
+                                            float scale_log2, float (&x)[8]) {
+  constexpr int KS = MfmaTile<D>::KS;
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
     s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k[0][kk]), qop[kk], s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k[1][kk]), qop[kk], s1, 0, 0, 0);
   }
-  float x[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     x[i] = s0[i] * scale_log2;
     x[4 + i] = s1[i] * scale_log2;
   }
+}
+
+// The block's max of this lane's column (over the 4 lane groups), after the
+// masked positions (slot tokens at or past nvl) are set to -inf.
+__device__ __forceinline__ float block_max(float (&x)[8], int grp, bool mask, int nvl) {
   if (mask) {                                // tail of the chunk, or causal limit of the column
+    // slot_token(grp, j) >= nvl, with the lane group's part on the right so
+    // that the slot's part stays an immediate (no registers held for it).
+    const int rel = nvl - 4 * grp;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (slot_token(grp, j) >= nvl) x[j] = -INFINITY;
+      if ((j < 4 ? j : 12 + j) >= rel) x[j] = -INFINITY;
   }
   float mb = x[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) mb = fmaxf(mb, x[j]);
-  mb = max_x32(max_x16(mb));                  // over the 4 lane groups of the column
-  const float mn = fmaxf(st.m, mb);
+  return max_x32(max_x16(mb));
+}
+
+// Slack of the lazy reference max (log2 units): see softmax_update.
+constexpr float kRescaleSlack = 8.f;
+
+// The online-softmax update of a tile's state for a block (running max, sum,
+// and the rescale of its accumulators) from the block's scores x and their
+// max mb; gives P^T as bf16 hi + lo parts.
+//
+// LAZY: st.m is a reference point instead of the running max. It moves (to
+// the block's max) only when a column's block max exceeds it by more than
+// kRescaleSlack, so the exponentials are taken against a reference up to 8
+// below the max: values up to 2^8, exact in fp32 and split into bf16 hi + lo
+// as before, and l and o stay consistent with the reference (o / l is the
+// same; m + log2(l) is the log-sum-exp either way). The accumulators are then
+// rescaled only in the rare blocks where the reference moves, instead of in
+// nearly every block of a chunk's first few dozen, where some of a tile's 16
+// columns finds a new max.
+template <int D, bool LAZY = false>
+__device__ __forceinline__ void softmax_update(const float (&x)[8], float mb, f32x4 (&acc)[MfmaTile<D>::NT],
+                                               SoftmaxState& st, bf16x8& ph, bf16x8& pl) {
+  constexpr int NT = MfmaTile<D>::NT;
+  // -inf + slack = -inf: the first block with a position moves the reference.
+  const float mn = LAZY ? (mb > st.m + kRescaleSlack ? mb : st.m) : fmaxf(st.m, mb);
   // mn = -inf only while every position this column has seen is masked (a
   // causal column before its first position); keep alpha and p at 0 then.
   const float mref = (mn == -INFINITY) ? 0.f : mn;
@@ -249,21 +295,20 @@ __device__ __forceinline__ void softmax_block(const KVRegs<D>& r, const bf16x8 (
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
   }
-  // Two values per conversion (round to nearest even, as the scalar cast);
-  // a bf16 read back as fp32 is its bits in the upper half.
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-#pragma unroll
-  for (int j = 0; j < 8; j += 2) {
-    const bf16x2_t h = __builtin_convertvector((f32x2_t){p[j], p[j + 1]}, bf16x2_t);
-    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
-    const float h0 = __uint_as_float(hb << 16), h1 = __uint_as_float(hb & 0xFFFF0000u);
-    const bf16x2_t l = __builtin_convertvector((f32x2_t){p[j] - h0, p[j + 1] - h1}, bf16x2_t);
-    ph[j] = h[0];
-    ph[j + 1] = h[1];
-    pl[j] = l[0];
-    pl[j + 1] = l[1];
-  }
+  split_p(p, ph, pl);
+}
+
+// Scores of one 16-column tile for a block and the online-softmax update of
+// its state; gives P^T as bf16 hi + lo parts in the B-operand layout.
+template <int D, bool LAZY = false>
+__device__ __forceinline__ void softmax_block(const KVRegs<D>& r, const bf16x8 (&qop)[MfmaTile<D>::KS],
+                                              f32x4 (&acc)[MfmaTile<D>::NT], SoftmaxState& st,
+                                              float scale_log2, int grp, bool mask, int nvl,
+                                              bf16x8& ph, bf16x8& pl) {
+  float x[8];
+  tile_scores<D>(r, qop, scale_log2, x);
+  const float mb = block_max(x, grp, mask, nvl);
+  softmax_update<D, LAZY>(x, mb, acc, st, ph, pl);
 }
 
 // O^T += V^T P^T for TILES column tiles that share the block's V: each V^T

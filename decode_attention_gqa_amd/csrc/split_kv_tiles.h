@@ -15,12 +15,29 @@
 // one triplet per (query token, head) of its tiles, or o / l when the
 // sequence has one chunk.
 //
+// TPW = 2: each wave carries two tiles (tiles w and w + 8 of the workgroup's
+// 16), with their own softmax states and accumulators; the block's K and V
+// operands are read from LDS once for both, the V^T permutes are formed once
+// for both, and the two tiles' independent softmax chains give the wave
+// work to interleave with the other's matrix products. Twice the state takes
+// about 200 registers: one workgroup (8 waves) per CU.
+//
 // Staging: two LDS buffers in turn. While the waves compute block i from one
 // buffer, each thread has its pieces of block i + 1 in flight from HBM to
 // registers; it stores them into the other buffer afterwards, and one
 // workgroup barrier per block orders the two. K rows are padded by 16 bytes
 // in LDS, so the 16 lanes of a lane group, which read the same columns of 16
 // different rows, hit 16 different bank groups.
+//
+// V^T operands come straight from LDS through gfx950's transposing read
+// (ds_read_b64_tr_b16): in each 16-lane group the lanes' 8-byte reads form a
+// 4 x 16 matrix of 16-bit values, 4 lanes per row, and lane i receives its
+// column i. With row r = token 4*grp + r (+ 16) and the 16 columns = 16
+// consecutive dimensions, lane (grp, n) receives dimension n of the tile's
+// 16 at the 4 tokens of its operand slots, which is the MFMA A operand of
+// O^T = V^T P^T with no byte permutes (split_kv_mfma forms it with 32
+// permutes per block from whole-row loads). V rows are padded by 32 bytes so
+// that the 4 rows a lane group reads fall in different banks.
 #pragma once
 
 #include "split_kv_mfma.h"
@@ -28,23 +45,33 @@
 namespace gqa {
 
 constexpr int kTileWaves = 8;                       // waves (= tiles) per workgroup
+constexpr int kTilePairs = 2 * kTileWaves;          // tiles per workgroup at two per wave
 
 template <int D>
 struct LdsBlock {
   static constexpr int ROW = D * 2;                 // bytes of one head's K (or V) row
   static constexpr int KROW = ROW + 16;             // padded K row in LDS
-  static constexpr int VROW = ROW;                  // V rows: a lane group reads one row across
+  static constexpr int VROW = ROW + 32;             // padded V row (transposing reads)
   static constexpr int KBYTES = 32 * KROW;
   static constexpr int BYTES = KBYTES + 32 * VROW;  // one staged block
   static constexpr int RP = ROW / 16;               // 16-byte pieces per row
   static constexpr int PIECES = 2 * 32 * RP;        // pieces of a block's K and V rows
 };
 
-template <int D, int NREP>
-__global__ __launch_bounds__(64 * kTileWaves) __attribute__((amdgpu_waves_per_eu(4)))
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// 8 bytes through the transposing LDS read (see above); p points into LDS.
+__device__ __forceinline__ s16x4_t lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+}
+
+template <int D, int NREP, int TPW = 1>
+__global__ __launch_bounds__(64 * kTileWaves) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 4 : 2)))
 void split_kv_tiles(SplitArgs a) {
+  static_assert(TPW == 1 || TPW == 2, "one or two tiles per wave");
   constexpr int NT = MfmaTile<D>::NT, KS = MfmaTile<D>::KS, VW = MfmaTile<D>::VW;
   constexpr int TW = kTileWaves, THREADS = 64 * TW;
+  constexpr int TPG = TW * TPW;                     // tiles of a workgroup (one pass)
   using L = LdsBlock<D>;
   static_assert(L::PIECES % THREADS == 0, "a block's pieces spread evenly over the threads");
   constexpr int PPT = L::PIECES / THREADS;
@@ -62,11 +89,16 @@ void split_kv_tiles(SplitArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = lane >> 4, n = lane & 15;
-  const int tile = pass * TW + w;                   // this wave's tile of the sequence
-  const bool has_tile = tile < a.qtiles;
   const int ti = n / NREP, hh = n % NREP;
-  const int qi = tile * a.tpt + ti;                 // column n: query token qi, head g*NREP + hh
-  const bool col = has_tile && ti < a.tpt && qi < a.s_q;
+  int tile[TPW], qi[TPW];                           // this wave's tiles of the sequence
+  bool col[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    tile[t] = pass * TPG + t * TW + w;
+    qi[t] = tile[t] * a.tpt + ti;                   // column n: query token qi, head g*NREP + hh
+    col[t] = tile[t] < a.qtiles && ti < a.tpt && qi[t] < a.s_q;
+  }
+  const bool has_tile = tile[0] < a.qtiles;         // a wave's second tile comes after every first one
   const int cols = NREP * a.tpt;                    // columns in use (<= 16)
 
   int S;
@@ -79,8 +111,8 @@ void split_kv_tiles(SplitArgs a) {
   chunking(S, a.n_splits, a.min_chunk, c, n_active);
   if (s >= n_active) {                              // the merge reads chunks < n_active only
     if (a.direct && n_active == 0 && s == 0) {      // nothing attended: out = 0
-      for (int idx = tid; idx < TW * cols * Q4; idx += THREADS) {
-        const int t = pass * TW + idx / (cols * Q4), h = (idx / Q4) % cols;
+      for (int idx = tid; idx < TPG * cols * Q4; idx += THREADS) {
+        const int t = pass * TPG + idx / (cols * Q4), h = (idx / Q4) % cols;
         const int cqi = t * a.tpt + h / NREP;
         if (t >= a.qtiles || cqi >= a.s_q) continue;
         const int64_t e = (((int64_t)b * a.s_q + cqi) * a.h_q + g * NREP + h % NREP) * D + (idx % Q4) * 4;
@@ -99,25 +131,31 @@ void split_kv_tiles(SplitArgs a) {
   const char* vb0 = reinterpret_cast<const char*>(static_cast<const __bf16*>(a.v) + ((off + t0) * a.h_kv + g) * D);
 
   // Q^T as the B operand, as in split_kv_mfma.
-  bf16x8 qop[KS];
-  {
+  bf16x8 qop[TPW][KS];
+  int lim[TPW], lim0[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
     const __bf16* qrow =
-        static_cast<const __bf16*>(a.q) + (((int64_t)b * a.s_q + qi) * a.h_q + g * NREP + hh) * D + 8 * grp;
+        static_cast<const __bf16*>(a.q) + (((int64_t)b * a.s_q + qi[t]) * a.h_q + g * NREP + hh) * D + 8 * grp;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       uint4 u = make_uint4(0u, 0u, 0u, 0u);
-      if (col) u = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
-      qop[kk] = __builtin_bit_cast(bf16x8, u);
+      if (col[t]) u = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
+      qop[t][kk] = __builtin_bit_cast(bf16x8, u);
     }
+    lim[t] = S - a.s_q + qi[t];                     // last position column n attends (causal)
+    lim0[t] = S - a.s_q + tile[t] * a.tpt;          // the tile's smallest limit (its first token's)
   }
-  const int lim = S - a.s_q + qi;                   // last position column n attends (causal)
-  const int lim0 = S - a.s_q + tile * a.tpt;        // the tile's smallest limit (its first token's)
   const bool causal = a.s_q > 1;
 
-  f32x4 acc[1][NT];
+  f32x4 acc[TPW][NT];
+  SoftmaxState st[TPW];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[0][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  SoftmaxState st{-INFINITY, 0.f};
+  for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st[t] = SoftmaxState{-INFINITY, 0.f};
+  }
 
   const int nblk = (ntok >> 5) + ((ntok & 31) != 0);
 
@@ -126,53 +164,83 @@ void split_kv_tiles(SplitArgs a) {
   // the block's valid count are clamped to its last valid row (masked in the
   // softmax).
   uint4 stage[PPT];
+  uint32_t goff[PPT], loff[PPT];                    // a piece's byte offset in a full block / in LDS
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int p = tid + i * THREADS;
+    const int r = (p / L::RP) % 32, pc = p % L::RP;
+    goff[i] = (uint32_t)r * row_bytes + 16 * pc;
+    loff[i] = p < 32 * L::RP ? r * L::KROW + 16 * pc : L::KBYTES + r * L::VROW + 16 * pc;
+  }
   auto gload = [&](int bk) {
     const int nv = min(32, ntok - bk * 32);
     const char* kb = kb0 + (int64_t)bk * 32 * row_bytes;
     const char* vb = vb0 + (int64_t)bk * 32 * row_bytes;
+    if (nv == 32) {                                 // every block but a chunk's partial last one
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = tid + i * THREADS;
-      const int r = min((p / L::RP) % 32, nv - 1), pc = p % L::RP;
-      stage[i] = load_stream16((p < 32 * L::RP ? kb : vb) + (uint32_t)r * row_bytes + 16 * pc);
+      for (int i = 0; i < PPT; ++i) stage[i] = load_stream16((tid + i * THREADS < 32 * L::RP ? kb : vb) + goff[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < PPT; ++i) {
+        const int p = tid + i * THREADS;
+        const int r = min((p / L::RP) % 32, nv - 1), pc = p % L::RP;
+        stage[i] = load_stream16((p < 32 * L::RP ? kb : vb) + (uint32_t)r * row_bytes + 16 * pc);
+      }
     }
   };
   auto lstore = [&](int buf) {
     char* base = lds + buf * L::BYTES;
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int p = tid + i * THREADS;
-      const int r = (p / L::RP) % 32, pc = p % L::RP;
-      char* dst = p < 32 * L::RP ? base + r * L::KROW + 16 * pc : base + L::KBYTES + r * L::VROW + 16 * pc;
-      *reinterpret_cast<uint4*>(dst) = stage[i];
-    }
+    for (int i = 0; i < PPT; ++i) *reinterpret_cast<uint4*>(base + loff[i]) = stage[i];
   };
+  // This lane's LDS offsets: K rows n (+ 16) at bytes 16*grp (+ 64*kk); the
+  // transposing V reads at row 4*grp + n/4 (+ 16), bytes 8*(n%4) (+ 32*nt).
+  const uint32_t kofs = n * L::KROW + 16 * grp;
+  const uint32_t vofs = L::KBYTES + (4 * grp + n / 4) * L::VROW + 8 * (n % 4);
   auto compute = [&](int buf, int bk) {
     const char* base = lds + buf * L::BYTES;
-    KVRegs<D> r;
+    KVRegs<D> r;                                    // K only (V^T below)
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk)
-        r.k[x][kk] = *reinterpret_cast<const uint4*>(base + (16 * x + n) * L::KROW + 16 * grp + 64 * kk);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const char* vp = base + L::KBYTES + slot_token(grp, j) * L::VROW + 2 * NT * n;
-      if constexpr (VW == 4) {
-        const uint4 u = *reinterpret_cast<const uint4*>(vp);
-        r.v[j][0] = u.x; r.v[j][1] = u.y; r.v[j][2] = u.z; r.v[j][3] = u.w;
-      } else {
-        const uint2 u = *reinterpret_cast<const uint2*>(vp);
-        r.v[j][0] = u.x; r.v[j][1] = u.y;
-      }
-    }
+        r.k[x][kk] = *reinterpret_cast<const uint4*>(base + kofs + 16 * x * L::KROW + 64 * kk);
     const int nv = min(32, ntok - bk * 32);
-    const int nvl = causal ? min(nv, lim - ((int)t0 + bk * 32) + 1) : nv;
-    // The causal mask matters only in blocks past the tile's first token's limit.
-    const bool mask = nv < 32 || (causal && (int)t0 + bk * 32 + nv - 1 > lim0);
-    bf16x8 ph[1], pl[1];
-    softmax_block<D>(r, qop, acc[0], st, a.scale_log2, grp, mask, nvl, ph[0], pl[0]);
-    pv_block<D, 1>(r, acc, ph, pl);
+    bool mask[TPW];
+    int nvl[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      nvl[t] = causal ? min(nv, lim[t] - ((int)t0 + bk * 32) + 1) : nv;
+      // The causal mask matters only in blocks past the tile's first token's limit.
+      mask[t] = nv < 32 || (causal && (int)t0 + bk * 32 + nv - 1 > lim0[t]);
+    }
+    // The scores first (the K registers are free once the products have
+    // read them), then the V^T operands of output tile nt: dimension
+    // 16*nt + n at tokens 4*grp + 0..3 and 16 + 4*grp + 0..3 (the slots of the
+    // P^T operand).
+    float x[TPW][8];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) tile_scores<D>(r, qop[t], a.scale_log2, x[t]);
+    bf16x8 vt[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const s16x4_t lo = lds_read_tr16(base + vofs + 32 * nt);
+      const s16x4_t hi = lds_read_tr16(base + vofs + 16 * L::VROW + 32 * nt);
+      vt[nt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    bf16x8 ph[TPW], pl[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const float mb = block_max(x[t], grp, mask[t], nvl[t]);
+      softmax_update<D, true>(x[t], mb, acc[t], st[t], ph[t], pl[t]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[nt], ph[t], acc[t][nt], 0, 0, 0);
+        acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[nt], pl[t], acc[t][nt], 0, 0, 0);
+      }
   };
 
   gload(0);
@@ -187,27 +255,30 @@ void split_kv_tiles(SplitArgs a) {
       __syncthreads();                              // the next block is staged; this one is read
     }
   }
-  __syncthreads();                                  // the staging buffers become the epilogue's
-
-  // Write the tiles' triplets (or o / l) through LDS, 4 floats per thread and step.
+  // Write the tiles' triplets (or o / l) through LDS, 4 floats per thread and
+  // step, the waves' t-th tiles in round t.
   float* sm_o = reinterpret_cast<float*>(lds);      // [TW][16][OP]
-  const float l = sum_x32(sum_x16(st.l));
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+  __syncthreads();                                  // the staging buffers (or the last round's) are free
+  const float l = sum_x32(sum_x16(st[t].l));
   if (grp == 0) {
-    sm_m[w][n] = st.m;
+    sm_m[w][n] = st[t].m;
     sm_l[w][n] = l;
   }
   if (n < cols) {
-    // lane (grp, n) holds o[column n][NT*(4*grp + r) + nt]
+    // lane (grp, n) holds o[column n][16*nt + 4*grp + r]
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sm_o[(w * 16 + n) * OP + NT * (4 * grp + r) + nt] = acc[0][nt][r];
+      for (int nt = 0; nt < NT; ++nt) sm_o[(w * 16 + n) * OP + 16 * nt + 4 * grp + r] = acc[t][nt][r];
   }
   __syncthreads();
   for (int idx = tid; idx < TW * cols * Q4; idx += THREADS) {
     const int ww = idx / (cols * Q4), h = (idx / Q4) % cols, d4 = (idx % Q4) * 4;
-    const int cqi = (pass * TW + ww) * a.tpt + h / NREP;
-    if (pass * TW + ww >= a.qtiles || cqi >= a.s_q) continue;
+    const int ct = pass * TPG + t * TW + ww;        // the tile of wave ww's round-t state
+    const int cqi = ct * a.tpt + h / NREP;
+    if (ct >= a.qtiles || cqi >= a.s_q) continue;
     const float4 o = *reinterpret_cast<const float4*>(sm_o + (ww * 16 + h) * OP + d4);
     const float M = sm_m[ww][h], Lsum = sm_l[ww][h];
     const int64_t orow = ((int64_t)b * a.s_q + cqi) * a.h_q + g * NREP + h % NREP;   // (b, token, head)
@@ -223,6 +294,7 @@ void split_kv_tiles(SplitArgs a) {
       *reinterpret_cast<float4*>(a.ws_o + row * D + d4) = o;
       if (d4 == 0) a.ws_ml[row] = make_float2(M, Lsum);
     }
+  }
   }
 }
 

@@ -98,10 +98,12 @@ LONG = 65536
 
 
 @pytest.mark.parametrize("n_rep,S_q,d", [(8, 16, 128), (8, 16, 64), (8, 13, 128), (8, 64, 128), (4, 32, 128),
-                                         (2, 64, 64), (1, 64, 128), (16, 8, 128), (16, 5, 64)])
+                                         (2, 64, 64), (1, 64, 128), (16, 8, 128), (16, 5, 64), (8, 40, 64),
+                                         (8, 40, 128)])
 def test_tile_waves_parity(n_rep, S_q, d):
-    """One tile per wave: ragged lengths (a partial last block, a sequence
-    shorter than one block), several passes (S_q = 64, n_rep = 8: 32 tiles),
+    """One or two tiles per wave (16 or more tiles: two): ragged lengths (a
+    partial last block, a sequence shorter than one block), several passes
+    (S_q = 64, n_rep = 8: 32 tiles; S_q = 40: 20, a second pass of 4),
     a last tile with fewer tokens than it holds (S_q = 13, 5), split counts
     from one chunk (written out directly) to more chunks than blocks; against
     the oracle, and against the two-tile kernel (the same sums in another
@@ -223,12 +225,15 @@ def test_two_tiles_eight_waves_with_a_hint_below_the_lengths():
         assert err <= TOL_F32
 
 
-@pytest.mark.parametrize("n_rep,S_q,d", [(8, 96, 128), (8, 256, 128), (1, 128, 128), (4, 200, 64), (16, 130, 128)])
+@pytest.mark.parametrize("n_rep,S_q,d", [(8, 96, 128), (8, 256, 128), (1, 128, 128), (4, 200, 64), (16, 130, 128),
+                                         (8, 90, 128), (8, 90, 64)])
 def test_many_query_tokens(n_rep, S_q, d):
     """Chunked-prefill sizes (past 64 query tokens): many passes of tiles over
     the KV, causal among the new tokens; sequences longer than S_q, one
     exactly S_q long and one shorter (its first tokens attend nothing), on
-    both kernels (the length hint picks one)."""
+    both kernels (the length hint picks one; the long hint gives 32 or more
+    tiles two per wave, with a last pass whose waves hold two tiles, one
+    tile (S_q = 90: 45 tiles, 13 in the last pass) or none (130 tiles, 2))."""
     h_kv = 2
     lens = [S_q + 600, S_q, max(1, S_q // 3)]
     inp, qm = make(f"manyq_r{n_rep}_q{S_q}_d{d}", 3, S_q, n_rep * h_kv, h_kv, d, lens, 300 + n_rep + S_q + d)
