@@ -303,12 +303,6 @@ constexpr int kTilesMinTiles = 8;
 constexpr int64_t kTilesMinTokens = 16384;
 constexpr int kTilesMinTilesLong = 4;          // fewer tiles take it only over longer KV
 constexpr int64_t kTilesMinTokensLong = 65536;
-// Many tiles (chunked-prefill sizes) take it from 8192 tokens: 70B B = 1,
-// 8k tokens, µs per call (one tile per wave vs two tiles): S_q = 64 59.4 vs
-// 64.8, 128 97.4 vs 110.9, 512 325.8 vs 396.0; at 2k tokens S_q = 128 41.4
-// vs 35.3 and at 2.5k S_q = 512 160.3 vs 154.4 (two tiles ahead).
-constexpr int kTilesMinTilesMany = 32;
-constexpr int64_t kTilesMinTokensMany = 8192;
 // Calls that take the tile-per-wave kernel with at least this many tiles per
 // sequence carry two tiles per wave (half the LDS reads per tile, one pass of
 // 16 tiles instead of two of 8). 70B B = 1, µs per call, two tiles per wave
@@ -316,6 +310,15 @@ constexpr int64_t kTilesMinTokensMany = 8192;
 // 32 52.0 vs 53.2, S_q = 48 70.7 vs 98.6; 32k S_q = 32 80.8 vs 86.3, S_q =
 // 64 127.0 vs 144.7; 64k S_q = 32 134.7 vs 151.4.
 constexpr int kTilePairsMinTiles = 16;
+// Such calls (chunked-prefill sizes) take it once tiles x tokens reaches
+// this. 70B B = 1, µs per call, two tiles per wave vs the two-tile kernel:
+// 2^18 and above: 512 tokens S_q = 1024 42.1 vs 89.3; 1k S_q = 512 51.8 vs
+// 74.2, S_q = 1024 67.7 vs 138.1; 2k S_q = 256 51.4 vs 63.8, S_q = 512 77.8
+// vs 124.4; 2.5k S_q = 512 86.8 vs 138.5; 4k S_q = 128 53.1 vs 59.5, S_q =
+// 256 77.7 vs 111.8; 8k S_q = 64 47.8 vs 64.8. Below: 1k S_q = 64 29.0 vs
+// 18.2; 2k S_q = 32 27.1 vs 18.3, S_q = 128 39.2 vs 33.9; 8k S_q = 32 39.0
+// vs 37.6 (4k S_q = 64: 36.6 vs 38.1, near even).
+constexpr int64_t kTilesMinWork = int64_t(1) << 18;
 
 // Query tokens per 16-column tile, tiles per sequence, tiles per workgroup
 // (two once a sequence needs two or more, each K/V block then read once for
@@ -328,7 +331,7 @@ void query_tiles(int s_q, int nrep, int B, int64_t hint, int* tpt, int* qtiles, 
   const int64_t tokens = hint > 0 ? (int64_t)B * hint : 0;
   if ((*qtiles >= kTilesMinTiles && tokens >= kTilesMinTokens) ||
       (*qtiles >= kTilesMinTilesLong && tokens >= kTilesMinTokensLong) ||
-      (*qtiles >= kTilesMinTilesMany && tokens >= kTilesMinTokensMany))
+      (*qtiles >= kTilePairsMinTiles && (int64_t)*qtiles * tokens >= kTilesMinWork))
     *tpw = *qtiles >= kTilePairsMinTiles ? gqa::kTilePairs : gqa::kTileWaves;
   *passes = (*qtiles + *tpw - 1) / *tpw;
 }

@@ -207,10 +207,13 @@ def test_multi_split_heuristic_values(gqa):
     assert f(2, 16, 8192) == 32                  # B times the longest length counts
     assert f(1, 8, 65535) == 16                  # 4 tiles: two per workgroup below 65536 tokens
     assert f(1, 8, 65536) == 64
-    assert f(1, 64, 65536) == 16                 # 32 tiles: four passes
-    assert f(1, 64, 8192) == 16                  # 32 tiles from 8192 tokens: one tile per wave, four passes
+    assert f(1, 64, 65536) == 16                 # 32 tiles: two per wave, two passes, one workgroup per CU
+    assert f(1, 64, 8192) == 16                  # 32 tiles x 8192 tokens = 2^18: the same
     assert f(1, 64, 8191) == 2                   # below: two tiles per workgroup, 16 passes
-    assert f(1, 1024, 8192) == 1                 # chunked prefill: 128 passes of 8 tiles fill the GPU
+    assert f(1, 128, 4096) == 8                  # 64 tiles x 4096: two per wave, four passes
+    assert f(1, 128, 2048) == 1                  # below: 32 passes of two tiles fill the GPU
+    assert f(1, 32, 16384) == 32                 # 16 tiles from 16384 tokens: one pass of two per wave
+    assert f(1, 1024, 8192) == 1                 # chunked prefill: 32 passes of 16 tiles fill the GPU
     assert f(8, 16, 32768) == 16                 # a batch: the longest over two rounds
     assert f(1, 4, 8192, 64, 0) == -1
     assert f(1, 0, 8192) == -1
