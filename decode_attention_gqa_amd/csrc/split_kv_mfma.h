@@ -485,7 +485,9 @@ void split_kv_mfma(SplitArgs a) {
         const int nvl = causal ? min(nv, lim[t] - ((int)t0 + bk * 32) + 1) : nv;
         // The causal mask matters only in blocks past the tile's first token's limit.
         const bool mask = nv < 32 || (causal && (int)t0 + bk * 32 + nv - 1 > lim0[t]);
-        softmax_block<D>(r, qop[t], acc[t], st[t], a.scale_log2, grp, mask, nvl, ph[t], pl[t]);
+        // Two tiles serve only multi-token calls, whose triplets stay inside
+        // the library: the lazy reference applies (see softmax_update).
+        softmax_block<D, TILES == 2>(r, qop[t], acc[t], st[t], a.scale_log2, grp, mask, nvl, ph[t], pl[t]);
       }
       pv_block<D, TILES>(r, acc, ph, pl);
     };

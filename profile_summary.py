@@ -164,7 +164,19 @@ def trace_only(a):
     for n, c, avg, mn, mx in kernel_stats(a.kt):
         if "gqa::" in n:
             lines.append(f"| `{n}` | {c} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} |")
-    lines += ["", "## Command (run from the repository root)", "", f"    {a.cmd_kt}", ""]
+    cmds = [a.cmd_kt]
+    if a.busy:
+        busy = {name: pick(counters(a.busy, name), a.split_key)
+                for name in ("VALUBusy", "MfmaUtil", "SQ_INSTS_VALU", "SQ_INSTS_MFMA")}
+        kname = busy["VALUBusy"][0]
+        lines += ["", "## Compute units (rocprofv3 --pmc), split kernel, per dispatch", "",
+                  f"`{kname}`: VALUBusy {busy['VALUBusy'][1][1]:.1f}% (vector ALU busy, share of the kernel's "
+                  f"GPU time), MfmaUtil {busy['MfmaUtil'][1][1]:.1f}% (matrix cores busy); "
+                  f"{busy['SQ_INSTS_VALU'][1][1]:.0f} VALU and {busy['SQ_INSTS_MFMA'][1][1]:.0f} MFMA "
+                  f"instructions ({busy['VALUBusy'][1][0]} dispatches)"]
+        if a.cmd_busy:
+            cmds.append(a.cmd_busy)
+    lines += ["", "## Commands (run from the repository root)", ""] + [f"    {c}" for c in cmds] + [""]
     md = os.path.join(ROOT, "profiles", f"{a.trace_only}.md")
     open(md, "w").write("\n".join(lines) + "\n")
     print(open(md).read())
