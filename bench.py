@@ -36,6 +36,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E datasheet peak
 DEFAULT_WORKLOAD = "llama70b_gqa_b1_s8192"
 ROTATE_BYTES = 1 << 30
@@ -606,6 +607,31 @@ def main() -> int:
                    "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
                    "hip": torch.version.hip},
     }
+    if args.s_q > 1:
+        # Several query tokens: the call is a batch of small matrix products
+        # (intensity grows with S_q), so its roofline is the bf16 matrix-core
+        # peak. Algorithmic FLOPs: QK^T and PV, 2*d each per (query token,
+        # head, attended position), token i of sequence b attending its
+        # S_b - S_q + i + 1 positions (causal among the new tokens). Timed as
+        # whole calls (split + merge) in the graph: there is no split-only
+        # entry point for S_q > 1.
+        import numpy as np
+        lens_np = inp.seq_lens.astype(np.int64)
+        att = np.clip(lens_np[:, None] - args.s_q + np.arange(args.s_q)[None, :] + 1, 0, None)
+        flops = float(att.sum()) * w.h_q * 4 * w.d
+        tflops = flops / sec_per_call / 1e12
+        res["roofline"] = {
+            "bound": "mfma",
+            "kernel": "multi-token split + merge (whole call)",
+            "achieved": round(tflops, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": None,
+            "algorithmic_flops_per_call": flops,
+            "kernel_us": sec_per_call * 1e6,
+            "kv_gbs_by_eager_calls": round(achieved, 2),
+        }
     if not args.no_extra and args.workload == DEFAULT_WORKLOAD and not args.seq_lens and args.s_q == 1 \
             and not (args.valu or args.fused or args.eager or args.n_splits):
         del sets
