@@ -226,7 +226,7 @@ def test_two_tiles_eight_waves_with_a_hint_below_the_lengths():
 
 
 @pytest.mark.parametrize("n_rep,S_q,d", [(8, 96, 128), (8, 256, 128), (1, 128, 128), (4, 200, 64), (16, 130, 128),
-                                         (8, 90, 128), (8, 90, 64)])
+                                         (8, 90, 128), (8, 90, 64), (2, 160, 64), (1, 272, 128)])
 def test_many_query_tokens(n_rep, S_q, d):
     """Chunked-prefill sizes (past 64 query tokens): many passes of tiles over
     the KV, causal among the new tokens; sequences longer than S_q, one
