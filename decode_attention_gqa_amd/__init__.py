@@ -36,7 +36,7 @@ GQA_DTYPE_BF16 = 1
 GQA_FLAG_VALU = 1
 GQA_FLAG_FUSED = 2
 GQA_MAX_SPLITS = 4096
-GQA_MAX_QUERY_TOKENS = 1024
+GQA_MAX_QUERY_TOKENS = 16384
 GQA_SCRATCH_BYTES = 16 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_decode.so")

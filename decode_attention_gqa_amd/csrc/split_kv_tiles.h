@@ -147,6 +147,13 @@ void split_kv_tiles(SplitArgs a) {
     lim0[t] = S - a.s_q + tile[t] * a.tpt;          // the tile's smallest limit (its first token's)
   }
   const bool causal = a.s_q > 1;
+  // The largest limit among the wave's query tokens: a block that starts
+  // past it is masked for every column of the wave, which skips it (the
+  // upper triangle of a prefill-sized call; its state stays as it was).
+  int lim_hi = -1;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+    if (tile[t] < a.qtiles) lim_hi = max(lim_hi, S - a.s_q + min(tile[t] * a.tpt + a.tpt, a.s_q) - 1);
 
   f32x4 acc[TPW][NT];
   SoftmaxState st[TPW];
@@ -249,7 +256,7 @@ void split_kv_tiles(SplitArgs a) {
   for (int bk = 0; bk < nblk; ++bk) {
     const bool more = bk + 1 < nblk;               // uniform over the workgroup
     if (more) gload(bk + 1);
-    if (has_tile) compute(bk & 1, bk);
+    if (has_tile && !(causal && (int)t0 + bk * 32 > lim_hi)) compute(bk & 1, bk);
     if (more) {
       lstore((bk + 1) & 1);
       __syncthreads();                              // the next block is staged; this one is read

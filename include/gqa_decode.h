@@ -87,8 +87,9 @@ enum {
 #define GQA_MAX_SPLITS 4096
 
 /* Largest number of query tokens per sequence of gqa_decode_attn_multi
- * (speculative decoding verifies a few; chunked prefill sends hundreds). */
-#define GQA_MAX_QUERY_TOKENS 1024
+ * (speculative decoding verifies a few, chunked prefill sends hundreds to
+ * thousands, the prefill of a whole prompt as many as it holds). */
+#define GQA_MAX_QUERY_TOKENS 16384
 
 /*
  * Attention for bf16 q/k_cache/v_cache in the packed layout, fp32 `out`, on

@@ -253,7 +253,7 @@ def test_multi_token_checks_on_the_host(gqa):
         kw.get("q", Q), K, V, L, None, kw.get("out", O), kw.get("B", 2), kw.get("S_q", 4), kw.get("h_q", 64),
         8, kw.get("d", 128), 0.088, 0, 0, 0, None, 0, None)
     assert f(S_q=0) == -1
-    assert f(S_q=1025) == -1
+    assert f(S_q=16385) == -1
     # B * S_q * h_q rows past 2^31 (each factor and B * passes within its own limit)
     assert L_.gqa_decode_attn_multi(Q, K, V, L, None, O, 2047, 64, 16 * 2048, 2048, 128, 0.088, 0, 0, 0,
                                     None, 0, None) == -1

@@ -247,3 +247,25 @@ def test_many_query_tokens_70b_bf16_out():
     inp, qm = make("manyq70b", 1, 512, 64, 8, 128, [2560], 310)
     check("70B S_q=512", inp, qm)
     check("70B S_q=512 bf16-out", inp, qm, out_dtype="bf16")
+
+
+@pytest.mark.parametrize("n_rep,S_q,d,lens", [(4, 2048, 64, [2348, 2048, 900]), (8, 1536, 128, [1536])])
+def test_prefill_sized(n_rep, S_q, d, lens):
+    """Prefill-sized calls: thousands of new tokens, the whole prompt when
+    S_b = S_q (its causal upper triangle is half the score matrix, and the
+    waves skip the blocks past all of their tokens' limits), with sequences
+    shorter than S_q; both kernels (the length hint picks one) and a forced
+    split count."""
+    h_kv = 2 if n_rep == 4 else 1
+    inp, qm = make(f"prefill_r{n_rep}_q{S_q}_d{d}", len(lens), S_q, n_rep * h_kv, h_kv, d, lens,
+                   400 + n_rep + S_q + d)
+    ref = oracle.attend_multi(qm, inp.k, inp.v, inp.seq_lens, inp.scale, h_kv, dtype="bf16")
+    for ns, hint in ((0, True), (0, LONG), (3, LONG)):
+        got, used = run(inp, qm, n_splits=ns, hint=hint)
+        err = max_err(got, ref)
+        print(f"[multi] prefill S_q={S_q} n_rep={n_rep} d={d} lens={lens} hint={hint}: n_splits={used} "
+              f"max_abs_err={err:.3e}", flush=True)
+        assert err <= TOL_F32
+        for b, S in enumerate(lens):
+            if S < S_q:
+                assert np.all(got[b, :S_q - S] == 0)     # positions before the cache's start
