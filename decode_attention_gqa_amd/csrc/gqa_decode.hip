@@ -289,7 +289,7 @@ hipError_t launch_merge(bool out_bf16, int B, int h_q, hipStream_t st, const gqa
 
 // Multi-token calls whose sequences need this many query tiles, over at
 // least this many tokens in all (B times the longest length), take the
-// kernel with one tile per wave (split_kv_tiles: 8 tiles read each K/V block
+// tile-per-wave kernel (split_kv_tiles: 8 or 16 tiles read each K/V block
 // once, through LDS); others take two tiles per workgroup (split_kv_mfma),
 // faster at fewer tiles and at shorter KV, where its repeated passes over the
 // KV hit in the caches. Measured at 70B shapes, µs per call, two-tile vs
@@ -322,8 +322,9 @@ constexpr int64_t kTilesMinWork = int64_t(1) << 18;
 
 // Query tokens per 16-column tile, tiles per sequence, tiles per workgroup
 // (two once a sequence needs two or more, each K/V block then read once for
-// both; kTileWaves for the one-tile-per-wave kernel) and workgroup passes per
-// sequence over the KV range. hint: the longest sequence (0: unknown).
+// both; kTileWaves / kTilePairs for the tile-per-wave kernel with one / two
+// tiles per wave) and workgroup passes per sequence over the KV range. hint:
+// the longest sequence (0: unknown).
 void query_tiles(int s_q, int nrep, int B, int64_t hint, int* tpt, int* qtiles, int* tpw, int* passes) {
   *tpt = s_q < 16 / nrep ? s_q : 16 / nrep;
   *qtiles = (s_q + *tpt - 1) / *tpt;
