@@ -139,18 +139,19 @@ def test_tile_waves_70b_shape():
     check("70B S_q=16 bf16-out", inp, qm, out_dtype="bf16")
 
 
+@pytest.mark.parametrize("S_q", [16, 40])
 @pytest.mark.parametrize("hint", [False, LONG])
-def test_multi_offset_layout_with_nan_gaps(hint):
+def test_multi_offset_layout_with_nan_gaps(hint, S_q):
     """Explicit token offsets, sequences stored in reverse order with rows of
     NaN between them: a read outside a sequence's rows would show as NaN in
     the output. Both multi-token kernels (no hint: two tiles; a long hint:
-    one tile per wave)."""
+    one tile per wave at S_q = 16 (8 tiles), two per wave at S_q = 40)."""
     import torch
 
     import decode_attention_gqa_amd as gqa
     lens = np.array([300, 0, 77, 1025, 33], dtype=np.int32)
-    B, S_q, h_kv, n_rep, d = len(lens), 16, 2, 8, 128
-    inp, qm = make("multi_offsets", B, S_q, n_rep * h_kv, h_kv, d, lens, 199)
+    B, h_kv, n_rep, d = len(lens), 2, 8, 128
+    inp, qm = make(f"multi_offsets_q{S_q}", B, S_q, n_rep * h_kv, h_kv, d, lens, 199 + S_q)
     ref = oracle.attend_multi(qm, inp.k, inp.v, inp.seq_lens, inp.scale, h_kv, dtype="bf16")
     _, k, v, dl = to_device(inp)
     packed = np.concatenate([[0], np.cumsum(lens[:-1])]).astype(np.int64)
@@ -173,26 +174,28 @@ def test_multi_offset_layout_with_nan_gaps(hint):
         torch.cuda.synchronize()
         got = out.cpu().numpy().astype(np.float64)
         err = max_err(got, ref)
-        print(f"[multi] offsets hint={hint} ns={ns}: max_abs_err={err:.3e}", flush=True)
+        print(f"[multi] offsets S_q={S_q} hint={hint} ns={ns}: max_abs_err={err:.3e}", flush=True)
         assert np.all(np.isfinite(got)) and err <= TOL_F32
 
 
 @pytest.mark.parametrize("scale", [-0.088, 0.0])
 @pytest.mark.parametrize("hint", [False, LONG])
-def test_multi_negative_and_zero_scale(scale, hint):
-    """Both multi-token kernels with a negative and a zero scale."""
+@pytest.mark.parametrize("S_q", [16, 40])
+def test_multi_negative_and_zero_scale(scale, hint, S_q):
+    """Both multi-token kernels with a negative and a zero scale (a long hint:
+    one tile per wave at S_q = 16, two per wave at S_q = 40)."""
     import torch
 
     import decode_attention_gqa_amd as gqa
     lens = [700, 37, 1500]
-    inp, qm = make("multi_scale", 3, 16, 16, 2, 128, lens, 200)
+    inp, qm = make(f"multi_scale_q{S_q}", 3, S_q, 16, 2, 128, lens, 200 + S_q)
     ref = oracle.attend_multi(qm, inp.k, inp.v, inp.seq_lens, np.float32(scale), 2, dtype="bf16")
     _, k, v, dl = to_device(inp)
     q = torch.from_numpy(np.ascontiguousarray(qm).view(np.int16)).cuda().view(torch.bfloat16)
     out = gqa.gqa_decode_attn_multi(q, k, v, dl, scale=scale, s_kv_hint=int(hint) if hint else 0)
     torch.cuda.synchronize()
     err = max_err(out.cpu().numpy().astype(np.float64), ref)
-    print(f"[multi] scale={scale} hint={hint}: max_abs_err={err:.3e}", flush=True)
+    print(f"[multi] scale={scale} hint={hint} S_q={S_q}: max_abs_err={err:.3e}", flush=True)
     assert err <= TOL_F32
 
 
