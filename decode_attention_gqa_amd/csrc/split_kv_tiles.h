@@ -5,9 +5,11 @@
 // a kv head fill ceil(S_q * n_rep / 16) tiles of 16 MFMA columns. Here each
 // of the workgroup's 8 waves owns one tile, and the workgroup stages every
 // 32-token K/V block of its chunk in LDS once for all 8: each wave computes
-// its tile against the staged block exactly as split_kv_mfma computes one
-// tile (the same operand layouts, softmax and P.V code), reading the
-// operands from LDS instead of HBM. So HBM delivers each K/V byte once per 8
+// its tile against the staged block with split_kv_mfma's score layout and
+// softmax (the lazy reference of softmax_update, as the triplets of a
+// multi-token call stay inside the library), reading the operands from LDS
+// instead of HBM (V^T through the transposing read below; the output tiles
+// are then 16 consecutive dimensions). So HBM delivers each K/V byte once per 8
 // tiles (split_kv_mfma with two tiles per workgroup reads it once per 2, and
 // a long sequence's passes then miss in the caches), and a wave holds one
 // tile's state and no prefetch buffer (128 registers: two workgroups, 16 waves,
@@ -16,11 +18,11 @@
 // sequence has one chunk.
 //
 // TPW = 2: each wave carries two tiles (tiles w and w + 8 of the workgroup's
-// 16), with their own softmax states and accumulators; the block's K and V
-// operands are read from LDS once for both, the V^T permutes are formed once
-// for both, and the two tiles' independent softmax chains give the wave
-// work to interleave with the other's matrix products. Twice the state takes
-// about 200 registers: one workgroup (8 waves) per CU.
+// 16), with their own softmax states and accumulators; the block's K and V^T
+// operands are read from LDS once for both, and the two tiles' independent
+// softmax chains give the wave work to interleave with the other's matrix
+// products. Twice the state takes about 200 registers: one workgroup (8
+// waves) per CU.
 //
 // Staging: two LDS buffers in turn. While the waves compute block i from one
 // buffer, each thread has its pieces of block i + 1 in flight from HBM to
@@ -69,7 +71,7 @@ template <int D, int NREP, int TPW = 1>
 __global__ __launch_bounds__(64 * kTileWaves) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 4 : 2)))
 void split_kv_tiles(SplitArgs a) {
   static_assert(TPW == 1 || TPW == 2, "one or two tiles per wave");
-  constexpr int NT = MfmaTile<D>::NT, KS = MfmaTile<D>::KS, VW = MfmaTile<D>::VW;
+  constexpr int NT = MfmaTile<D>::NT, KS = MfmaTile<D>::KS;
   constexpr int TW = kTileWaves, THREADS = 64 * TW;
   constexpr int TPG = TW * TPW;                     // tiles of a workgroup (one pass)
   using L = LdsBlock<D>;
