@@ -45,6 +45,9 @@ struct SplitArgs {
   int capacity;               // token rows per sequence; rows start at kv_off[b] or b * capacity
   // one chunk per sequence (n_splits = 1): write out = o / l directly, no merge kernel
   int direct;
+  // tile-per-wave kernel: the grid is (h_kv, n_splits, B * passes), kv heads
+  // fastest (split_grid_heads_fastest), instead of split_grid's order
+  int heads_fastest;
 };
 
 struct MergeArgs {

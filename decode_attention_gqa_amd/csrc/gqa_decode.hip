@@ -243,6 +243,10 @@ hipError_t launch_split_append(int nrep, Form form, dim3 grid, hipStream_t st, c
   return hipGetLastError();
 }
 
+// Split counts that merge_wave merges (one workgroup per row, which is what
+// MergeArgs::xcd_rep remaps).
+constexpr int kMergeWaveMinSplits = 9, kMergeWaveMaxSplits = 32;
+
 template <int D, typename TO>
 hipError_t launch_merge_t(int rows, hipStream_t st, const gqa::MergeArgs& a) {
   // Up to 8 chunks per row: several rows per workgroup (32 / SPR of them).
@@ -261,7 +265,7 @@ hipError_t launch_merge_t(int rows, hipStream_t st, const gqa::MergeArgs& a) {
   // Up to 32 chunks: one wave per 32-column slice, D / 32 waves per row
   // (measured faster than the workgroup-per-slice merge up to 32 chunks,
   // slower at 64).
-  if (a.n_splits <= 32) {
+  if (a.n_splits <= kMergeWaveMaxSplits) {
     const dim3 g((unsigned)rows), blk(64 * (D / 32));
     if (a.n_splits <= 16)
       hipLaunchKernelGGL((gqa::merge_wave<D, TO, 2>), g, blk, 0, st, a);
@@ -603,6 +607,17 @@ bool two_tile_eight_waves(const Plan& pl, int64_t units, int h_kv) {
   return tok > 4 * kBlockTokens && tok <= 8 * kBlockTokens && (int64_t)pl.ns * h_kv * units <= cus;
 }
 
+// The tile-per-wave forms launch kv heads fastest when that lets the merge
+// run each kv head's rows on the XCD that wrote them (8 kv heads, a
+// merge_wave split count): workgroup L runs on XCD L mod 8, so kv head g's
+// workgroups then all run on XCD g. 70B B = 1, µs per call, 7 interleaved
+// rounds: 8k S_q = 64 50.7 -> 47.3, 16k S_q = 32 52.4 -> 46.4, 32k S_q = 64
+// 126.7 -> 121.8; other split counts, whose merges are not remapped, stay in
+// split order (8k S_q = 128, 8 splits: 78.6 -> 80.2 in kv-head order).
+bool tiles_heads_fastest(int h_kv, int ns) {
+  return h_kv == 8 && ns >= kMergeWaveMinSplits && ns <= kMergeWaveMaxSplits;
+}
+
 // The matrix-core split kernel's form for a call (four waves for anything
 // else: the vector-ALU kernel, fp32 inputs).
 Form choose_form(const Plan& pl, int B, int h_q, int h_kv, int d_head, int s_q, bool mfma, bool fused) {
@@ -653,6 +668,10 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
     return fail(GQA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
   const Form form = choose_form(pl, B, h_q, h_kv, d_head, s_q, mfma, fused);
   if (form == Form::kEightWave) grid = gqa::split_grid_heads_fastest(pl.ns, h_kv, B * passes);
+  if ((form == Form::kTiles || form == Form::kTilePairs) && tiles_heads_fastest(h_kv, pl.ns)) {
+    grid = gqa::split_grid_heads_fastest(pl.ns, h_kv, B * passes);
+    sa.heads_fastest = 1;
+  }
   e = d_head == 128 ? launch_split_nrep<128>(nrep, bf16, valu, form, grid, stream, sa)
                     : launch_split_nrep<64>(nrep, bf16, valu, form, grid, stream, sa);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
@@ -661,14 +680,15 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
   return GQA_OK;
 }
 
-// eight_wave: the split kernel ran in an 8-wave form (kv heads fastest).
+// heads_fastest: the split kernel's grid ran kv heads fastest (the 8-wave
+// forms, and the tile-per-wave forms where tiles_heads_fastest says so).
 int run_merge(const Plan& pl, const int32_t* seq_lens, void* out, int B, int h_q, int h_kv, int d_head,
-              int out_dtype, hipStream_t stream, bool eight_wave, int s_q = 1, float2* tri_ml = nullptr,
+              int out_dtype, hipStream_t stream, bool heads_fastest, int s_q = 1, float2* tri_ml = nullptr,
               float* tri_o = nullptr) {
   // With 8 kv heads launched heads fastest, kv head g's chunks ran on XCD g;
   // merging its heads there measured faster for several query tokens (8k
   // tokens, 4 query tokens: 14.86 -> 14.02 us per call; one token: no change).
-  const int xcd_rep = eight_wave && h_kv == 8 ? h_q / 8 : 0;
+  const int xcd_rep = heads_fastest && h_kv == 8 ? h_q / 8 : 0;
   gqa::MergeArgs ma{s_q, seq_lens, pl.ws_o, pl.ws_ml, out, h_q, pl.ns, pl.min_chunk,
                     pl.ns, 1, tri_ml, tri_o, xcd_rep};
   const bool obf16 = out_dtype == GQA_DTYPE_BF16;
@@ -862,8 +882,11 @@ int gqa_decode_attn_multi(const void* q, const void* k_cache, const void* v_cach
                       GQA_DTYPE_BF16, stream, 0, out, out_dtype, S_q, &merged)))
     return st;
   if (merged) return GQA_OK;
-  const bool eight = choose_form(pl, B, h_q, h_kv, d_head, S_q, true, false) == Form::kEightWave;
-  return run_merge(pl, seq_lens, out, B, h_q, h_kv, d_head, out_dtype, stream, eight, S_q);
+  // the split kernel's workgroups ran kv heads fastest: merge each head's rows on its XCD
+  const Form fm = choose_form(pl, B, h_q, h_kv, d_head, S_q, true, false);
+  const bool heads_fastest = fm == Form::kEightWave ||
+                             ((fm == Form::kTiles || fm == Form::kTilePairs) && tiles_heads_fastest(h_kv, pl.ns));
+  return run_merge(pl, seq_lens, out, B, h_q, h_kv, d_head, out_dtype, stream, heads_fastest, S_q);
 }
 
 int gqa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

@@ -85,7 +85,7 @@ void split_kv_tiles(SplitArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   __shared__ float sm_m[TW][16], sm_l[TW][16];
 
-  const WgCoord wc = wg_coord();
+  const WgCoord wc = a.heads_fastest ? WgCoord{(int)blockIdx.y, (int)blockIdx.x, (int)blockIdx.z} : wg_coord();
   const int s = wc.s, g = wc.g;
   const int b = wc.b / a.passes, pass = wc.b - b * a.passes;
   const int tid = threadIdx.x, lane = tid & 63;
