@@ -591,7 +591,7 @@ Form split_form(const Plan& pl, int B, int h_kv, int d_head) {
 
 // Two query tiles per workgroup: eight waves (one block each, one register
 // buffer) instead of four when every chunk holds 5 to 8 blocks and the grid
-// is one workgroup per CU or less. Measured on one box, 21 interleaved
+// is one workgroup per CU or less. Measured on one GPU, 21 interleaved
 // rounds each, µs per call p10 / p50 / p90 (eight waves against four): 70B
 // shapes, 8k tokens, 3 query tokens 13.90 / 13.97 / 14.07 against 15.35 /
 // 15.43 / 15.55, 4 tokens 14.23 / 14.28 / 14.40 against 16.24 / 16.28 /
