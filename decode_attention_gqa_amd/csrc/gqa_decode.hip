@@ -307,6 +307,13 @@ constexpr int kTilesMinTiles = 8;
 constexpr int64_t kTilesMinTokens = 16384;
 constexpr int kTilesMinTilesLong = 4;          // fewer tiles take it only over longer KV
 constexpr int64_t kTilesMinTokensLong = 65536;
+// 12 or more tiles from 8192 tokens (after the whole-round split rule): 70B
+// B = 1, 8k tokens, µs per call, tile-per-wave vs two-tile kernel: S_q = 24
+// (12 tiles) 28.4 vs 30.7, S_q = 31 (16) 33.3 vs 36.5, S_q = 48 (24) 43.3 vs
+// 53.6; S_q = 20 (10 tiles) 27.0 vs 27.6 and S_q = 16 (8) 30.2 vs 23.5 stay
+// on two tiles, as do 4k tokens (S_q = 24: 22.6 vs 22.4).
+constexpr int kTilesMinTilesMid = 12;
+constexpr int64_t kTilesMinTokensMid = 8192;
 // Calls that take the tile-per-wave kernel with at least this many tiles per
 // sequence carry two tiles per wave (half the LDS reads per tile, one pass of
 // 16 tiles instead of two of 8). 70B B = 1, µs per call, two tiles per wave
@@ -336,6 +343,7 @@ void query_tiles(int s_q, int nrep, int B, int64_t hint, int* tpt, int* qtiles, 
   const int64_t tokens = hint > 0 ? (int64_t)B * hint : 0;
   if ((*qtiles >= kTilesMinTiles && tokens >= kTilesMinTokens) ||
       (*qtiles >= kTilesMinTilesLong && tokens >= kTilesMinTokensLong) ||
+      (*qtiles >= kTilesMinTilesMid && tokens >= kTilesMinTokensMid) ||
       (*qtiles >= kTilePairsMinTiles && (int64_t)*qtiles * tokens >= kTilesMinWork))
     *tpw = *qtiles >= kTilePairsMinTiles ? gqa::kTilePairs : gqa::kTileWaves;
   *passes = (*qtiles + *tpw - 1) / *tpw;
@@ -346,6 +354,16 @@ int pick_splits_host(int B, int passes, int h_kv, int64_t s_kv_max, int num_cus,
   const int64_t units = (int64_t)B * passes * h_kv;
   const int64_t slots = (int64_t)p.wg_per_cu * num_cus;
   int64_t n = (slots + units - 1) / units;
+  // A grid that overshoots the slots by part of a round pays for that round
+  // in full: one sequence takes the whole rounds that fit when they keep at
+  // least three quarters of the slots busy (multi-token, two tiles per
+  // workgroup, 70B shapes, 8k tokens, µs per call: S_q = 12, 24 units, 10
+  // instead of 11 splits: 31.7 -> 21.8; S_q = 20, 40 units, 6 instead of 7:
+  // 43.3 -> 27.6; S_q = 24, 48 units, 5 instead of 6: 46.5 -> 30.7; S_q =
+  // 40, 80 units, 3 instead of 4: 59.5 -> 42.5; S_q = 48, 96 units, 2
+  // instead of 3: 74.7 -> 53.6).
+  if (B == 1 && n * units > slots && slots / units >= 1 && 4 * (slots / units) * units >= 3 * slots)
+    n = slots / units;
   if (s_kv_max > 0 && B == 1 && p.eight_wave) {
     // ... one sequence that one round of 8-wave workgroups, one per CU,
     // covers in chunks of kEightWaveMinChunk to kEightWaveMaxChunk tokens:

@@ -211,6 +211,11 @@ def test_multi_split_heuristic_values(gqa):
     assert f(1, 64, 8192) == 16                  # 32 tiles x 8192 tokens = 2^18: the same
     assert f(1, 64, 8191) == 2                   # below: two tiles per workgroup, 16 passes
     assert f(1, 128, 4096) == 8                  # 64 tiles x 4096: two per wave, four passes
+    assert f(1, 12, 8192) == 10                  # 6 tiles, two per workgroup, 24 units: 10 (240 workgroups), not 11
+    assert f(1, 20, 8192) == 6                   # 40 units: 6 (240 workgroups), not 7 (280 > 256 slots)
+    assert f(1, 24, 8192) == 32                  # 12 tiles from 8192 tokens: one per wave, two passes
+    assert f(1, 24, 4096) == 5                   # below 8192 tokens: two tiles per workgroup, 48 units
+    assert f(1, 48, 8192) == 16                  # 24 tiles: two per wave, two passes
     assert f(1, 128, 2048) == 1                  # below: 32 passes of two tiles fill the GPU
     assert f(1, 32, 16384) == 32                 # 16 tiles from 16384 tokens: one pass of two per wave
     assert f(1, 1024, 8192) == 1                 # chunked prefill: 32 passes of 16 tiles fill the GPU
