@@ -314,6 +314,14 @@ constexpr int64_t kTilesMinTokensLong = 65536;
 // on two tiles, as do 4k tokens (S_q = 24: 22.6 vs 22.4).
 constexpr int kTilesMinTilesMid = 12;
 constexpr int64_t kTilesMinTokensMid = 8192;
+// 5 to 7 tiles from 32768 tokens (the two-tile kernel's 3 or 4 passes drift
+// apart over long KV): 70B B = 1, 32k tokens, µs per call, tile-per-wave vs
+// two-tile kernel: S_q = 10 46.6 vs 51.3, S_q = 12 50.2 vs 51.8, S_q = 14
+// 52.4 vs 62.5; 4 tiles stay on two tiles up to 65536 tokens (32k S_q = 8:
+// 43.7 vs 38.5; 48k 55.7 vs 52.9), and so do 5 to 7 tiles at 16k (S_q = 12:
+// 35.5 vs 31.6).
+constexpr int kTilesMinTilesFew = 5;
+constexpr int64_t kTilesMinTokensFew = 32768;
 // Calls that take the tile-per-wave kernel with at least this many tiles per
 // sequence carry two tiles per wave (half the LDS reads per tile, one pass of
 // 16 tiles instead of two of 8). 70B B = 1, µs per call, two tiles per wave
@@ -344,6 +352,7 @@ void query_tiles(int s_q, int nrep, int B, int64_t hint, int* tpt, int* qtiles, 
   if ((*qtiles >= kTilesMinTiles && tokens >= kTilesMinTokens) ||
       (*qtiles >= kTilesMinTilesLong && tokens >= kTilesMinTokensLong) ||
       (*qtiles >= kTilesMinTilesMid && tokens >= kTilesMinTokensMid) ||
+      (*qtiles >= kTilesMinTilesFew && tokens >= kTilesMinTokensFew) ||
       (*qtiles >= kTilePairsMinTiles && (int64_t)*qtiles * tokens >= kTilesMinWork))
     *tpw = *qtiles >= kTilePairsMinTiles ? gqa::kTilePairs : gqa::kTileWaves;
   *passes = (*qtiles + *tpw - 1) / *tpw;

@@ -180,8 +180,9 @@ int gqa_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_ca
  * columns single-token decode leaves empty when n_rep < 16). A pass over the
  * KV range serves two tiles (2t tokens read the KV once), or, when a sequence
  * has at least 8 tiles and B * s_kv_hint >= 16384 tokens, at least 4
- * tiles and B * s_kv_hint >= 65536, at least 12 tiles and B * s_kv_hint
- * >= 8192, or at least 16 tiles and tiles * B * s_kv_hint >= 2^18, eight
+ * tiles and B * s_kv_hint >= 65536, at least 5 tiles and B * s_kv_hint >=
+ * 32768, at least 12 tiles and B * s_kv_hint >= 8192, or at least 16 tiles
+ * and tiles * B * s_kv_hint >= 2^18, eight
  * tiles (one per wave, the K/V blocks shared
  * through LDS), sixteen (two per wave) from 16 tiles on; more tokens take
  * more passes. The hint only

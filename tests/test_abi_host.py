@@ -216,6 +216,9 @@ def test_multi_split_heuristic_values(gqa):
     assert f(1, 24, 8192) == 32                  # 12 tiles from 8192 tokens: one per wave, two passes
     assert f(1, 24, 4096) == 5                   # below 8192 tokens: two tiles per workgroup, 48 units
     assert f(1, 48, 8192) == 16                  # 24 tiles: two per wave, two passes
+    assert f(1, 10, 32768) == 64                 # 5 tiles from 32768 tokens: one per wave, one pass
+    assert f(1, 10, 16384) == 10                 # below: two tiles per workgroup, 24 units
+    assert f(1, 8, 32768) == 16                  # 4 tiles stay on two tiles below 65536 tokens
     assert f(1, 128, 2048) == 1                  # below: 32 passes of two tiles fill the GPU
     assert f(1, 32, 16384) == 32                 # 16 tiles from 16384 tokens: one pass of two per wave
     assert f(1, 1024, 8192) == 1                 # chunked prefill: 32 passes of 16 tiles fill the GPU
