@@ -451,7 +451,7 @@ def main() -> int:
         qm = workloads.normals(w.seed, 9, w.B * args.s_q * w.h_q * w.d, 1.0, w.dtype).reshape(
             w.B, args.s_q, w.h_q, w.d)
         qms = [up(qm)] + [up(qm) for _ in range(R - 1)]
-        ns = gqa.multi_splits(w.B, args.s_q, w.h_q, w.h_kv, s_max, args.n_splits)
+        ns = gqa.multi_splits(w.B, args.s_q, w.h_q, w.h_kv, s_max, args.n_splits, w.d)
         ws = torch.empty(gqa.gqa_decode_workspace_bytes(w.B * args.s_q, w.h_q, w.d, ns),
                          dtype=torch.uint8, device=dev)
         out = torch.empty((w.B, args.s_q, w.h_q, w.d), dtype=torch.float32, device=dev)

@@ -88,6 +88,8 @@ lib.gqa_decode_pick_splits_d.argtypes = [_i32, _i32, _i32, _i64, _i32]
 lib.gqa_decode_pick_splits_d.restype = _i32
 lib.gqa_decode_multi_splits.argtypes = [_i32, _i32, _i32, _i32, _i64, _i32]
 lib.gqa_decode_multi_splits.restype = _i32
+lib.gqa_decode_multi_splits_d.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _i32]
+lib.gqa_decode_multi_splits_d.restype = _i32
 lib.gqa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
 lib.gqa_decode_workspace_bytes.restype = _sz
 lib.gqa_status_string.argtypes = [_i32]
@@ -246,13 +248,14 @@ def _check_inputs(q, k_cache, v_cache, seq_lens, kv_token_offsets):
         raise ValueError("kv_token_offsets must be an int64 [B] GPU tensor")
 
 
-def multi_splits(B: int, S_q: int, h_q: int, h_kv: int, s_kv_hint: int = 0, n_splits: int = 0) -> int:
+def multi_splits(B: int, S_q: int, h_q: int, h_kv: int, s_kv_hint: int = 0, n_splits: int = 0,
+                 d_head: int = 128) -> int:
     """Split count gqa_decode_attn_multi uses (for sizing its workspace)."""
     if n_splits > 0:
         return n_splits
-    r = lib.gqa_decode_multi_splits(B, S_q, h_q, h_kv, int(s_kv_hint), 0)
+    r = lib.gqa_decode_multi_splits_d(B, S_q, h_q, h_kv, d_head, int(s_kv_hint), 0)
     if r < 1:
-        raise GQAError(r, "gqa_decode_multi_splits")
+        raise GQAError(r, "gqa_decode_multi_splits_d")
     return r
 
 
@@ -282,7 +285,7 @@ def gqa_decode_attn_multi(q, k_cache, v_cache, seq_lens, out=None, *, scale=None
         raise ValueError("out must be a contiguous [B, S_q, h_q, d_head] tensor of out_dtype")
     with torch.cuda.device(q.device):
         if workspace is None:
-            ns = multi_splits(B, S_q, h_q, h_kv, int(s_kv_hint), n_splits)
+            ns = multi_splits(B, S_q, h_q, h_kv, int(s_kv_hint), n_splits, d)
             workspace = torch.empty(gqa_decode_workspace_bytes(B * S_q, h_q, d, ns), dtype=torch.uint8,
                                     device=q.device)
         st = stream if stream is not None else torch.cuda.current_stream(q.device)

@@ -62,6 +62,11 @@ constexpr SplitPolicy kOneTile{2, 2, 4, 4096, true, true};
 constexpr SplitPolicy kOneTile64{2, 2, 4, 4096, false, true};
 // One tile of several query tokens (multi-token calls).
 constexpr SplitPolicy kOneTileMulti{2, 2, 4, 4096, false, false};
+// The same with 128-dimension heads: a single sequence may take the 8-wave
+// round like a single-token call (one tile of several query tokens, e.g. two
+// at 70B shapes: 8k 13.8 -> 12.5 µs per call, 16k 19.5 -> 17.7, 32k 31.8 ->
+// 27.8).
+constexpr SplitPolicy kOneTileMulti8{2, 2, 4, 4096, true, false};
 // Two tiles per workgroup (multi-token decode), one workgroup per CU: one
 // round for a single sequence; chunks up to 16384 tokens.
 constexpr SplitPolicy kTwoTiles{1, 1, 4, 16384, false, false};
@@ -72,8 +77,9 @@ constexpr SplitPolicy kTileWavesPolicy{2, 1, 2, 16384, false, false};
 // Two tiles per wave, sixteen per workgroup, one workgroup per CU.
 constexpr SplitPolicy kTilePairsPolicy{1, 1, 2, 16384, false, false};
 
-// single_token: a single-token entry point. The multi-token one never takes
-// the 8-wave count (so gqa_decode_multi_splits needs no d_head), and takes the
+// single_token: a single-token entry point. The multi-token one takes the
+// 8-wave count for one tile of several query tokens with 128-dimension heads
+// (so its split count depends on d_head: gqa_decode_multi_splits_d), and the
 // short-sequence count only for one query token, where it then plans like a
 // single-token call outside the 8-wave range.
 const SplitPolicy& split_policy(int tiles_per_wg, int d_head, bool single_token, int s_q) {
@@ -81,6 +87,7 @@ const SplitPolicy& split_policy(int tiles_per_wg, int d_head, bool single_token,
   if (tiles_per_wg == gqa::kTilePairs) return kTilePairsPolicy;
   if (tiles_per_wg == 2) return kTwoTiles;
   if (single_token && d_head == 128) return kOneTile;
+  if (!single_token && s_q > 1 && d_head == 128) return kOneTileMulti8;
   return single_token || s_q == 1 ? kOneTile64 : kOneTileMulti;
 }
 // A single sequence with 128-dimension heads whose chunks, at one 8-wave
@@ -475,8 +482,9 @@ int gqa_decode_pick_splits(int B, int h_kv, int64_t s_kv_max, int num_cus) {
   return gqa_decode_pick_splits_d(B, h_kv, 128, s_kv_max, num_cus);
 }
 
-int gqa_decode_multi_splits(int B, int S_q, int h_q, int h_kv, int64_t s_kv_max, int num_cus) {
+int gqa_decode_multi_splits_d(int B, int S_q, int h_q, int h_kv, int d_head, int64_t s_kv_max, int num_cus) {
   if (B < 1 || h_kv < 1 || h_q < h_kv || h_q % h_kv) return fail(GQA_ERR_INVALID_ARG, "bad B / h_q / h_kv");
+  if (d_head != 64 && d_head != 128) return fail(GQA_ERR_UNSUPPORTED, "d_head %d not 64 or 128", d_head);
   if (S_q < 1 || S_q > GQA_MAX_QUERY_TOKENS)
     return fail(GQA_ERR_INVALID_ARG, "S_q %d not in [1, %d]", S_q, GQA_MAX_QUERY_TOKENS);
   if (num_cus <= 0) {
@@ -485,7 +493,11 @@ int gqa_decode_multi_splits(int B, int S_q, int h_q, int h_kv, int64_t s_kv_max,
   }
   int tpt, qtiles, tpw, passes;
   query_tiles(S_q, h_q / h_kv, B, s_kv_max, &tpt, &qtiles, &tpw, &passes);
-  return pick_splits_host(B, passes, h_kv, s_kv_max, num_cus, split_policy(tpw, 128, false, S_q));
+  return pick_splits_host(B, passes, h_kv, s_kv_max, num_cus, split_policy(tpw, d_head, false, S_q));
+}
+
+int gqa_decode_multi_splits(int B, int S_q, int h_q, int h_kv, int64_t s_kv_max, int num_cus) {
+  return gqa_decode_multi_splits_d(B, S_q, h_q, h_kv, 128, s_kv_max, num_cus);
 }
 
 }  // extern "C"
@@ -655,6 +667,8 @@ Form choose_form(const Plan& pl, int B, int h_q, int h_kv, int d_head, int s_q, 
     const Form f = split_form(pl, B, h_kv, d_head);
     return fused && f == Form::kOneWave ? Form::kFourWave : f;
   }
+  // one tile of several query tokens: the single-token 8-wave round when it applies
+  if (tpw == 1 && !fused && split_form(pl, B, h_kv, d_head) == Form::kEightWave) return Form::kEightWave;
   if (tpw == gqa::kTileWaves) return Form::kTiles;
   if (tpw == gqa::kTilePairs) return Form::kTilePairs;
   if (tpw == 2 && !fused && two_tile_eight_waves(pl, B * passes, h_kv)) return Form::kEightWave;

@@ -188,8 +188,8 @@ int gqa_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_ca
  * more passes. The hint only
  * picks the kernel and the split count: either kernel takes any length, and
  * the two round differently. Workspace: gqa_decode_workspace_bytes(B * S_q,
- * h_q, d_head, n) with n = n_splits if > 0, else gqa_decode_multi_splits(B,
- * S_q, h_q, h_kv, s_kv_hint, 0). B * passes <= 65535. Other
+ * h_q, d_head, n) with n = n_splits if > 0, else gqa_decode_multi_splits_d(B,
+ * S_q, h_q, h_kv, d_head, s_kv_hint, 0). B * passes <= 65535. Other
  * arguments as in gqa_decode_attn_ex.
  */
 int gqa_decode_attn_multi(const void* q, const void* k_cache, const void* v_cache,
@@ -335,9 +335,15 @@ int gqa_decode_pick_splits(int B, int h_kv, int64_t s_kv_max, int num_cus);
  * for its kernels: with two column tiles per workgroup, one workgroup per CU,
  * one round of them for a single sequence; with eight (one per wave), two
  * workgroups per CU, one round for a single sequence and up to two for a
- * batch; chunks of up to 16384 tokens). s_kv_max is also the hint that picks
- * the kernel (see gqa_decode_attn_multi). Negative status on invalid
- * arguments or a failed device query. */
+ * batch; with sixteen (two per wave), one per CU; one tile of several query
+ * tokens with d_head = 128 as gqa_decode_pick_splits_d, the 8-wave round
+ * included; chunks of up to 16384 tokens). s_kv_max is also the hint that
+ * picks the kernel (see gqa_decode_attn_multi). Negative status on invalid
+ * arguments or a failed device query; GQA_ERR_UNSUPPORTED for a d_head other
+ * than 64 or 128. */
+int gqa_decode_multi_splits_d(int B, int S_q, int h_q, int h_kv, int d_head, int64_t s_kv_max, int num_cus);
+
+/* gqa_decode_multi_splits_d for d_head = 128. */
 int gqa_decode_multi_splits(int B, int S_q, int h_q, int h_kv, int64_t s_kv_max, int num_cus);
 
 /* Workspace bytes for n_splits chunks. Layout, each part starting on a

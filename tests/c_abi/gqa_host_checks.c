@@ -98,6 +98,9 @@ int main(void) {
   expect("multi S_q 4", gqa_decode_multi_splits(1, 4, 64, 8, 8192, 256), 32);
   expect("multi S_q 16, 16k (one tile per wave)", gqa_decode_multi_splits(1, 16, 64, 8, 16384, 256), 64);
   expect("multi bad h_kv", gqa_decode_multi_splits(1, 4, 64, 0, 8192, 256), GQA_ERR_INVALID_ARG);
+  expect("multi S_q 2, d 128 (8-wave round)", gqa_decode_multi_splits_d(1, 2, 64, 8, 128, 8192, 256), 32);
+  expect("multi S_q 2, d 64", gqa_decode_multi_splits_d(1, 2, 64, 8, 64, 8192, 256), 64);
+  expect("multi bad d_head", gqa_decode_multi_splits_d(1, 2, 64, 8, 96, 8192, 256), GQA_ERR_UNSUPPORTED);
   expect("workspace bytes", (long)gqa_decode_workspace_bytes(8, 64, 128, 37),
          (long)(512 * 8 + ((8L * 64 * 37 * 128 * 4 + 255) / 256) * 256 + ((8L * 64 * 37 * 8 + 255) / 256) * 256 +
                 256));

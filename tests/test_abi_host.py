@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
                             "gqa_decode_attn_multi", "gqa_decode_partial",
                             "gqa_decode_merge", "gqa_kv_append", "gqa_decode_step", "gqa_decode_attn_triplet",
                             "gqa_merge_triplets", "gqa_decode_pick_splits", "gqa_decode_pick_splits_d",
-                            "gqa_decode_multi_splits",
+                            "gqa_decode_multi_splits", "gqa_decode_multi_splits_d",
                             "gqa_decode_workspace_bytes", "gqa_status_string", "gqa_last_error",
                             "gqa_decode_set_split_events"])
 
@@ -190,10 +190,16 @@ def test_split_heuristic_values(gqa):
 
 def test_multi_split_heuristic_values(gqa):
     f = lambda B, S_q, S, h_q=64, h_kv=8: gqa.lib.gqa_decode_multi_splits(B, S_q, h_q, h_kv, S, 256)
-    # one or several query tokens in a single 16-column tile: the
-    # single-token rule without the 8-wave count
+    # one query token: the single-token rule without the 8-wave count; several
+    # in a single 16-column tile with 128-dimension heads: with it (d = 64:
+    # without it)
+    fd = lambda B, S_q, S, d: gqa.lib.gqa_decode_multi_splits_d(B, S_q, 64, 8, d, S, 256)
     assert f(1, 1, 8192) == gqa.gqa_decode_pick_splits_d(1, 8, 64, 8192, 256) == 64
-    assert f(1, 2, 8192) == 64
+    assert f(1, 2, 8192) == fd(1, 2, 8192, 128) == gqa.gqa_decode_pick_splits_d(1, 8, 128, 8192, 256) == 32
+    assert f(1, 2, 32768) == 32                  # the 8-wave round up to 1024 tokens per chunk
+    assert f(1, 2, 65536) == 128
+    assert fd(1, 2, 8192, 64) == 64
+    assert fd(1, 2, 8192, 96) == -2              # GQA_ERR_UNSUPPORTED
     # two tiles per workgroup, one workgroup per CU: one round for one sequence
     assert f(1, 4, 8192) == 32
     assert f(1, 8, 8192) == 16                   # two passes of two tiles

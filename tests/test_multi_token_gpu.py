@@ -28,7 +28,7 @@ def run(inp, qm, n_splits=0, out_dtype="f32", poison=True, hint=True):
         s_max = int(inp.seq_lens.max())
     else:
         s_max = int(hint) if hint else 0               # False / 0: no hint; an int: that hint
-    ns = gqa.multi_splits(B, S_q, w.h_q, w.h_kv, s_max, n_splits)
+    ns = gqa.multi_splits(B, S_q, w.h_q, w.h_kv, s_max, n_splits, w.d)
     ws = torch.empty(gqa.gqa_decode_workspace_bytes(B * S_q, w.h_q, w.d, ns), dtype=torch.uint8, device="cuda")
     if poison:
         ws.view(torch.float32).fill_(float("nan"))
@@ -213,6 +213,20 @@ def test_two_tiles_eight_waves(n_rep, S_q, d):
                          n_splits=ns, hint=True)
         four, _ = run(inp, qm, n_splits=ns, hint=False)
         assert max_err(got, four) <= 1e-3
+
+
+@pytest.mark.parametrize("n_rep,S_q,S", [(8, 2, 8192), (8, 2, 20000), (4, 4, 9000), (16, 1, 8192), (8, 2, 40000)])
+def test_one_tile_eight_waves(n_rep, S_q, S):
+    """One tile of several query tokens (S_q <= 16 / n_rep) over a single
+    sequence with 128-dimension heads takes the single-token 8-wave round
+    when its chunks hold 256 to 1024 tokens (8k to 32k at 8 kv heads; 40000:
+    past it, four waves); S_q = 1 through this entry point keeps its own
+    plan. Against the oracle, and against a forced split count."""
+    h_kv = 8
+    inp, qm = make(f"t1w8_r{n_rep}_q{S_q}_s{S}", 1, S_q, n_rep * h_kv, h_kv, 128, [S], 250 + n_rep + S_q + S % 97)
+    got, ref = check(f"one tile, 8 waves n_rep={n_rep} S_q={S_q} S={S}", inp, qm, hint=True)
+    forced, _ = run(inp, qm, n_splits=7, hint=True)
+    assert max_err(forced, ref) <= TOL_F32
 
 
 def test_two_tiles_eight_waves_with_a_hint_below_the_lengths():
