@@ -356,6 +356,15 @@ void query_tiles(int s_q, int nrep, int B, int64_t hint, int* tpt, int* qtiles, 
   *qtiles = (s_q + *tpt - 1) / *tpt;
   *tpw = *qtiles >= 2 ? 2 : 1;
   const int64_t tokens = hint > 0 ? (int64_t)B * hint : 0;
+  // Two tiles over short KV: one per pass (twice the workgroups, each
+  // reading the KV; the second read hits the caches). 70B shapes, S_q = 4,
+  // µs per call, one vs two tiles per workgroup: B = 1, 1k 8.3 vs 10.2, 2k
+  // 9.2 vs 10.7, 4k 10.7 vs 12.8, 6k 11.6 vs 13.1, 8k 14.1 vs 14.3; B = 4 x
+  // 2k 19.7 vs 21.4; but B = 2 x 4k 15.8 vs 15.0, and 16k or 32k tokens
+  // (20.6 vs 20.6, 52.5 vs 31.6) and the ragged B = 8 batch (144.0 vs 92.0)
+  // read the KV twice from HBM. Grouped heads only (measured at 8 query
+  // heads per KV head; many KV heads already fill the chip).
+  if (*qtiles == 2 && nrep >= 4 && hint > 0 && ((B == 1 && hint <= 8192) || (hint <= 2048 && tokens <= 8192))) *tpw = 1;
   if ((*qtiles >= kTilesMinTiles && tokens >= kTilesMinTokens) ||
       (*qtiles >= kTilesMinTilesLong && tokens >= kTilesMinTokensLong) ||
       (*qtiles >= kTilesMinTilesMid && tokens >= kTilesMinTokensMid) ||

@@ -185,7 +185,9 @@ int gqa_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_ca
  * and tiles * B * s_kv_hint >= 2^18, eight
  * tiles (one per wave, the K/V blocks shared
  * through LDS), sixteen (two per wave) from 16 tiles on; more tokens take
- * more passes. The hint only
+ * more passes. Exactly two tiles with n_rep >= 4 over short KV (B == 1 and
+ * s_kv_hint <= 8192, or s_kv_hint <= 2048 and B * s_kv_hint <= 8192) take
+ * one tile per pass. The hint only
  * picks the kernel and the split count: either kernel takes any length, and
  * the two round differently. Workspace: gqa_decode_workspace_bytes(B * S_q,
  * h_q, d_head, n) with n = n_splits if > 0, else gqa_decode_multi_splits_d(B,

@@ -201,7 +201,8 @@ def test_multi_split_heuristic_values(gqa):
     assert fd(1, 2, 8192, 64) == 64
     assert fd(1, 2, 8192, 96) == -2              # GQA_ERR_UNSUPPORTED
     # two tiles per workgroup, one workgroup per CU: one round for one sequence
-    assert f(1, 4, 8192) == 32
+    assert f(1, 4, 8192) == 16                   # two tiles, one per pass, 8-wave round
+    assert f(1, 4, 16384) == 32                  # longer: both tiles in one pass
     assert f(1, 8, 8192) == 16                   # two passes of two tiles
     assert f(1, 4, 1 << 20) == 64                # chunks of up to 16384 tokens
     assert f(8, 4, 32768) == 16                  # a batch: the longest over four rounds
