@@ -95,7 +95,8 @@ int main(void) {
   expect("pick d96", gqa_decode_pick_splits_d(1, 8, 96, 8192, 256), GQA_ERR_UNSUPPORTED);
   expect("pick ragged", gqa_decode_pick_splits(8, 8, 32768, 256), 32);
   expect("pick huge", gqa_decode_pick_splits(1, 1, (int64_t)1 << 40, 256), GQA_MAX_SPLITS);
-  expect("multi S_q 4", gqa_decode_multi_splits(1, 4, 64, 8, 8192, 256), 32);
+  expect("multi S_q 4 (two tiles, one per pass)", gqa_decode_multi_splits(1, 4, 64, 8, 8192, 256), 16);
+  expect("multi S_q 4, 16k (two tiles per pass)", gqa_decode_multi_splits(1, 4, 64, 8, 16384, 256), 32);
   expect("multi S_q 16, 16k (one tile per wave)", gqa_decode_multi_splits(1, 16, 64, 8, 16384, 256), 64);
   expect("multi bad h_kv", gqa_decode_multi_splits(1, 4, 64, 0, 8192, 256), GQA_ERR_INVALID_ARG);
   expect("multi S_q 2, d 128 (8-wave round)", gqa_decode_multi_splits_d(1, 2, 64, 8, 128, 8192, 256), 32);
