@@ -645,7 +645,9 @@ Form split_form(const Plan& pl, int B, int h_kv, int d_head) {
 // 15.43 / 15.55, 4 tokens 14.23 / 14.28 / 14.40 against 16.24 / 16.28 /
 // 16.40; 6k tokens, 4 tokens 12.85 / 12.92 / 13.01 against 14.31 / 14.34 /
 // 14.42; 64-dimension heads, 8k tokens, 4 tokens 10.32 / 10.38 / 10.50
-// against 10.95 / 10.98 / 11.13.
+// against 10.95 / 10.98 / 11.13. (A single sequence of up to 8k tokens with
+// exactly two tiles now takes one tile per pass instead, see query_tiles; this
+// form still serves two-tile calls such as B = 2 x 4k tokens.)
 bool two_tile_eight_waves(const Plan& pl, int64_t units, int h_kv) {
   if (pl.hint <= 0) return false;
   const int64_t per_chunk = (pl.hint + pl.ns - 1) / pl.ns;
