@@ -252,6 +252,14 @@ hipError_t launch_split_append(int nrep, Form form, dim3 grid, hipStream_t st, c
 
 // Split counts that merge_wave merges (one workgroup per row, which is what
 // MergeArgs::xcd_rep remaps).
+// Rows from which merge_wave takes two 32-column slices per wave (half the
+// waves: a multi-token call's 4096 rows then fit the wave slots in one
+// round). 70B B = 1, µs per call p50, two interleaved A/B runs of 9 rounds,
+// one slice vs two (the same bits): 8k S_q = 64 44.7 / 44.7 vs 43.4 / 44.0,
+// S_q = 32 31.4 / 31.0 vs 31.0 / 30.5; 32k S_q = 16 52.6 / 52.5 vs 52.1 /
+// 51.3, S_q = 64 119.5 / 118.0 vs 117.1 / 117.5. One wave per row (four
+// slices) measured the same as two.
+constexpr int64_t kMergeWideRows = 1024;
 constexpr int kMergeWaveMinSplits = 9, kMergeWaveMaxSplits = 32;
 
 template <int D, typename TO>
@@ -273,7 +281,16 @@ hipError_t launch_merge_t(int rows, hipStream_t st, const gqa::MergeArgs& a) {
   // (measured faster than the workgroup-per-slice merge up to 32 chunks,
   // slower at 64).
   if (a.n_splits <= kMergeWaveMaxSplits) {
-    const dim3 g((unsigned)rows), blk(64 * (D / 32));
+    const dim3 g((unsigned)rows);
+    if (rows >= kMergeWideRows) {
+      const dim3 blk(64 * (D / 64));
+      if (a.n_splits <= 16)
+        hipLaunchKernelGGL((gqa::merge_wave<D, TO, 2, 2>), g, blk, 0, st, a);
+      else
+        hipLaunchKernelGGL((gqa::merge_wave<D, TO, 4, 2>), g, blk, 0, st, a);
+      return hipGetLastError();
+    }
+    const dim3 blk(64 * (D / 32));
     if (a.n_splits <= 16)
       hipLaunchKernelGGL((gqa::merge_wave<D, TO, 2>), g, blk, 0, st, a);
     else

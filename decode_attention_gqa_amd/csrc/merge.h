@@ -143,32 +143,37 @@ __global__ __launch_bounds__(256) void merge_splits(MergeArgs a) {
   }
 }
 
-// The same merge for 9 to 32 chunks per row, one wave per 32-column slice
-// of a row: slot j of the wave (8 lanes, a float4 each) holds chunks j,
-// j + 8, ..., U of them, all loaded at once; the max and the sums over the
-// 8 slots are lane butterflies (xor 8, 16, 32), so no LDS step and no
-// barrier. Grid: one workgroup of D / 32 waves per row.
-template <int D, typename TO, int U>
-__global__ __launch_bounds__(64 * (D / 32)) void merge_wave(MergeArgs a) {
+// The same merge for 9 to 32 chunks per row, one wave per SL 32-column
+// slices of a row: slot j of the wave (8 lanes, SL float4s each, 32 columns
+// apart) holds chunks j, j + 8, ..., U of them, all loaded at once; the max
+// and the sums over the 8 slots are lane butterflies (xor 8, 16, 32), so no
+// LDS step and no barrier. Grid: one workgroup of D / (32 * SL) waves per
+// row. SL = 2 halves the waves of a call with many rows (multi-token calls),
+// so that they fit the GPU's wave slots at once and the merge pays one
+// memory latency instead of two.
+template <int D, typename TO, int U, int SL = 1>
+__global__ __launch_bounds__(64 * (D / (32 * SL))) void merge_wave(MergeArgs a) {
   constexpr int LPS = 8, SLOTS = 64 / LPS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slot = lane / LPS, q = lane % LPS;
   const int wg = blockIdx.x, R = a.xcd_rep;
   const int bh = R > 0 ? wg - wg % (8 * R) + (wg % 8) * R + (wg / 8) % R : wg;   // see MergeArgs::xcd_rep
   const int b = bh / (a.h_q * a.s_q);
-  const int d0 = wave * 4 * LPS;
+  const int d0 = wave * 4 * LPS * SL;
   const int64_t ps = a.part_stride;
   const float2* ml = a.ws_ml + (int64_t)bh * a.row_stride;
   const float* o = a.ws_o + (int64_t)bh * a.row_stride * D + d0 + 4 * q;
   // Clamped indices: every load is in bounds and issued before the wait for
   // seq_lens; chunks at or past n_active are selected out before any use.
   float2 mv[U];
-  float4 ov[U];
+  float4 ov[U][SL];
 #pragma unroll
   for (int u = 0; u < U; ++u) mv[u] = ml[min(u * SLOTS + slot, a.n_splits - 1) * ps];
 #pragma unroll
   for (int u = 0; u < U; ++u)
-    ov[u] = *reinterpret_cast<const float4*>(o + min(u * SLOTS + slot, a.n_splits - 1) * ps * D);
+#pragma unroll
+    for (int sl = 0; sl < SL; ++sl)
+      ov[u][sl] = *reinterpret_cast<const float4*>(o + min(u * SLOTS + slot, a.n_splits - 1) * ps * D + 32 * sl);
   __builtin_amdgcn_sched_barrier(0);
   int c, n_active = a.n_splits;
   if (a.seq_lens) chunking(a.seq_lens[b], a.n_splits, a.min_chunk, c, n_active);
@@ -177,32 +182,44 @@ __global__ __launch_bounds__(64 * (D / 32)) void merge_wave(MergeArgs a) {
   for (int u = 0; u < U; ++u)
     if (u * SLOTS + slot < n_active) M = fmaxf(M, mv[u].x);
   M = max_x32(max_x16(max_x8(M)));
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 acc[SL];
+#pragma unroll
+  for (int sl = 0; sl < SL; ++sl) acc[sl] = make_float4(0.f, 0.f, 0.f, 0.f);
   float L = 0.f;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (u * SLOTS + slot < n_active) {
       const float w = rescale(mv[u].x, M);   // a causal column can have empty chunks (m = -inf)
-      acc.x += w * ov[u].x;
-      acc.y += w * ov[u].y;
-      acc.z += w * ov[u].z;
-      acc.w += w * ov[u].w;
+#pragma unroll
+      for (int sl = 0; sl < SL; ++sl) {
+        acc[sl].x += w * ov[u][sl].x;
+        acc[sl].y += w * ov[u][sl].y;
+        acc[sl].z += w * ov[u][sl].z;
+        acc[sl].w += w * ov[u][sl].w;
+      }
       L += w * mv[u].y;
     }
   }
-  acc.x = sum_x32(sum_x16(sum_x8(acc.x)));
-  acc.y = sum_x32(sum_x16(sum_x8(acc.y)));
-  acc.z = sum_x32(sum_x16(sum_x8(acc.z)));
-  acc.w = sum_x32(sum_x16(sum_x8(acc.w)));
+#pragma unroll
+  for (int sl = 0; sl < SL; ++sl) {
+    acc[sl].x = sum_x32(sum_x16(sum_x8(acc[sl].x)));
+    acc[sl].y = sum_x32(sum_x16(sum_x8(acc[sl].y)));
+    acc[sl].z = sum_x32(sum_x16(sum_x8(acc[sl].z)));
+    acc[sl].w = sum_x32(sum_x16(sum_x8(acc[sl].w)));
+  }
   L = sum_x32(sum_x16(sum_x8(L)));
   if (slot != 0) return;
   if (a.tri_ml) {                            // merged triplet, relative to M
     if (q == 0 && wave == 0) a.tri_ml[bh] = make_float2(M, L);
-    *reinterpret_cast<float4*>(a.tri_o + (int64_t)bh * D + d0 + 4 * q) = acc;
+#pragma unroll
+    for (int sl = 0; sl < SL; ++sl)
+      *reinterpret_cast<float4*>(a.tri_o + (int64_t)bh * D + d0 + 32 * sl + 4 * q) = acc[sl];
   } else {
     const float inv = L > 0.f ? 1.f / L : 0.f;   // L = 0 only when nothing was attended
-    store4<TO>(static_cast<TO*>(a.out) + (int64_t)bh * D + d0 + 4 * q,
-               make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv));
+#pragma unroll
+    for (int sl = 0; sl < SL; ++sl)
+      store4<TO>(static_cast<TO*>(a.out) + (int64_t)bh * D + d0 + 32 * sl + 4 * q,
+                 make_float4(acc[sl].x * inv, acc[sl].y * inv, acc[sl].z * inv, acc[sl].w * inv));
   }
 }
 
