@@ -258,7 +258,9 @@ hipError_t launch_split_append(int nrep, Form form, dim3 grid, hipStream_t st, c
 // one slice vs two (the same bits): 8k S_q = 64 44.7 / 44.7 vs 43.4 / 44.0,
 // S_q = 32 31.4 / 31.0 vs 31.0 / 30.5; 32k S_q = 16 52.6 / 52.5 vs 52.1 /
 // 51.3, S_q = 64 119.5 / 118.0 vs 117.1 / 117.5. One wave per row (four
-// slices) measured the same as two.
+// slices) measured the same as two. Calls with few rows keep one slice per
+// wave (more waves, each with less to load): one query token, 64 rows, 8k
+// 11.84 vs 11.99 (two slices) and 12.19 (four), 16k 16.77 vs 17.06 / 16.98.
 constexpr int64_t kMergeWideRows = 1024;
 constexpr int kMergeWaveMinSplits = 9, kMergeWaveMaxSplits = 32;
 
