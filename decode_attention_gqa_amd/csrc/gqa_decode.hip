@@ -269,6 +269,18 @@ hipError_t launch_merge_t(int rows, hipStream_t st, const gqa::MergeArgs& a) {
   // Up to 8 chunks per row: several rows per workgroup (32 / SPR of them).
   auto packed = [&](auto spr) {
     constexpr int SPR = decltype(spr)::value;
+    if (rows >= kMergeWideRows) {
+      // A lane holds its chunk's whole row (D / 32 float4s), a quarter of
+      // the workgroups. 70B B = 1, µs per call p50, 9 interleaved rounds, one
+      // / two / four float4s per lane (the same bits): 8k S_q = 128 72.8 /
+      // 71.4 / 70.6; 4k S_q = 256 73.1 / 71.9 / 71.6; 2.5k S_q = 512 84.3 /
+      // 83.7 / 84.0; 1k S_q = 1024 62.6 / 62.6 / 62.5; one query token, B =
+      // 32 x 4k and 64 x 2k 95.1 / 95.0 / 94.9 and 98.0 / 97.3 / 97.3.
+      constexpr int SL = D / 32;
+      const dim3 g((unsigned)((rows + 32 / SPR - 1) / (32 / SPR)), D / (32 * SL));
+      hipLaunchKernelGGL((gqa::merge_rows<D, TO, SPR, SL>), g, dim3(256), 0, st, a, rows);
+      return;
+    }
     const dim3 g((unsigned)((rows + 32 / SPR - 1) / (32 / SPR)), D / 32);
     hipLaunchKernelGGL((gqa::merge_rows<D, TO, SPR>), g, dim3(256), 0, st, a, rows);
   };

@@ -226,14 +226,15 @@ __global__ __launch_bounds__(64 * (D / (32 * SL))) void merge_wave(MergeArgs a) 
 // The same merge for many rows with few chunks each (n_splits <= 8): the 32
 // chunk slots of a workgroup form groups of SPR consecutive slots, one row
 // per group (32 / SPR rows per workgroup), so each row's reductions run over
-// lane bits 3.. of one wave and need no LDS step. Grid (row groups, 32-column
-// slices of d). Rows past `rows` load clamped, in-bounds data and store
-// nothing; chunks at or past a row's n_active are selected out before any
-// arithmetic touches their (possibly never written) workspace values.
-template <int D, typename TO, int SPR>
+// lane bits 3.. of one wave and need no LDS step. Each lane holds SL float4s,
+// 32 columns apart. Grid (row groups, (32 * SL)-column slices of d). Rows
+// past `rows` load clamped, in-bounds data and store nothing; chunks at or
+// past a row's n_active are selected out before any arithmetic touches their
+// (possibly never written) workspace values.
+template <int D, typename TO, int SPR, int SL = 1>
 __global__ __launch_bounds__(256) void merge_rows(MergeArgs a, int rows) {
   static_assert(SPR == 1 || SPR == 2 || SPR == 4 || SPR == 8, "a row's slots lie within one wave");
-  constexpr int LPS = 8;                     // lanes per chunk: a float4 each of a 32-column slice
+  constexpr int LPS = 8;                     // lanes per chunk: SL float4s each of a slice
   constexpr int RPW = 32 / SPR;              // rows per workgroup
   const int tid = threadIdx.x;
   const int slot = tid / LPS, q = tid % LPS;
@@ -241,10 +242,12 @@ __global__ __launch_bounds__(256) void merge_rows(MergeArgs a, int rows) {
   const int r = blockIdx.x * RPW + slot / SPR;
   const bool live = r < rows;
   const int64_t rr = live ? r : rows - 1;
-  const int d0 = blockIdx.y * 4 * LPS;
+  const int d0 = blockIdx.y * 4 * LPS * SL;
   const int64_t at = rr * a.row_stride + (int64_t)min(c, a.n_splits - 1) * a.part_stride;
   const float2 mv = a.ws_ml[at];
-  const float4 ov = *reinterpret_cast<const float4*>(a.ws_o + at * D + d0 + 4 * q);
+  float4 ov[SL];
+#pragma unroll
+  for (int sl = 0; sl < SL; ++sl) ov[sl] = *reinterpret_cast<const float4*>(a.ws_o + at * D + d0 + 32 * sl + 4 * q);
   int n_active = a.n_splits;
   if (a.seq_lens) {
     int cc;
@@ -256,35 +259,40 @@ __global__ __launch_bounds__(256) void merge_rows(MergeArgs a, int rows) {
   if constexpr (SPR >= 4) M = max_x16(M);
   if constexpr (SPR >= 8) M = max_x32(M);
   const float w = act ? rescale(mv.x, M) : 0.f;   // a causal column can have empty chunks (m = -inf)
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);  // sums from +0, as the one-row merge does
+  float4 acc[SL];                            // sums from +0, as the one-row merge does
   float L = 0.f;
-  if (act) {
-    acc.x += w * ov.x;
-    acc.y += w * ov.y;
-    acc.z += w * ov.z;
-    acc.w += w * ov.w;
-    L += w * mv.y;
+#pragma unroll
+  for (int sl = 0; sl < SL; ++sl) {
+    acc[sl] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (act) {
+      acc[sl].x += w * ov[sl].x;
+      acc[sl].y += w * ov[sl].y;
+      acc[sl].z += w * ov[sl].z;
+      acc[sl].w += w * ov[sl].w;
+    }
   }
-  if constexpr (SPR >= 2) {
-    acc.x = sum_x8(acc.x); acc.y = sum_x8(acc.y); acc.z = sum_x8(acc.z); acc.w = sum_x8(acc.w);
-    L = sum_x8(L);
+  if (act) L += w * mv.y;
+#pragma unroll
+  for (int sl = 0; sl < SL; ++sl) {
+    float4& v = acc[sl];
+    if constexpr (SPR >= 2) { v.x = sum_x8(v.x); v.y = sum_x8(v.y); v.z = sum_x8(v.z); v.w = sum_x8(v.w); }
+    if constexpr (SPR >= 4) { v.x = sum_x16(v.x); v.y = sum_x16(v.y); v.z = sum_x16(v.z); v.w = sum_x16(v.w); }
+    if constexpr (SPR >= 8) { v.x = sum_x32(v.x); v.y = sum_x32(v.y); v.z = sum_x32(v.z); v.w = sum_x32(v.w); }
   }
-  if constexpr (SPR >= 4) {
-    acc.x = sum_x16(acc.x); acc.y = sum_x16(acc.y); acc.z = sum_x16(acc.z); acc.w = sum_x16(acc.w);
-    L = sum_x16(L);
-  }
-  if constexpr (SPR >= 8) {
-    acc.x = sum_x32(acc.x); acc.y = sum_x32(acc.y); acc.z = sum_x32(acc.z); acc.w = sum_x32(acc.w);
-    L = sum_x32(L);
-  }
+  if constexpr (SPR >= 2) L = sum_x8(L);
+  if constexpr (SPR >= 4) L = sum_x16(L);
+  if constexpr (SPR >= 8) L = sum_x32(L);
   if (!live || c != 0) return;
   if (a.tri_ml) {                            // merged triplet, relative to M
     if (q == 0 && blockIdx.y == 0) a.tri_ml[r] = make_float2(M, L);
-    *reinterpret_cast<float4*>(a.tri_o + (int64_t)r * D + d0 + 4 * q) = acc;
+#pragma unroll
+    for (int sl = 0; sl < SL; ++sl) *reinterpret_cast<float4*>(a.tri_o + (int64_t)r * D + d0 + 32 * sl + 4 * q) = acc[sl];
   } else {
     const float inv = L > 0.f ? 1.f / L : 0.f;   // L = 0 only when nothing was attended
-    store4<TO>(static_cast<TO*>(a.out) + (int64_t)r * D + d0 + 4 * q,
-               make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv));
+#pragma unroll
+    for (int sl = 0; sl < SL; ++sl)
+      store4<TO>(static_cast<TO*>(a.out) + (int64_t)r * D + d0 + 32 * sl + 4 * q,
+                 make_float4(acc[sl].x * inv, acc[sl].y * inv, acc[sl].z * inv, acc[sl].w * inv));
   }
 }
 
