@@ -178,18 +178,16 @@ int gqa_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_ca
  * fp32 or bf16 out, 1 <= S_q <= GQA_MAX_QUERY_TOKENS. The (token, head)
  * columns fill 16-wide MFMA tiles of t = min(S_q, 16 / n_rep) tokens (the
  * columns single-token decode leaves empty when n_rep < 16). A pass over the
- * KV range serves two tiles (2t tokens read the KV once), or, when a sequence
- * has at least 8 tiles and B * s_kv_hint >= 16384 tokens, at least 4
- * tiles and B * s_kv_hint >= 65536, at least 5 tiles and B * s_kv_hint >=
- * 32768, at least 12 tiles and B * s_kv_hint >= 8192, or at least 16 tiles
- * and tiles * B * s_kv_hint >= 2^18, eight
- * tiles (one per wave, the K/V blocks shared
- * through LDS), sixteen (two per wave) from 16 tiles on; more tokens take
- * more passes. Exactly two tiles with n_rep >= 4 over short KV (B == 1 and
- * s_kv_hint <= 8192, or s_kv_hint <= 2048 and B * s_kv_hint <= 8192) take
- * one tile per pass. The hint only
- * picks the kernel and the split count: either kernel takes any length, and
- * the two round differently. Workspace: gqa_decode_workspace_bytes(B * S_q,
+ * KV range serves two tiles (2t tokens read the KV once), or eight tiles (one
+ * per wave, the K/V blocks shared through LDS; sixteen, two per wave, from
+ * 16 tiles on) when a sequence has at least 8 tiles and B * s_kv_hint >=
+ * 16384 tokens, at least 4 tiles and B * s_kv_hint >= 65536, at least 5
+ * tiles and B * s_kv_hint >= 32768, at least 12 tiles and B * s_kv_hint >=
+ * 8192, or at least 16 tiles and tiles * B * s_kv_hint >= 2^18; more tokens
+ * take more passes. Exactly two tiles with n_rep >= 4 over short KV (B == 1
+ * and s_kv_hint <= 8192, or s_kv_hint <= 2048 and B * s_kv_hint <= 8192)
+ * take one tile per pass. The hint only picks the kernel and the split
+ * count: every kernel takes any length, and they round differently. Workspace: gqa_decode_workspace_bytes(B * S_q,
  * h_q, d_head, n) with n = n_splits if > 0, else gqa_decode_multi_splits_d(B,
  * S_q, h_q, h_kv, d_head, s_kv_hint, 0). B * passes <= 65535. Other
  * arguments as in gqa_decode_attn_ex.
