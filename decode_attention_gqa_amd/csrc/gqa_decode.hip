@@ -94,9 +94,13 @@ const SplitPolicy& split_policy(int tiles_per_wg, int d_head, bool single_token,
 // workgroup per CU, hold this many tokens (each wave one to four 32-token
 // blocks) takes that form: measured faster at 70B shapes from 8k to 32k
 // tokens (and at 1 to 16 kv heads in the same chunk range), slower below
-// (waves without a block) and above (two rounds of 4-wave workgroups balance
-// better), and slower with 64-dimension heads.
-constexpr int64_t kEightWaveMinChunk = 256, kEightWaveMaxChunk = 1024;
+// (waves without a block), and slower with 64-dimension heads. Up to 2048
+// tokens per chunk (64k tokens at 8 kv heads; µs per call p50, two rounds of
+// 4-wave workgroups vs one of 8-wave: 40k 32.98 vs 32.54, 64k 50.44 vs
+// 48.88); above that two rounds of 4-wave workgroups balance better (128k
+// 88.74 vs 90.79, 256k 168.36 vs 170.37; 1M 657.66 vs 648.66 is the
+// exception, not fitted).
+constexpr int64_t kEightWaveMinChunk = 256, kEightWaveMaxChunk = 2048;
 
 // Library-owned fallback workspace, one grow-only buffer per device.
 std::mutex g_ws_mu;
@@ -457,6 +461,16 @@ int pick_splits_host(int B, int passes, int h_kv, int64_t s_kv_max, int num_cus,
     const int64_t cap = (s_kv_max + kMinChunk - 1) / kMinChunk;   // no chunk shorter than kMinChunk
     if (n > cap) n = cap;
   }
+  if (s_kv_max <= 0 && B == 1 && p.eight_wave && p.short_one && num_cus / units >= 1) {
+    // ... no length known, one sequence, one query token, 128-dimension
+    // heads: one round of 8-wave workgroups, one per CU, each sizing its
+    // chunk on the device (c = S / n, at least chunk_floor's). 70B, µs per
+    // call p50, no hint before / after (the hinted plan): 1k 9.74 / 7.65
+    // (7.28), 4k 11.37 / 9.37 (9.26), 8k 13.49 / 12.59 (12.13), 16k 20.03 /
+    // 17.93 (17.11), 32k 32.97 / 28.00 (27.28), 128k 92.86 / 90.92 (90.40),
+    // 1M 655.98 / 648.86 (657.66).
+    return (int)(num_cus / units);
+  }
   if (s_kv_max <= 0 && p.short_one) {
     // ... no length known (one query token): enough chunks for a long
     // sequence, kNoHintRounds rounds of the resident slots, with a chunk
@@ -656,7 +670,16 @@ int make_plan(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv_h
 // forms give a chunk's blocks to their waves differently, so their results
 // differ in rounding.
 Form split_form(const Plan& pl, int B, int h_kv, int d_head) {
-  if (pl.hint <= 0) return Form::kFourWave;
+  if (pl.hint <= 0) {
+    // no length known: the one-round 8-wave plan of a single sequence with
+    // 128-dimension heads (pick_splits_host; min_chunk 0 marks the
+    // heuristic's single-token plan without a hint)
+    int cus = 0;
+    if (B == 1 && d_head == 128 && pl.min_chunk == 0 && device_cus(&cus) == GQA_OK &&
+        (int64_t)pl.ns * h_kv <= cus)
+      return Form::kEightWave;
+    return Form::kFourWave;
+  }
   const int64_t per_chunk = (pl.hint + pl.ns - 1) / pl.ns;
   const int64_t tok = std::min<int64_t>(pl.hint, std::max<int64_t>(per_chunk, pl.min_chunk));
   int cus = 0;

@@ -100,10 +100,11 @@ enum {
  *  scale     multiplies q.k before the softmax (1/sqrt(d_head) for Llama).
  *  n_splits  > 0 forces the number of KV chunks per (sequence, kv head);
  *            <= 0 lets gqa_decode_pick_splits_d choose with no length hint:
- *            a grid of four rounds of workgroups whose chunks, sized on the
- *            device from each sequence's length, hold at least 32 to 128
- *            tokens (at most 4096 tokens each for one 8-kv-head sequence of
- *            up to 1M tokens).
+ *            chunks sized on the device from each sequence's length; for
+ *            one sequence with d_head = 128, num_cus / h_kv chunks run by
+ *            one 8-wave workgroup per compute unit (32 for 8 kv heads on 256
+ *            CUs), otherwise a grid of four rounds of workgroups whose
+ *            chunks hold at least 32 to 128 tokens.
  */
 int gqa_decode_attn(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* seq_lens, void* out,
@@ -308,17 +309,18 @@ int gqa_decode_merge(const int32_t* seq_lens, const void* workspace, size_t work
 
 /*
  * Split count the library uses when n_splits <= 0: enough workgroups that
- * every compute unit has work at B = 1 (s_kv_max = 0, no length known: four
- * rounds of two workgroups per compute unit, e.g. 256 chunks for one
- * sequence with 8 kv heads on 256 CUs, with the chunk floor of a hint-less
- * call, see gqa_decode_partial, so short sequences leave most chunks empty);
- * when s_kv_max > 0 is known, also
+ * every compute unit has work at B = 1 (s_kv_max = 0, no length known: one
+ * sequence with d_head = 128 gets num_cus / h_kv chunks, one 8-wave
+ * workgroup per compute unit, each chunk sized on the device; otherwise four
+ * rounds of two workgroups per compute unit, with the chunk floor of a
+ * hint-less call, see gqa_decode_partial, so short sequences leave most
+ * chunks empty); when s_kv_max > 0 is known, also
  * enough that the longest sequence's chunks fill about two rounds of the
  * resident workgroup slots (B = 1) or B / 2 up to four (B > 1, where lengths
  * may differ),
  * with chunks of 128 to 4096 tokens; at most GQA_MAX_SPLITS. Exceptions for
  * a single sequence: with d_head = 128, one that one workgroup per compute
- * unit covers in chunks of 256 to 1024 tokens gets exactly that many chunks
+ * unit covers in chunks of 256 to 2048 tokens gets exactly that many chunks
  * (num_cus / h_kv), which the library runs with 8-wave workgroups; short
  * sequences in a batch of at most 4 get up to num_cus / (B * h_kv) chunks of
  * at least 32 tokens.

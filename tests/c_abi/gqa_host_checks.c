@@ -89,7 +89,9 @@ int main(void) {
   /* split-count rules and workspace sizes: host arithmetic */
   expect("pick 8k", gqa_decode_pick_splits(1, 8, 8192, 256), 32);
   expect("pick 8191", gqa_decode_pick_splits(1, 8, 8191, 256), 64);
-  expect("pick 40000", gqa_decode_pick_splits(1, 8, 40000, 256), 128);
+  expect("pick 40000 (8-wave round)", gqa_decode_pick_splits(1, 8, 40000, 256), 32);
+  expect("pick 65537", gqa_decode_pick_splits(1, 8, 65537, 256), 128);
+  expect("pick no hint (8-wave round)", gqa_decode_pick_splits(1, 8, 0, 256), 32);
   expect("pick 1M", gqa_decode_pick_splits(1, 8, 1 << 20, 256), 256);
   expect("pick d64 8k", gqa_decode_pick_splits_d(1, 8, 64, 8192, 256), 64);
   expect("pick d96", gqa_decode_pick_splits_d(1, 8, 96, 8192, 256), GQA_ERR_UNSUPPORTED);

@@ -131,7 +131,11 @@ def test_split_heuristic_contract(gqa, B, h_kv, S):
     n = gqa.gqa_decode_pick_splits(B, h_kv, S, cus)
     assert 1 <= n <= gqa.GQA_MAX_SPLITS
     fill = math.ceil(2 * cus / (B * h_kv))
-    if S == 0:
+    if S == 0 and B == 1 and cus // h_kv >= 1:
+        # no length known, one sequence: one round of 8-wave workgroups, one
+        # per CU (each sizes its chunk on the device)
+        assert n == cus // h_kv
+    elif S == 0:
         # no length known: four rounds of the resident slots (the chunk floor
         # then grows with each length on the device)
         assert n == min(4 * fill, gqa.GQA_MAX_SPLITS)
@@ -140,18 +144,19 @@ def test_split_heuristic_contract(gqa, B, h_kv, S):
         # each (32 for a single sequence)
         assert n <= max(1, math.ceil(S / (32 if B <= 4 else 128)))
         # every CU gets work whenever the sequence is long enough: two 4-wave
-        # workgroups per CU, or, for one sequence of 256 to 1024 tokens per
+        # workgroups per CU, or, for one sequence of 256 to 2048 tokens per
         # chunk, one 8-wave workgroup per CU
-        eight_wave = B == 1 and n * h_kv == cus and 256 * n <= S <= 1024 * n
+        eight_wave = B == 1 and n * h_kv == cus and 256 * n <= S <= 2048 * n
         if S >= 128 * fill:
             assert n * B * h_kv >= 2 * cus or eight_wave
 
 
 def test_split_heuristic_values(gqa):
-    # 70B GQA at B = 1, 8k to 32k tokens: one 8-wave workgroup per CU, 8 kv
-    # heads x 32 chunks of 256 to 1024 tokens
+    # 70B GQA at B = 1, 8k to 64k tokens: one 8-wave workgroup per CU, 8 kv
+    # heads x 32 chunks of 256 to 2048 tokens
     assert gqa.gqa_decode_pick_splits(1, 8, 8192, 256) == 32
     assert gqa.gqa_decode_pick_splits(1, 8, 32768, 256) == 32
+    assert gqa.gqa_decode_pick_splits(1, 8, 65536, 256) == 32
     # below: 512 workgroups of 4 waves, chunks of 128 tokens
     assert gqa.gqa_decode_pick_splits(1, 8, 8191, 256) == 64
     assert gqa.gqa_decode_pick_splits(1, 8, 4096, 256) == 32
@@ -165,7 +170,7 @@ def test_split_heuristic_values(gqa):
     assert gqa.gqa_decode_pick_splits(2, 8, 256, 256) == 8      # B <= 4: the same
     assert gqa.gqa_decode_pick_splits(8, 8, 256, 256) == 2      # larger batches: 128-token chunks
     # above: two rounds of the 512 resident slots
-    assert gqa.gqa_decode_pick_splits(1, 8, 32769, 256) == 128
+    assert gqa.gqa_decode_pick_splits(1, 8, 65537, 256) == 128
     assert gqa.gqa_decode_pick_splits(1, 8, 131072, 256) == 128
     # the 7B MHA shape (32 kv heads): 8 chunks from 2048 to 8192 tokens
     assert gqa.gqa_decode_pick_splits(1, 32, 4096, 256) == 8
@@ -181,10 +186,13 @@ def test_split_heuristic_values(gqa):
     assert gqa.gqa_decode_pick_splits(1, 8, 1 << 22, 256) == 1024
     # several sequences: the longest over four rounds
     assert gqa.gqa_decode_pick_splits(8, 8, 32768, 256) == 32
-    # no length hint: four rounds of the resident slots
-    assert gqa.gqa_decode_pick_splits(1, 8, 0, 256) == 256
+    # no length hint: one sequence with 128-dimension heads, one round of
+    # 8-wave workgroups (chunks sized on the device); otherwise four rounds
+    # of the resident slots
+    assert gqa.gqa_decode_pick_splits(1, 8, 0, 256) == 32
+    assert gqa.gqa_decode_pick_splits(1, 32, 0, 256) == 8
+    assert gqa.gqa_decode_pick_splits(1, 512, 0, 256) == 4       # more kv heads than CUs
     assert gqa.gqa_decode_pick_splits(8, 8, 0, 256) == 32
-    assert gqa.gqa_decode_pick_splits(1, 32, 0, 256) == 64
     assert gqa.gqa_decode_pick_splits_d(1, 8, 64, 0, 256) == 256
 
 
@@ -196,8 +204,9 @@ def test_multi_split_heuristic_values(gqa):
     fd = lambda B, S_q, S, d: gqa.lib.gqa_decode_multi_splits_d(B, S_q, 64, 8, d, S, 256)
     assert f(1, 1, 8192) == gqa.gqa_decode_pick_splits_d(1, 8, 64, 8192, 256) == 64
     assert f(1, 2, 8192) == fd(1, 2, 8192, 128) == gqa.gqa_decode_pick_splits_d(1, 8, 128, 8192, 256) == 32
-    assert f(1, 2, 32768) == 32                  # the 8-wave round up to 1024 tokens per chunk
-    assert f(1, 2, 65536) == 128
+    assert f(1, 2, 32768) == 32                  # the 8-wave round up to 2048 tokens per chunk
+    assert f(1, 2, 65536) == 32
+    assert f(1, 2, 65537) == 128
     assert fd(1, 2, 8192, 64) == 64
     assert fd(1, 2, 8192, 96) == -2              # GQA_ERR_UNSUPPORTED
     # two tiles per workgroup, one workgroup per CU: one round for one sequence
