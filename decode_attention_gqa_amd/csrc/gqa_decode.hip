@@ -65,7 +65,8 @@ constexpr SplitPolicy kOneTileMulti{2, 2, 4, 4096, false, false};
 // The same with 128-dimension heads: a single sequence may take the 8-wave
 // round like a single-token call (one tile of several query tokens, e.g. two
 // at 70B shapes: 8k 13.8 -> 12.5 µs per call, 16k 19.5 -> 17.7, 32k 31.8 ->
-// 27.8).
+// 27.8; with the round up to 2048-token chunks, 40k 37.2 -> 32.8, 64k 54.1
+// -> 49.4).
 constexpr SplitPolicy kOneTileMulti8{2, 2, 4, 4096, true, false};
 // Two tiles per workgroup (multi-token decode), one workgroup per CU: one
 // round for a single sequence; chunks up to 16384 tokens.

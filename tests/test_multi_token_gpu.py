@@ -217,11 +217,12 @@ def test_two_tiles_eight_waves(n_rep, S_q, d):
         assert max_err(got, four) <= 1e-3
 
 
-@pytest.mark.parametrize("n_rep,S_q,S", [(8, 2, 8192), (8, 2, 20000), (4, 4, 9000), (16, 1, 8192), (8, 2, 40000)])
+@pytest.mark.parametrize("n_rep,S_q,S", [(8, 2, 8192), (8, 2, 20000), (4, 4, 9000), (16, 1, 8192), (8, 2, 40000),
+                                         (8, 2, 70000)])
 def test_one_tile_eight_waves(n_rep, S_q, S):
     """One tile of several query tokens (S_q <= 16 / n_rep) over a single
     sequence with 128-dimension heads takes the single-token 8-wave round
-    when its chunks hold 256 to 1024 tokens (8k to 32k at 8 kv heads; 40000:
+    when its chunks hold 256 to 2048 tokens (8k to 64k at 8 kv heads; 70000:
     past it, four waves); S_q = 1 through this entry point keeps its own
     plan. Against the oracle, and against a forced split count."""
     h_kv = 8
