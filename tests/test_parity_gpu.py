@@ -219,14 +219,17 @@ def test_base_entry_point_and_library_workspace():
         report(f"base entry ns={ns}", max_err(out.cpu().numpy().astype(np.float64), ref), ns, TOL_F32)
 
 
-@pytest.mark.parametrize("lens", [[1], [31], [32], [256], [1000], [1024], [3000], [4096], [4097], [8192],
-                                  [20000], [70000], [5, 0, 2049, 8191], [11032, 4287, 10486, 11180, 21209, 32739,
-                                                                     5895, 7145]])
+@pytest.mark.parametrize("lens", [[1], [31], [32], [33], [256], [1000], [1024], [3000], [4096], [4097],
+                                  [8192], [8193], [20000], [70000], [5, 0, 2049, 8191],
+                                  [11032, 4287, 10486, 11180, 21209, 32739, 5895, 7145]])
 def test_base_entry_point_without_hint_at_many_lengths(lens):
-    """The base entry point plans without the lengths: a grid of several
-    rounds of chunks, whose floor grows with each sequence's length on the
-    device. Every length class against the oracle; the merge must agree with
-    the split kernel on which chunks exist (the workspace is NaN-poisoned)."""
+    """The base entry point plans without the lengths: one sequence gets one
+    round of 8-wave workgroups (one per CU), a batch a grid of several rounds
+    of 4-wave ones, and either sizes its chunks on the device from each
+    sequence's length. Every length class (an empty sequence, one token, a
+    block and one past it, lengths just past a multiple of the 32 chunks)
+    against the oracle; the merge must agree with the split kernel on which
+    chunks exist (the workspace is NaN-poisoned)."""
     import torch
 
     import decode_attention_gqa_amd as gqa
@@ -240,6 +243,37 @@ def test_base_entry_point_without_hint_at_many_lengths(lens):
         out = gqa.gqa_decode_attn(q, k, v, dl, scale=float(inp.scale))
         torch.cuda.synchronize()
         np.testing.assert_array_equal(out.cpu().numpy().astype(np.float64), got)
+
+
+@pytest.mark.parametrize("hint", [0, 4096])
+def test_single_empty_sequence_reads_nothing(hint):
+    """One sequence of length 0 (its rows at an explicit offset into a cache
+    of NaN rows): without a hint (the one-round 8-wave plan, chunks sized on
+    the device) and with one, the output is exactly 0 and no row is read."""
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    k = torch.full((64, 8, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    v = torch.full_like(k, float("nan"))
+    q = torch.randn((1, 64, 128), device="cuda").to(torch.bfloat16)
+    lens = torch.zeros(1, dtype=torch.int32, device="cuda")
+    offs = torch.tensor([16], dtype=torch.int64, device="cuda")
+    out = gqa.gqa_decode_attn_ex(q, k, v, lens, kv_token_offsets=offs, scale=0.088, s_kv_hint=hint)
+    torch.cuda.synchronize()
+    assert torch.equal(out, torch.zeros_like(out))
+
+
+@pytest.mark.parametrize("h_kv,lens", [(32, [4096]), (32, [77]), (1, [50000]), (16, [9000])])
+def test_base_entry_point_without_hint_other_head_counts(h_kv, lens):
+    """The hint-less one-round plan at other kv-head counts (N_CU / h_kv
+    chunks: 8 for MHA's 32 kv heads, 256 for one kv head, 16 for 16)."""
+    import decode_attention_gqa_amd as gqa
+    h_q = 32 if h_kv == 32 else 8 * h_kv
+    inp = workloads.custom(f"nohint_h{h_kv}_{lens[0]}", B=1, h_q=h_q, h_kv=h_kv, d=128, seq_lens=lens,
+                           seed=120 + h_kv + lens[0] % 89)
+    got, ns = run_gpu(inp, hint=False)
+    assert ns == gqa.gqa_decode_pick_splits(1, h_kv, 0)
+    report(f"no hint h_kv={h_kv} lens={lens}", max_err(got, ref_of(inp)), ns, TOL_F32)
 
 
 def test_runs_on_a_side_stream():
