@@ -92,7 +92,7 @@ const SplitPolicy& split_policy(int tiles_per_wg, int d_head, bool single_token,
   return single_token || s_q == 1 ? kOneTile64 : kOneTileMulti;
 }
 // A single sequence with 128-dimension heads whose chunks, at one 8-wave
-// workgroup per CU, hold this many tokens (each wave one to four 32-token
+// workgroup per CU, hold this many tokens (each wave one to eight 32-token
 // blocks) takes that form: measured faster at 70B shapes from 8k to 32k
 // tokens (and at 1 to 16 kv heads in the same chunk range), slower below
 // (waves without a block), and slower with 64-dimension heads. Up to 2048
@@ -255,8 +255,6 @@ hipError_t launch_split_append(int nrep, Form form, dim3 grid, hipStream_t st, c
   return hipGetLastError();
 }
 
-// Split counts that merge_wave merges (one workgroup per row, which is what
-// MergeArgs::xcd_rep remaps).
 // Rows from which merge_wave takes two 32-column slices per wave (half the
 // waves: a multi-token call's 4096 rows then fit the wave slots in one
 // round). 70B B = 1, µs per call p50, two interleaved A/B runs of 9 rounds,
@@ -267,6 +265,8 @@ hipError_t launch_split_append(int nrep, Form form, dim3 grid, hipStream_t st, c
 // wave (more waves, each with less to load): one query token, 64 rows, 8k
 // 11.84 vs 11.99 (two slices) and 12.19 (four), 16k 16.77 vs 17.06 / 16.98.
 constexpr int64_t kMergeWideRows = 1024;
+// Split counts that merge_wave merges (one workgroup per row, which is what
+// MergeArgs::xcd_rep remaps).
 constexpr int kMergeWaveMinSplits = 9, kMergeWaveMaxSplits = 32;
 
 template <int D, typename TO>
