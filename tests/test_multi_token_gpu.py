@@ -261,6 +261,20 @@ def test_two_tiles_one_per_pass(lens, S_q):
     assert max_err(got, two) <= 1e-3
 
 
+@pytest.mark.parametrize("ns", [2, 5, 8, 9, 16, 17, 32])
+@pytest.mark.parametrize("d", [64, 128])
+def test_merges_of_many_rows(ns, d):
+    """Calls of 1024 or more (token, head) rows merge with wider lanes (a
+    chunk's whole row per lane up to 8 chunks, two 32-column slices per wave
+    from 9 to 32): forced split counts that pick each merge kernel and its
+    chunk-count variants, against the oracle (B = 2, S_q = 48, 16 query heads:
+    1536 rows; a sequence shorter than the chunk count leaves chunks empty)."""
+    lens = [1500, 40]
+    inp, qm = make(f"wide_merge_ns{ns}_d{d}", 2, 48, 16, 2, d, lens, 300 + ns + d)
+    check(f"wide merge ns={ns} d={d}", inp, qm, n_splits=ns)
+    check(f"wide merge ns={ns} d={d} bf16", inp, qm, n_splits=ns, out_dtype="bf16")
+
+
 @pytest.mark.parametrize("n_rep,S_q,d", [(8, 96, 128), (8, 256, 128), (1, 128, 128), (4, 200, 64), (16, 130, 128),
                                          (8, 90, 128), (8, 90, 64), (2, 160, 64), (1, 272, 128)])
 def test_many_query_tokens(n_rep, S_q, d):
