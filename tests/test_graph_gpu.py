@@ -84,3 +84,39 @@ def test_graph_decode_loop_append_attend():
         e = gqa.gqa_decode_attn_ex(q_d, k_d, v_d, lens_e, kv_token_offsets=offs, s_kv_hint=cap)
         torch.cuda.synchronize()
         assert torch.equal(e, out_d), f"step {t}: graph replay differs from the eager call"
+
+
+def test_one_graph_serves_every_length_without_a_hint():
+    """A call without a length hint (one sequence: one round of 8-wave
+    workgroups whose chunks are sized on the device) captured once and
+    replayed while the length in device memory changes from a few tokens to
+    the whole cache: every replay matches the oracle, with eager work and
+    synchronisations between replays."""
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    h_q, h_kv, d, cap = 64, 8, 128, 20000
+    k = workloads.normals(9, 1, cap * h_kv * d).reshape(cap, h_kv, d)
+    v = workloads.normals(9, 2, cap * h_kv * d).reshape(cap, h_kv, d)
+    q = workloads.normals(9, 3, h_q * d).reshape(1, h_q, d)
+    k_d, v_d, q_d = bf16_dev(k), bf16_dev(v), bf16_dev(q)
+    lens = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out_d = torch.empty((1, h_q, d), dtype=torch.float32, device="cuda")
+    ns = gqa.gqa_decode_pick_splits_d(1, h_kv, d, 0)
+    ws = torch.empty(gqa.gqa_decode_workspace_bytes(1, h_q, d, ns), dtype=torch.uint8, device="cuda")
+    st = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        gqa.gqa_decode_attn_ex(q_d, k_d, v_d, lens, out_d, s_kv_hint=0, workspace=ws)
+    torch.cuda.synchronize()
+    scale = np.float32(d ** -0.5)
+    for S in (3, 700, 8192, 8193, 20000, 31):
+        lens.fill_(S)
+        out_d.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = oracle.attend(q, k[:S], v[:S], np.array([S], dtype=np.int32), scale, h_kv, dtype="bf16")
+        err = max_err(out_d.cpu().numpy().astype(np.float64), ref)
+        print(f"[graph, no hint] S={S} n_splits={ns} max_abs_err={err:.3e}", flush=True)
+        assert err <= TOL_F32
