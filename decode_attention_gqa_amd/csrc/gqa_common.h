@@ -48,6 +48,10 @@ struct SplitArgs {
   // tile-per-wave kernel: the grid is (h_kv, n_splits, B * passes), kv heads
   // fastest (split_grid_heads_fastest), instead of split_grid's order
   int heads_fastest;
+  // B (2 to kRankedMaxBatch sequences): the grid's batch slot z runs the
+  // sequence of rank z by length, longest first (seq_info_ranked); 0: slot z
+  // runs sequence z
+  int ranked;
 };
 
 struct MergeArgs {
@@ -206,6 +210,46 @@ __device__ __forceinline__ void seq_info(const int32_t* seq_lens, const int64_t*
   }
   S = sb;
   off = (int64_t)wave_sum_u64((uint64_t)acc);
+}
+
+// Longest sequences first. The hardware starts workgroups in grid order, and
+// with the batch as the grid's slowest dimension a ragged batch whose
+// longest sequence comes late starts that sequence's chunks (every sequence
+// gets the same number, so its chunks are the longest) in the last rounds,
+// where they form the launch's tail. Here batch slot z (z < B <= kRankedMaxBatch)
+// runs the sequence of rank z by length, longest first, ties in batch order:
+// the longest chunks start first (the longest-processing-time-first order
+// of list scheduling). One wave loads the B lengths (and explicit offsets),
+// one lane per sequence; each lane counts the sequences that rank before
+// its own, with keys (length, 63 - lane) that are all distinct, so exactly
+// one lane holds rank z (the ballot below is never empty; should it be, the
+// slot keeps sequence z). The same loads give the chosen sequence's length
+// and its packed token base (the lengths of the sequences before it in the
+// batch), so this costs no memory round trip over seq_info. Which workgroup
+// computes which chunk changes no arithmetic: the bits are those of the
+// batch order.
+constexpr int kRankedMaxBatch = 8;
+__device__ __forceinline__ void seq_info_ranked(const int32_t* seq_lens, const int64_t* kv_off, int B, int z,
+                                                int lane, int& b, int& S, int64_t& off) {
+  const bool in = lane < B;
+  const int v = in ? seq_lens[lane] : 0;
+  const int64_t o = (in && kv_off) ? kv_off[lane] : 0;
+  const uint64_t key = ((uint64_t)(uint32_t)v << 6) | (uint32_t)(63 - lane);
+  int rank = 0;
+  for (int j = 0; j < B; ++j) {                   // j is uniform: readlane takes it as a scalar
+    const uint64_t kj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(key >> 32), j) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key, j);
+    rank += kj > key ? 1 : 0;
+  }
+  const uint64_t hit = __builtin_amdgcn_ballot_w64(in && rank == z);
+  b = hit ? (int)__builtin_ctzll(hit) : z;
+  S = __builtin_amdgcn_readlane(v, b);
+  if (kv_off) {
+    off = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(o >> 32), b) << 32) |
+                    (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)o, b));
+  } else {
+    off = (int64_t)wave_sum_u64(lane < b ? (uint64_t)(uint32_t)v : 0ull);
+  }
 }
 
 // Streaming loads of the KV cache: every K/V byte is read once per call, so

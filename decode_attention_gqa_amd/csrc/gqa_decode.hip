@@ -779,6 +779,15 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
     grid = gqa::split_grid_heads_fastest(pl.ns, h_kv, B * passes);
     sa.heads_fastest = 1;
   }
+  // A few sequences over several rounds of workgroups start longest first
+  // (gqa::seq_info_ranked). Within one round the order gains nothing, and the
+  // ranking loop, one step per sequence, costs more with larger batches. 70B
+  // shapes, µs per call, batch order / longest first: ragged B = 8 78.8 /
+  // 75.5; B = 32 of 64-2100 tokens 31.9 / 37.1, 16 x 4k 53.7 / 55.8, 12k + 3k
+  // (one round) 16.3 / 16.5 with every batch ranked.
+  int cus = 0;
+  const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
+  if (B >= 2 && B <= gqa::kRankedMaxBatch && device_cus(&cus) == GQA_OK && wgs > 2 * (int64_t)cus) sa.ranked = B;
   e = d_head == 128 ? launch_split_nrep<128>(nrep, bf16, valu, form, grid, stream, sa)
                     : launch_split_nrep<64>(nrep, bf16, valu, form, grid, stream, sa);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));

@@ -351,7 +351,8 @@ void split_kv_mfma(SplitArgs a) {
   // 8 waves: the grid has kv heads fastest (split_grid_heads_fastest).
   const WgCoord wc = WAVES == 8 ? WgCoord{(int)blockIdx.y, (int)blockIdx.x, (int)blockIdx.z} : wg_coord();
   const int s = wc.s, g = wc.g;
-  const int b = a.passes == 1 ? wc.b : wc.b / a.passes, pass = wc.b - b * a.passes;
+  const int zb = a.passes == 1 ? wc.b : wc.b / a.passes, pass = wc.b - zb * a.passes;
+  int b = zb;                                      // the sequence (batch slot zb runs it)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   const int grp = lane >> 4, n = lane & 15;
@@ -374,6 +375,8 @@ void split_kv_mfma(SplitArgs a) {
     off = a.kv_off ? a.kv_off[b] : (int64_t)b * a.capacity;
     appended = old < a.capacity;                   // else the new row is dropped
     S = appended ? old + 1 : a.capacity;
+  } else if (a.ranked) {
+    seq_info_ranked(a.seq_lens, a.kv_off, a.ranked, zb, lane, b, S, off);
   } else {
     seq_info(a.seq_lens, a.kv_off, b, lane, S, off);
   }

@@ -87,7 +87,8 @@ void split_kv_tiles(SplitArgs a) {
 
   const WgCoord wc = a.heads_fastest ? WgCoord{(int)blockIdx.y, (int)blockIdx.x, (int)blockIdx.z} : wg_coord();
   const int s = wc.s, g = wc.g;
-  const int b = wc.b / a.passes, pass = wc.b - b * a.passes;
+  const int zb = wc.b / a.passes, pass = wc.b - zb * a.passes;
+  int b = zb;                                       // the sequence (batch slot zb runs it)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = lane >> 4, n = lane & 15;
@@ -105,7 +106,10 @@ void split_kv_tiles(SplitArgs a) {
 
   int S;
   int64_t off;
-  seq_info(a.seq_lens, a.kv_off, b, lane, S, off);
+  if (a.ranked)
+    seq_info_ranked(a.seq_lens, a.kv_off, a.ranked, zb, lane, b, S, off);
+  else
+    seq_info(a.seq_lens, a.kv_off, b, lane, S, off);
   S = __builtin_amdgcn_readfirstlane(S);
   off = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(off >> 32)) << 32) |
                   (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)off));

@@ -77,12 +77,16 @@ __global__ __launch_bounds__(kThreads) void split_kv_valu(SplitArgs a) {
   constexpr int DPL = D / 64;                      // output dimensions per lane
   constexpr int TB = 64;                           // tokens per block (one per lane)
   const WgCoord wc = wg_coord();
-  const int s = wc.s, g = wc.g, b = wc.b;
+  const int s = wc.s, g = wc.g;
+  int b = wc.b;                                    // the sequence (batch slot wc.b runs it)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
   int S;
   int64_t off;
-  seq_info(a.seq_lens, a.kv_off, b, lane, S, off);
+  if (a.ranked)
+    seq_info_ranked(a.seq_lens, a.kv_off, a.ranked, wc.b, lane, b, S, off);
+  else
+    seq_info(a.seq_lens, a.kv_off, b, lane, S, off);
   int c, n_active;
   chunking(S, a.n_splits, a.min_chunk, c, n_active);
   if (s >= n_active) {
