@@ -229,11 +229,10 @@ __device__ __forceinline__ void seq_info(const int32_t* seq_lens, const int64_t*
 // computes which chunk changes no arithmetic: the bits are those of the
 // batch order.
 constexpr int kRankedMaxBatch = 8;
-__device__ __forceinline__ void seq_info_ranked(const int32_t* seq_lens, const int64_t* kv_off, int B, int z,
-                                                int lane, int& b, int& S, int64_t& off) {
+// The sequence b of rank z given lane j's length v (lanes below B), ties in
+// batch order.
+__device__ __forceinline__ int rank_slot(int v, int B, int z, int lane) {
   const bool in = lane < B;
-  const int v = in ? seq_lens[lane] : 0;
-  const int64_t o = (in && kv_off) ? kv_off[lane] : 0;
   const uint64_t key = ((uint64_t)(uint32_t)v << 6) | (uint32_t)(63 - lane);
   int rank = 0;
   for (int j = 0; j < B; ++j) {                   // j is uniform: readlane takes it as a scalar
@@ -242,7 +241,14 @@ __device__ __forceinline__ void seq_info_ranked(const int32_t* seq_lens, const i
     rank += kj > key ? 1 : 0;
   }
   const uint64_t hit = __builtin_amdgcn_ballot_w64(in && rank == z);
-  b = hit ? (int)__builtin_ctzll(hit) : z;
+  return hit ? (int)__builtin_ctzll(hit) : z;
+}
+__device__ __forceinline__ void seq_info_ranked(const int32_t* seq_lens, const int64_t* kv_off, int B, int z,
+                                                int lane, int& b, int& S, int64_t& off) {
+  const bool in = lane < B;
+  const int v = in ? seq_lens[lane] : 0;
+  const int64_t o = (in && kv_off) ? kv_off[lane] : 0;
+  b = rank_slot(v, B, z, lane);
   S = __builtin_amdgcn_readlane(v, b);
   if (kv_off) {
     off = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(o >> 32), b) << 32) |

@@ -371,7 +371,14 @@ void split_kv_mfma(SplitArgs a) {
   int64_t off;
   bool appended = false;                           // APPEND: the new token is position S - 1
   if constexpr (APPEND) {
-    const int old = a.seq_lens[b];
+    int old;
+    if (a.ranked) {                                // longest first, as seq_info_ranked
+      const int v = lane < a.ranked ? a.seq_lens[lane] : 0;
+      b = rank_slot(v, a.ranked, zb, lane);
+      old = __builtin_amdgcn_readlane(v, b);
+    } else {
+      old = a.seq_lens[b];
+    }
     off = a.kv_off ? a.kv_off[b] : (int64_t)b * a.capacity;
     appended = old < a.capacity;                   // else the new row is dropped
     S = appended ? old + 1 : a.capacity;

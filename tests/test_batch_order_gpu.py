@@ -96,3 +96,40 @@ def test_permuted_multi_token_batch(S_q):
                    scale, hint, s_q=S_q)
         assert torch.equal(got, base[perm]), f"S_q={S_q} {name}: rows differ from the batch order's"
         print(f"[order] S_q={S_q} B={B} {name}: rows equal the batch order's", flush=True)
+
+
+def test_permuted_decode_step():
+    """The decode step with the append folded in (gqa_decode_step) ranks the
+    batch by its lengths before the append. A permuted batch, addressed
+    through permuted token offsets into the same padded cache, gives the
+    permuted output rows and lengths bit for bit, and writes the same cache
+    rows (each new row to its own sequence's slot)."""
+    import torch
+
+    import decode_attention_gqa_amd as gqa
+    lens = np.array([11032, 4287, 10486, 0, 21209, 32739, 5895, 7145], dtype=np.int32)
+    B, h_q, h_kv, d, cap = len(lens), 64, 8, 128, 32768
+    g = torch.Generator(device="cpu").manual_seed(340)
+    rnd = lambda *shape: torch.randn(*shape, generator=g).to(torch.bfloat16).cuda()   # noqa: E731
+    q, kn, vn = rnd(B, h_q, d), rnd(B, h_kv, d), rnd(B, h_kv, d)
+    kc, vc = rnd(B * cap, h_kv, d), rnd(B * cap, h_kv, d)
+    dl = torch.from_numpy(lens).cuda()
+    off = torch.arange(B, dtype=torch.int64, device="cuda") * cap
+
+    def step(perm, kc, vc):
+        pt = torch.from_numpy(perm).cuda()
+        lo = torch.empty(B, dtype=torch.int32, device="cuda")
+        out = gqa.gqa_decode_step(q[pt].contiguous(), kn[pt].contiguous(), vn[pt].contiguous(), kc, vc,
+                                  dl[pt].contiguous(), lo, capacity=cap, kv_token_offsets=off[pt].contiguous())
+        torch.cuda.synchronize()
+        return out.cpu(), lo.cpu()
+
+    kc0, vc0 = kc.clone(), vc.clone()
+    base, lo0 = step(np.arange(B), kc0, vc0)
+    for name, perm in orders(B, 350).items():
+        kc1, vc1 = kc.clone(), vc.clone()
+        got, lo1 = step(perm, kc1, vc1)
+        assert torch.equal(got, base[perm]), f"decode step {name}: rows differ from the batch order's"
+        assert torch.equal(lo1, lo0[perm]), f"decode step {name}: lengths differ"
+        assert torch.equal(kc1, kc0) and torch.equal(vc1, vc0), f"decode step {name}: cache rows differ"
+        print(f"[order] decode step B={B} {name}: rows, lengths and cache equal the batch order's", flush=True)
