@@ -223,22 +223,30 @@ __device__ __forceinline__ void seq_info(const int32_t* seq_lens, const int64_t*
 // one lane per sequence; each lane counts the sequences that rank before
 // its own, with keys (length, 63 - lane) that are all distinct, so exactly
 // one lane holds rank z (the ballot below is never empty; should it be, the
-// slot keeps sequence z). The same loads give the chosen sequence's length
+// slot keeps sequence z). The count takes one step per sequence, so the host
+// asks for it only where the order pays (ranked_batch). The same loads give the chosen sequence's length
 // and its packed token base (the lengths of the sequences before it in the
 // batch), so this costs no memory round trip over seq_info. Which workgroup
 // computes which chunk changes no arithmetic: the bits are those of the
 // batch order.
-constexpr int kRankedMaxBatch = 8;
+constexpr int kRankedMaxBatch = 64;
 // The sequence b of rank z given lane j's length v (lanes below B), ties in
 // batch order.
 __device__ __forceinline__ int rank_slot(int v, int B, int z, int lane) {
   const bool in = lane < B;
-  const uint64_t key = ((uint64_t)(uint32_t)v << 6) | (uint32_t)(63 - lane);
+  // Keys: the length (clamped to 2^26 - 1; longer ones tie and keep the batch
+  // order) above the lane's 6 bits, reversed so that an earlier sequence
+  // wins a tie. Groups of 8 lanes per step: j0 <= 56 when B <= 64, so every
+  // lane index read is below 64.
+  const uint32_t key = (min((uint32_t)v, (1u << 26) - 1u) << 6) | (uint32_t)(63 - lane);
   int rank = 0;
-  for (int j = 0; j < B; ++j) {                   // j is uniform: readlane takes it as a scalar
-    const uint64_t kj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(key >> 32), j) << 32) |
-                        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key, j);
-    rank += kj > key ? 1 : 0;
+  for (int j0 = 0; j0 < B; j0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;                       // uniform: readlane takes it as a scalar
+      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key, j);
+      rank += (j < B && kj > key) ? 1 : 0;
+    }
   }
   const uint64_t hit = __builtin_amdgcn_ballot_w64(in && rank == z);
   return hit ? (int)__builtin_ctzll(hit) : z;

@@ -741,17 +741,25 @@ Form choose_form(const Plan& pl, int B, int h_q, int h_kv, int d_head, int s_q, 
   return Form::kFourWave;
 }
 
-// A few sequences over several rounds of workgroups start longest first
-// (gqa::seq_info_ranked): returns B for the kernels' `ranked`, else 0. Within
-// one round the order gains nothing, and the ranking loop, one step per
-// sequence, costs more with larger batches. 70B shapes, µs per call, batch
-// order / longest first: ragged B = 8 78.8 / 75.5; with every batch up to 64
-// ranked, B = 32 of 64-2100 tokens 31.9 / 37.1, 16 x 4k 53.7 / 55.8, 12k + 3k
-// (one round) 16.3 / 16.5.
-int ranked_batch(int B, dim3 grid) {
+// Sequences of a batch over several rounds of workgroups start longest
+// first (gqa::seq_info_ranked): returns B for the kernels' `ranked`, else 0.
+// Within one round the order gains nothing. The ranking takes one step per
+// sequence in every workgroup, so batches of more than 8 are ranked only
+// when the longest chunk (hint / split count) holds at least
+// kRankedMinChunk tokens, long enough for the order to pay for it. 70B
+// shapes, µs per call, batch order / longest first: ragged B = 8 80.2 /
+// 75.4, 16 sequences of 1k-32k 178.4 / 165.0, 32 of 1k-16k 224.8 / 215.9,
+// 64 of 512-8k 216.2 / 205.0; ranked without the chunk rule, 32 x 4k
+// (512-token chunks) 94.6 / 97.1; with the earlier loop of one 64-bit step
+// per sequence and no chunk rule, 32 of 64-2100 tokens 31.9 / 37.1 and
+// 12k + 3k (one round) 16.3 / 16.5.
+constexpr int64_t kRankedMinChunk = 1024;
+int ranked_batch(int B, dim3 grid, int64_t hint, int ns) {
   int cus = 0;
   const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
-  return (B >= 2 && B <= gqa::kRankedMaxBatch && device_cus(&cus) == GQA_OK && wgs > 2 * (int64_t)cus) ? B : 0;
+  if (B < 2 || B > gqa::kRankedMaxBatch || device_cus(&cus) != GQA_OK || wgs <= 2 * (int64_t)cus) return 0;
+  if (B > 8 && (hint <= 0 || (hint + ns - 1) / ns < kRankedMinChunk)) return 0;
+  return B;
 }
 
 // direct: the caller merges nothing afterwards; with one chunk per sequence
@@ -792,7 +800,7 @@ int run_split(const Plan& pl, const void* q, const void* k_cache, const void* v_
     grid = gqa::split_grid_heads_fastest(pl.ns, h_kv, B * passes);
     sa.heads_fastest = 1;
   }
-  sa.ranked = ranked_batch(B, grid);
+  sa.ranked = ranked_batch(B, grid, pl.hint, pl.ns);
   e = d_head == 128 ? launch_split_nrep<128>(nrep, bf16, valu, form, grid, stream, sa)
                     : launch_split_nrep<64>(nrep, bf16, valu, form, grid, stream, sa);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
@@ -1072,7 +1080,7 @@ int gqa_decode_step(const void* q, const void* k_new, const void* v_new, void* k
   const Form form = split_form(pl, B, h_kv, d_head);   // the same form as gqa_decode_attn_ex with this hint
   const dim3 grid = form == Form::kEightWave ? gqa::split_grid_heads_fastest(pl.ns, h_kv, B)
                                              : gqa::split_grid(pl.ns, h_kv, B);
-  sa.ranked = ranked_batch(B, grid);
+  sa.ranked = ranked_batch(B, grid, pl.hint, pl.ns);
   hipError_t e = d_head == 128 ? launch_split_append<128>(nrep, form, grid, stream, sa)
                                : launch_split_append<64>(nrep, form, grid, stream, sa);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));

@@ -1,12 +1,14 @@
-"""Batch order. With 2 to 8 sequences over more than one round of
-workgroups, the split kernels start the longest sequence's chunks first:
-batch slot z of the grid runs the sequence of rank z by length (ties in batch
-order). Which workgroup computes which chunk changes no arithmetic, so
-permuting a batch must permute the output rows bit for bit, and every order
-must match the fp64 oracle. Both the packed layout (token bases summed from
-the lengths) and explicit token offsets are covered, with ties and an empty
-sequence, ranked batches of 8 and 2 (a forced split count gives the pair
-more than one round) and larger batches, which keep the batch order."""
+"""Batch order. Over more than one round of workgroups, the split kernels
+start the longest sequence's chunks first for batches of 2 to 8 sequences,
+and for batches of up to 64 whose longest chunk holds 1024 or more tokens:
+batch slot z of the grid runs the sequence of rank z by length (ties in
+batch order). Which workgroup computes which chunk changes no arithmetic,
+so permuting a batch must permute the output rows bit for bit, and every
+order must match the fp64 oracle. Both the packed layout (token bases summed
+from the lengths) and explicit token offsets are covered, with ties and an
+empty sequence, ranked batches of 8, 2 (a forced split count gives the pair
+more than one round) and 12, and batches that keep the batch order (9 and
+65 short sequences)."""
 import numpy as np
 import pytest
 
@@ -73,6 +75,29 @@ def test_permuted_batch_permutes_output(lens, ns):
                    n_splits=ns)
         assert torch.equal(got, base[perm]), f"B={B} {name}: explicit offsets, rows differ from the batch order's"
         print(f"[order] B={B} {name}: packed and offset calls equal the batch order's rows", flush=True)
+
+
+def test_permuted_large_ranked_batch():
+    """Twelve sequences of 2k-24k tokens at 70B shapes: 22 chunks of up to
+    1118 tokens, so the batch is ranked; the oracle checks every kv group on
+    one query head each (0, 9, ..., 63)."""
+    import torch
+    lens = np.random.default_rng(360).integers(2048, 24577, 12).astype(np.int32)
+    B = len(lens)
+    inp = workloads.custom("order12", B=B, h_q=64, h_kv=8, d=128, seq_lens=lens, seed=360)
+    q, k, v, dl = to_device(inp)
+    hint, scale = int(lens.max()), float(inp.scale)
+    base = call(q, k, v, dl, scale, hint)
+    heads = list(range(0, 64, 9))                      # rows left out stay NaN, which max_err skips
+    ref = oracle.attend(inp.q, inp.k, inp.v, inp.seq_lens, inp.scale, inp.w.h_kv, dtype="bf16",
+                        heads=[(b, h) for b in range(B) for h in heads])
+    report(f"B={B} batch order, heads {heads}", max_err(base.numpy().astype(np.float64), ref), TOL_F32)
+    for name, perm in orders(B, 370).items():
+        pt = torch.from_numpy(perm).cuda()
+        got = call(q[pt].contiguous(), packed(k, lens, perm), packed(v, lens, perm), dl[pt].contiguous(),
+                   scale, hint)
+        assert torch.equal(got, base[perm]), f"B={B} {name}: rows differ from the batch order's"
+        print(f"[order] B={B} {name}: rows equal the batch order's", flush=True)
 
 
 @pytest.mark.parametrize("S_q", [4, 64])
