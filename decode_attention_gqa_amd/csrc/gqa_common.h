@@ -216,19 +216,19 @@ __device__ __forceinline__ void seq_info(const int32_t* seq_lens, const int64_t*
 // with the batch as the grid's slowest dimension a ragged batch whose
 // longest sequence comes late starts that sequence's chunks (every sequence
 // gets the same number, so its chunks are the longest) in the last rounds,
-// where they form the launch's tail. Here batch slot z (z < B <= kRankedMaxBatch)
-// runs the sequence of rank z by length, longest first, ties in batch order:
-// the longest chunks start first (the longest-processing-time-first order
-// of list scheduling). One wave loads the B lengths (and explicit offsets),
-// one lane per sequence; each lane counts the sequences that rank before
-// its own, with keys (length, 63 - lane) that are all distinct, so exactly
-// one lane holds rank z (the ballot below is never empty; should it be, the
-// slot keeps sequence z). The count takes one step per sequence, so the host
-// asks for it only where the order pays (ranked_batch). The same loads give the chosen sequence's length
-// and its packed token base (the lengths of the sequences before it in the
-// batch), so this costs no memory round trip over seq_info. Which workgroup
-// computes which chunk changes no arithmetic: the bits are those of the
-// batch order.
+// where they form the launch's tail. Here batch slot z (z < B <=
+// kRankedMaxBatch) runs the sequence of rank z by length, longest first,
+// ties in batch order: the longest chunks start first (the
+// longest-processing-time-first order of list scheduling). One wave loads
+// the B lengths (and explicit offsets), one lane per sequence; each lane
+// counts the sequences that rank before its own, with keys (length, 63 -
+// lane) that are all distinct, so exactly one lane holds rank z (the ballot
+// is never empty; should it be, the slot keeps sequence z). The count takes
+// one step per sequence, so the host asks for it only where the order pays
+// (ranked_batch). The same loads give the chosen sequence's length and its
+// packed token base (the lengths of the sequences before it in the batch),
+// so this costs no memory round trip over seq_info. Which workgroup computes
+// which chunk changes no arithmetic: the bits are those of the batch order.
 constexpr int kRankedMaxBatch = 64;
 // The sequence b of rank z given lane j's length v (lanes below B), ties in
 // batch order.
