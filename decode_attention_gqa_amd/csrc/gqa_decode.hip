@@ -350,13 +350,15 @@ constexpr int kTilesMinTiles = 8;
 constexpr int64_t kTilesMinTokens = 16384;
 constexpr int kTilesMinTilesLong = 4;          // fewer tiles take it only over longer KV
 constexpr int64_t kTilesMinTokensLong = 65536;
-// 12 or more tiles from 8192 tokens (after the whole-round split rule): 70B
-// B = 1, 8k tokens, µs per call, tile-per-wave vs two-tile kernel: S_q = 24
-// (12 tiles) 28.4 vs 30.7, S_q = 31 (16) 33.3 vs 36.5, S_q = 48 (24) 43.3 vs
-// 53.6; S_q = 20 (10 tiles) 27.0 vs 27.6 and S_q = 16 (8) 30.2 vs 23.5 stay
-// on two tiles, as do 4k tokens (S_q = 24: 22.6 vs 22.4).
-constexpr int kTilesMinTilesMid = 12;
-constexpr int64_t kTilesMinTokensMid = 8192;
+// 9 or more tiles from 4096 tokens (after the whole-round split rule): 70B
+// B = 1, µs per call, tile-per-wave vs two-tile kernel: 8k tokens, S_q = 18
+// (9 tiles) 24.1 vs 28.3, S_q = 20 (10) 24.9 vs 28.7; 4k, S_q = 24 (12) 21.2
+// vs 23.0; S_q = 16 (8 tiles) stays on two tiles (8k: 30.0 vs 24.5). (12
+// tiles from 8192 tokens until the tile-per-wave kernel read its V^T
+// operands per output tile: then S_q = 20 27.0 vs 27.6, 4k S_q = 24 22.6
+// vs 22.4.)
+constexpr int kTilesMinTilesMid = 9;
+constexpr int64_t kTilesMinTokensMid = 4096;
 // 5 to 7 tiles from 32768 tokens (the two-tile kernel's 3 or 4 passes drift
 // apart over long KV): 70B B = 1, 32k tokens, µs per call, tile-per-wave vs
 // two-tile kernel: S_q = 10 46.6 vs 51.3, S_q = 12 50.2 vs 51.8, S_q = 14
