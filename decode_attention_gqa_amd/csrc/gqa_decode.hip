@@ -53,6 +53,10 @@ struct SplitPolicy {
   int64_t max_chunk;
   bool eight_wave;              // a single sequence may take one 8-wave workgroup per CU
   bool short_one;               // short sequences, B <= 4: chunks down to one block (single token)
+  // > 0: a single sequence in one pass whose chunks, at one workgroup per CU,
+  // hold at most this many tokens takes that one round instead of wg_per_cu
+  // workgroups per CU (half the triplets to store and merge)
+  int64_t one_per_cu_max_chunk = 0;
 };
 // One 16-column tile per workgroup, two workgroups per CU, one query token. A
 // second round hides each workgroup's start-up behind another's streaming.
@@ -74,7 +78,7 @@ constexpr SplitPolicy kTwoTiles{1, 1, 4, 16384, false, false};
 // One tile per wave, eight per workgroup (multi-token decode), two workgroups
 // per CU: one round for a single sequence, up to two for a batch (ragged
 // B = 8, S_q = 16: 209.9 µs at two rounds, 227.9 at four).
-constexpr SplitPolicy kTileWavesPolicy{2, 1, 2, 16384, false, false};
+constexpr SplitPolicy kTileWavesPolicy{2, 1, 2, 16384, false, false, 512};
 // Two tiles per wave, sixteen per workgroup, one workgroup per CU.
 constexpr SplitPolicy kTilePairsPolicy{1, 1, 2, 16384, false, false};
 
@@ -350,15 +354,19 @@ constexpr int kTilesMinTiles = 8;
 constexpr int64_t kTilesMinTokens = 16384;
 constexpr int kTilesMinTilesLong = 4;          // fewer tiles take it only over longer KV
 constexpr int64_t kTilesMinTokensLong = 65536;
-// 9 or more tiles from 4096 tokens (after the whole-round split rule): 70B
-// B = 1, µs per call, tile-per-wave vs two-tile kernel: 8k tokens, S_q = 18
-// (9 tiles) 24.1 vs 28.3, S_q = 20 (10) 24.9 vs 28.7; 4k, S_q = 24 (12) 21.2
-// vs 23.0; S_q = 16 (8 tiles) stays on two tiles (8k: 30.0 vs 24.5). (12
-// tiles from 8192 tokens until the tile-per-wave kernel read its V^T
-// operands per output tile: then S_q = 20 27.0 vs 27.6, 4k S_q = 24 22.6
-// vs 22.4.)
-constexpr int kTilesMinTilesMid = 9;
-constexpr int64_t kTilesMinTokensMid = 4096;
+// 12 or more tiles from 8192 tokens (after the whole-round split rule): 70B
+// B = 1, 8k tokens, µs per call, tile-per-wave vs two-tile kernel: S_q = 24
+// (12 tiles) 28.4 vs 30.7, S_q = 31 (16) 33.3 vs 36.5, S_q = 48 (24) 43.3 vs
+// 53.6.
+constexpr int kTilesMinTilesMid = 12;
+constexpr int64_t kTilesMinTokensMid = 8192;
+// 9 to 15 tiles (one per wave) from 4096 tokens, since the tile-per-wave
+// kernel reads its V^T operands per output tile: 70B B = 1, µs per call,
+// tile-per-wave vs two-tile kernel: 8k tokens, S_q = 18 (9 tiles) 24.1 vs
+// 28.3, S_q = 20 (10) 24.9 vs 28.7; 4k, S_q = 18 18.6 vs 20.9, S_q = 24 (12)
+// 21.1 vs 22.8; S_q = 16 (8 tiles) stays on two tiles (8k: 30.0 vs 24.5).
+constexpr int kTilesMinTilesLow = 9;
+constexpr int64_t kTilesMinTokensLow = 4096;
 // 5 to 7 tiles from 32768 tokens (the two-tile kernel's 3 or 4 passes drift
 // apart over long KV): 70B B = 1, 32k tokens, µs per call, tile-per-wave vs
 // two-tile kernel: S_q = 10 46.6 vs 51.3, S_q = 12 50.2 vs 51.8, S_q = 14
@@ -406,13 +414,17 @@ void query_tiles(int s_q, int nrep, int B, int64_t hint, int* tpt, int* qtiles, 
   if ((*qtiles >= kTilesMinTiles && tokens >= kTilesMinTokens) ||
       (*qtiles >= kTilesMinTilesLong && tokens >= kTilesMinTokensLong) ||
       (*qtiles >= kTilesMinTilesMid && tokens >= kTilesMinTokensMid) ||
+      (*qtiles >= kTilesMinTilesLow && *qtiles < kTilePairsMinTiles && tokens >= kTilesMinTokensLow) ||
       (*qtiles >= kTilesMinTilesFew && tokens >= kTilesMinTokensFew) ||
       (*qtiles >= kTilePairsMinTiles && (int64_t)*qtiles * tokens >= kTilesMinWork))
     *tpw = *qtiles >= kTilePairsMinTiles ? gqa::kTilePairs : gqa::kTileWaves;
   *passes = (*qtiles + *tpw - 1) / *tpw;
 }
 
-int pick_splits_host(int B, int passes, int h_kv, int64_t s_kv_max, int num_cus, const SplitPolicy& p) {
+// full_pass: every pass's workgroups give each wave a query tile (the
+// tile-per-wave kernel with a multiple of 8 tiles).
+int pick_splits_host(int B, int passes, int h_kv, int64_t s_kv_max, int num_cus, const SplitPolicy& p,
+                     bool full_pass = false) {
   // Enough workgroups to fill every CU at B = 1 ...
   const int64_t units = (int64_t)B * passes * h_kv;
   const int64_t slots = (int64_t)p.wg_per_cu * num_cus;
@@ -427,6 +439,16 @@ int pick_splits_host(int B, int passes, int h_kv, int64_t s_kv_max, int num_cus,
   // instead of 3: 74.7 -> 53.6).
   if (B == 1 && n * units > slots && slots / units >= 1 && 4 * (slots / units) * units >= 3 * slots)
     n = slots / units;
+  if (s_kv_max > 0 && B == 1 && passes == 1 && full_pass && p.one_per_cu_max_chunk > 0 &&
+      num_cus / units >= 1 && s_kv_max <= p.one_per_cu_max_chunk * (num_cus / units)) {
+    // ... one round of one tile-per-wave workgroup per CU (70B, µs per call,
+    // S_q = 16, 64 -> 32 chunks: 16k 36.1 / 36.1 -> 32.0 / 31.5 (and 36.5
+    // -> 31.7 on another box); 32k even (53.4 / 59.2 -> 57.9 / 54.8), 64k
+    // better on two per CU (105.1 / 109.4 against 110.2 / 120.6); not
+    // measured better with waves left without a tile, 32k S_q = 12: 47.5
+    // either way, nor with two passes, 8k S_q = 20: 24.8 -> 29.6).
+    return (int)(num_cus / units);
+  }
   if (s_kv_max > 0 && B == 1 && p.eight_wave) {
     // ... one sequence that one round of 8-wave workgroups, one per CU,
     // covers in chunks of kEightWaveMinChunk to kEightWaveMaxChunk tokens:
@@ -550,7 +572,8 @@ int gqa_decode_multi_splits_d(int B, int S_q, int h_q, int h_kv, int d_head, int
   }
   int tpt, qtiles, tpw, passes;
   query_tiles(S_q, h_q / h_kv, B, s_kv_max, &tpt, &qtiles, &tpw, &passes);
-  return pick_splits_host(B, passes, h_kv, s_kv_max, num_cus, split_policy(tpw, d_head, false, S_q));
+  return pick_splits_host(B, passes, h_kv, s_kv_max, num_cus, split_policy(tpw, d_head, false, S_q),
+                          tpw == gqa::kTileWaves && qtiles % gqa::kTileWaves == 0);
 }
 
 int gqa_decode_multi_splits(int B, int S_q, int h_q, int h_kv, int64_t s_kv_max, int num_cus) {
@@ -622,7 +645,8 @@ int plan_splits(int B, int h_q, int h_kv, int d_head, int n_splits, int64_t s_kv
   if (st != GQA_OK) return st;
   int tpt, qtiles, tpw, passes;
   query_tiles(s_q, h_q / h_kv, B, s_kv_hint, &tpt, &qtiles, &tpw, &passes);
-  *ns = pick_splits_host(B, passes, h_kv, s_kv_hint, num_cus, split_policy(tpw, d_head, !multi_entry, s_q));
+  *ns = pick_splits_host(B, passes, h_kv, s_kv_hint, num_cus, split_policy(tpw, d_head, !multi_entry, s_q),
+                         tpw == gqa::kTileWaves && qtiles % gqa::kTileWaves == 0);
   return GQA_OK;
 }
 

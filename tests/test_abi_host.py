@@ -219,7 +219,8 @@ def test_multi_split_heuristic_values(gqa):
     # one tile per wave (8 tiles or more over 16384 tokens, 4 or more over
     # 65536), two workgroups per CU: one round for one sequence, two for a batch
     assert f(1, 16, 8192) == 8                   # 8 tiles, too short: two tiles per workgroup
-    assert f(1, 16, 16384) == 64
+    assert f(1, 16, 16384) == 32                 # 8 tiles, one pass, up to 512 tokens a chunk: one workgroup per CU
+    assert f(1, 16, 16385) == 64                 # longer: two workgroups per CU
     assert f(2, 16, 8192) == 32                  # B times the longest length counts
     assert f(1, 8, 65535) == 16                  # 4 tiles: two per workgroup below 65536 tokens
     assert f(1, 8, 65536) == 64
@@ -228,9 +229,13 @@ def test_multi_split_heuristic_values(gqa):
     assert f(1, 64, 8191) == 2                   # below: two tiles per workgroup, 16 passes
     assert f(1, 128, 4096) == 8                  # 64 tiles x 4096: two per wave, four passes
     assert f(1, 12, 8192) == 10                  # 6 tiles, two per workgroup, 24 units: 10 (240 workgroups), not 11
-    assert f(1, 20, 8192) == 6                   # 40 units: 6 (240 workgroups), not 7 (280 > 256 slots)
+    assert f(1, 20, 2048) == 6                   # 40 units: 6 (240 workgroups), not 7 (280 > 256 slots)
+    assert f(1, 20, 8192) == 32                  # 10 tiles from 4096 tokens: one per wave
     assert f(1, 24, 8192) == 32                  # 12 tiles from 8192 tokens: one per wave, two passes
-    assert f(1, 24, 4096) == 5                   # below 8192 tokens: two tiles per workgroup, 48 units
+    assert f(1, 24, 4096) == 32                  # 9 to 15 tiles from 4096 tokens: one per wave, two passes
+    assert f(1, 24, 2048) == 5                   # below: two tiles per workgroup, 48 units
+    assert f(1, 18, 8192) == 32                  # 9 tiles: one per wave
+    assert f(1, 32, 4096) == 4                   # 16 tiles below 8192 tokens and 2^18: two tiles per workgroup
     assert f(1, 48, 8192) == 16                  # 24 tiles: two per wave, two passes
     assert f(1, 10, 32768) == 64                 # 5 tiles from 32768 tokens: one per wave, one pass
     assert f(1, 10, 16384) == 10                 # below: two tiles per workgroup, 24 units
