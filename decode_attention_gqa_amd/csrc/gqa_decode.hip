@@ -352,6 +352,12 @@ hipError_t launch_merge(bool out_bf16, int B, int h_q, hipStream_t st, const gqa
 // 43.7 vs 42.1; S_q = 8, 65535 vs 65536: 85.6 vs 74.2.
 constexpr int kTilesMinTiles = 8;
 constexpr int64_t kTilesMinTokens = 16384;
+// One sequence of 8 to 15 tiles takes it from 4096 tokens, one workgroup
+// per CU (the split rule below): 70B, S_q = 16, µs per call, tile-per-wave
+// vs two-tile kernel: 4k 17.0 vs 18.1, 6k 19.6 vs 21.3, 8k 22.1 vs 24.2, 9k
+// 23.2 vs 25.8, 12k 26.8 vs 29.9, 15k 30.5 vs 35.1. Batches stay at 16384
+// tokens (B = 2 x 4k 26.0 vs 24.0, ragged 4 x 1k-4k 45.6 vs 41.9).
+constexpr int64_t kTilesMinTokensOne = 4096;
 constexpr int kTilesMinTilesLong = 4;          // fewer tiles take it only over longer KV
 constexpr int64_t kTilesMinTokensLong = 65536;
 // 12 or more tiles from 8192 tokens (after the whole-round split rule): 70B
@@ -364,7 +370,8 @@ constexpr int64_t kTilesMinTokensMid = 8192;
 // kernel reads its V^T operands per output tile: 70B B = 1, µs per call,
 // tile-per-wave vs two-tile kernel: 8k tokens, S_q = 18 (9 tiles) 24.1 vs
 // 28.3, S_q = 20 (10) 24.9 vs 28.7; 4k, S_q = 18 18.6 vs 20.9, S_q = 24 (12)
-// 21.1 vs 22.8; S_q = 16 (8 tiles) stays on two tiles (8k: 30.0 vs 24.5).
+// 21.1 vs 22.8. (8 tiles: the one-sequence rule above; with 64 chunks, two
+// workgroups per CU, they lost at 8k, 30.0 vs 24.5.)
 constexpr int kTilesMinTilesLow = 9;
 constexpr int64_t kTilesMinTokensLow = 4096;
 // 5 to 7 tiles from 32768 tokens (the two-tile kernel's 3 or 4 passes drift
@@ -412,6 +419,7 @@ void query_tiles(int s_q, int nrep, int B, int64_t hint, int* tpt, int* qtiles, 
   // heads per KV head; many KV heads already fill the chip).
   if (*qtiles == 2 && nrep >= 4 && hint > 0 && ((B == 1 && hint <= 8192) || (hint <= 2048 && tokens <= 8192))) *tpw = 1;
   if ((*qtiles >= kTilesMinTiles && tokens >= kTilesMinTokens) ||
+      (*qtiles >= kTilesMinTiles && *qtiles < kTilePairsMinTiles && B == 1 && tokens >= kTilesMinTokensOne) ||
       (*qtiles >= kTilesMinTilesLong && tokens >= kTilesMinTokensLong) ||
       (*qtiles >= kTilesMinTilesMid && tokens >= kTilesMinTokensMid) ||
       (*qtiles >= kTilesMinTilesLow && *qtiles < kTilePairsMinTiles && tokens >= kTilesMinTokensLow) ||

@@ -100,6 +100,7 @@ int main(void) {
   expect("multi S_q 4 (two tiles, one per pass)", gqa_decode_multi_splits(1, 4, 64, 8, 8192, 256), 16);
   expect("multi S_q 4, 16k (two tiles per pass)", gqa_decode_multi_splits(1, 4, 64, 8, 16384, 256), 32);
   expect("multi S_q 16, 16k (one tile per wave, one workgroup per CU)", gqa_decode_multi_splits(1, 16, 64, 8, 16384, 256), 32);
+  expect("multi S_q 16, 8k (one sequence of 8 tiles from 4096 tokens: one tile per wave)", gqa_decode_multi_splits(1, 16, 64, 8, 8192, 256), 32);
   expect("multi S_q 16, 64k (one tile per wave, two workgroups per CU)", gqa_decode_multi_splits(1, 16, 64, 8, 65536, 256), 64);
   expect("multi bad h_kv", gqa_decode_multi_splits(1, 4, 64, 0, 8192, 256), GQA_ERR_INVALID_ARG);
   expect("multi S_q 2, d 128 (8-wave round)", gqa_decode_multi_splits_d(1, 2, 64, 8, 128, 8192, 256), 32);

@@ -216,9 +216,13 @@ def test_multi_split_heuristic_values(gqa):
     assert f(1, 4, 1 << 20) == 64                # chunks of up to 16384 tokens
     assert f(8, 4, 32768) == 16                  # a batch: the longest over four rounds
     assert f(1, 32, 4096, 32, 32) == 8           # MHA: 16 tokens per tile
-    # one tile per wave (8 tiles or more over 16384 tokens, 4 or more over
-    # 65536), two workgroups per CU: one round for one sequence, two for a batch
-    assert f(1, 16, 8192) == 8                   # 8 tiles, too short: two tiles per workgroup
+    # one tile per wave (8 tiles or more over 16384 tokens, one sequence from
+    # 4096; 4 or more over 65536), two workgroups per CU: one round for one
+    # sequence, two for a batch
+    assert f(1, 16, 4095) == 8                   # 8 tiles, too short: two tiles per workgroup
+    assert f(1, 16, 4096) == 32                  # one sequence from 4096 tokens: one workgroup per CU
+    assert f(1, 16, 8192) == 32
+    assert f(2, 16, 4096) == 4                   # a batch below 16384 tokens: two tiles per workgroup
     assert f(1, 16, 16384) == 32                 # 8 tiles, one pass, up to 512 tokens a chunk: one workgroup per CU
     assert f(1, 16, 16385) == 64                 # longer: two workgroups per CU
     assert f(2, 16, 8192) == 32                  # B times the longest length counts

@@ -131,6 +131,20 @@ def test_tile_waves_short_sequences_and_bf16_out():
     check("tiles short bf16-out", inp, qm, out_dtype="bf16", hint=LONG)
 
 
+@pytest.mark.parametrize("S_q,S", [(16, 4096), (16, 6001), (15, 12000)])
+def test_tile_waves_one_sequence(S_q, S):
+    """One sequence of 8 query tiles at 70B heads from 4096 tokens: the
+    default plan takes one tile per wave in one workgroup per CU (32 chunks
+    of 128 to 375 tokens, the last one partial at 6001; S_q = 15 leaves the
+    last tile half full). Against the oracle, and against the two-tile
+    kernel (no hint) within 1e-3."""
+    inp, qm = make(f"tiles_one_q{S_q}_{S}", 1, S_q, 64, 8, 128, [S], 210 + S_q + S % 97)
+    got, _ = check(f"tiles one sequence S_q={S_q} S={S}", inp, qm)
+    assert run(inp, qm)[1] == 32
+    two, _ = run(inp, qm, hint=False)
+    assert max_err(got, two) <= 1e-3
+
+
 def test_tile_waves_70b_shape():
     """70B heads, 16 query tokens, the kernel taken by the default rule (the
     true longest length as hint, 2 x 20000 tokens)."""
