@@ -352,13 +352,13 @@ hipError_t launch_merge(bool out_bf16, int B, int h_q, hipStream_t st, const gqa
 // 43.7 vs 42.1; S_q = 8, 65535 vs 65536: 85.6 vs 74.2.
 constexpr int kTilesMinTiles = 8;
 constexpr int64_t kTilesMinTokens = 16384;
-// One sequence of 8 to 15 tiles takes it from 4096 tokens, one workgroup
-// per CU (the split rule below): 70B, S_q = 16, µs per call, tile-per-wave
-// vs two-tile kernel: 4k 17.0 vs 18.1, 6k 19.6 vs 21.3, 8k 22.1 vs 24.2, 9k
-// 23.2 vs 25.8, 12k 26.8 vs 29.9, 15k 30.5 vs 35.1. Batches stay at 16384
+// One sequence of 8 to 15 tiles takes it from 4096 tokens (8 tiles in one
+// workgroup per CU, by the split rule below): 70B, S_q = 16, µs per call,
+// tile-per-wave vs two-tile kernel: 4k 17.0 vs 18.1, 6k 19.6 vs 21.3, 8k 22.1
+// vs 24.2, 9k 23.2 vs 25.8, 12k 26.8 vs 29.9, 15k 30.5 vs 35.1. Batches stay at 16384
 // tokens (B = 2 x 4k 26.0 vs 24.0, ragged 4 x 1k-4k 45.6 vs 41.9), and
-// shorter sequences on two tiles (1k 15.1 vs 12.9, 2k 15.9 vs 14.8, 3k 16.6
-// vs 17.0).
+// shorter sequences on two tiles (1k 15.1 vs 12.9, 2k 15.9 vs 14.8; about
+// even at 3k, 16.6 vs 17.0).
 constexpr int64_t kTilesMinTokensOne = 4096;
 constexpr int kTilesMinTilesLong = 4;          // fewer tiles take it only over longer KV
 constexpr int64_t kTilesMinTokensLong = 65536;
