@@ -131,15 +131,17 @@ def test_tile_waves_short_sequences_and_bf16_out():
     check("tiles short bf16-out", inp, qm, out_dtype="bf16", hint=LONG)
 
 
-@pytest.mark.parametrize("S_q,S", [(16, 4096), (16, 6001), (15, 12000)])
-def test_tile_waves_one_sequence(S_q, S):
-    """One sequence of 8 query tiles at 70B heads from 4096 tokens: the
+@pytest.mark.parametrize("n_rep,S_q,d,S", [(8, 16, 128, 4096), (8, 16, 128, 6001), (8, 15, 128, 12000),
+                                           (16, 8, 128, 5000), (8, 16, 64, 4096)])
+def test_tile_waves_one_sequence(n_rep, S_q, d, S):
+    """One sequence of 8 query tiles over 8 kv heads from 4096 tokens: the
     default plan takes one tile per wave in one workgroup per CU (32 chunks
     of 128 to 375 tokens, the last one partial at 6001; S_q = 15 leaves the
-    last tile half full). Against the oracle, and against the two-tile
-    kernel (no hint) within 1e-3."""
-    inp, qm = make(f"tiles_one_q{S_q}_{S}", 1, S_q, 64, 8, 128, [S], 210 + S_q + S % 97)
-    got, _ = check(f"tiles one sequence S_q={S_q} S={S}", inp, qm)
+    last tile half full; 16 query heads per kv head make a tile of one
+    token; d = 64). Against the oracle, and against the two-tile kernel (no
+    hint) within 1e-3."""
+    inp, qm = make(f"tiles_one_r{n_rep}_q{S_q}_d{d}_{S}", 1, S_q, 8 * n_rep, 8, d, [S], 210 + S_q + S % 97 + d)
+    got, _ = check(f"tiles one sequence n_rep={n_rep} S_q={S_q} d={d} S={S}", inp, qm)
     assert run(inp, qm)[1] == 32
     two, _ = run(inp, qm, hint=False)
     assert max_err(got, two) <= 1e-3
