@@ -78,7 +78,7 @@ constexpr SplitPolicy kTwoTiles{1, 1, 4, 16384, false, false};
 // One tile per wave, eight per workgroup (multi-token decode), two workgroups
 // per CU: one round for a single sequence, up to two for a batch (ragged
 // B = 8, S_q = 16: 209.9 µs at two rounds, 227.9 at four).
-constexpr SplitPolicy kTileWavesPolicy{2, 1, 2, 16384, false, false, 512};
+constexpr SplitPolicy kTileWavesPolicy{2, 1, 2, 16384, false, false, 768};
 // Two tiles per wave, sixteen per workgroup, one workgroup per CU.
 constexpr SplitPolicy kTilePairsPolicy{1, 1, 2, 16384, false, false};
 
@@ -453,7 +453,10 @@ int pick_splits_host(int B, int passes, int h_kv, int64_t s_kv_max, int num_cus,
       num_cus / units >= 1 && s_kv_max <= p.one_per_cu_max_chunk * (num_cus / units)) {
     // ... one round of one tile-per-wave workgroup per CU (70B, µs per call,
     // S_q = 16, 64 -> 32 chunks: 16k 36.1 / 36.1 -> 32.0 / 31.5 (and 36.5
-    // -> 31.7 on another box); 32k even (53.4 / 59.2 -> 57.9 / 54.8), 64k
+    // -> 31.7 on another box), 18k 38.1 / 38.3 / 38.1 -> 35.0 / 34.4 / 35.2,
+    // 20k 41.4 / 40.7 / 40.7 -> 37.3 / 37.0 / 37.8, 24k 45.6 / 43.8 / 46.0
+    // -> 42.6 / 41.9 / 41.6, S_q = 15 at 22k 40.8 / 42.0 / 42.7 -> 39.6 /
+    // 39.6 / 39.3; 32k even (53.4 / 59.2 -> 57.9 / 54.8), 64k
     // better on two per CU (105.1 / 109.4 against 110.2 / 120.6); not
     // measured better with waves left without a tile, 32k S_q = 12: 47.5
     // either way, nor with two passes, 8k S_q = 20: 24.8 -> 29.6).

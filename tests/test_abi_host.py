@@ -225,8 +225,9 @@ def test_multi_split_heuristic_values(gqa):
     assert f(2, 16, 4096) == 4                   # a batch below 16384 tokens: two tiles per workgroup
     assert f(1, 8, 5000, 128, 8) == 32           # 16 query heads per kv head: 8 one-token tiles
     assert fd(1, 16, 4096, 64) == 32             # d = 64
-    assert f(1, 16, 16384) == 32                 # 8 tiles, one pass, up to 512 tokens a chunk: one workgroup per CU
-    assert f(1, 16, 16385) == 64                 # longer: two workgroups per CU
+    assert f(1, 16, 16384) == 32                 # 8 tiles, one pass, up to 768 tokens a chunk: one workgroup per CU
+    assert f(1, 16, 24576) == 32
+    assert f(1, 16, 24577) == 64                 # longer: two workgroups per CU
     assert f(2, 16, 8192) == 32                  # B times the longest length counts
     assert f(1, 8, 65535) == 16                  # 4 tiles: two per workgroup below 65536 tokens
     assert f(1, 8, 65536) == 64

@@ -132,11 +132,11 @@ def test_tile_waves_short_sequences_and_bf16_out():
 
 
 @pytest.mark.parametrize("n_rep,S_q,d,S", [(8, 16, 128, 4096), (8, 16, 128, 6001), (8, 15, 128, 12000),
-                                           (16, 8, 128, 5000), (8, 16, 64, 4096)])
+                                           (8, 16, 128, 24000), (16, 8, 128, 5000), (8, 16, 64, 4096)])
 def test_tile_waves_one_sequence(n_rep, S_q, d, S):
     """One sequence of 8 query tiles over 8 kv heads from 4096 tokens: the
     default plan takes one tile per wave in one workgroup per CU (32 chunks
-    of 128 to 375 tokens, the last one partial at 6001; S_q = 15 leaves the
+    of 128 to 750 tokens, the last one partial at 6001; S_q = 15 leaves the
     last tile half full; 16 query heads per kv head make a tile of one
     token; d = 64). Against the oracle, and against the two-tile kernel (no
     hint) within 1e-3."""
